@@ -1,0 +1,162 @@
+"""Plant plausible mistakes in the CPU oracle and check that the pins reject each one.
+
+Each mutant replaces one piece of ``oracle.lrq_oracle`` (on the CPU, for the
+duration of one test) with a wrong variant; the pin suite must then fail at
+least one check.  This shows the pins are strong enough to catch a dropped
+term, a wrong sign or index, or a transposed operand anywhere in the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle.lrq_oracle as o
+import pins
+
+
+def _eps_outside(x, eps):
+    x = np.asarray(x, np.float64)
+    return 1.0 / np.sqrt(np.mean(x * x, axis=-1)) + eps
+
+
+def _sum_not_mean(x, eps):
+    x = np.asarray(x, np.float64)
+    return 1.0 / np.sqrt(np.sum(x * x, axis=-1) + eps)
+
+
+def _no_sqrt(x, eps):
+    x = np.asarray(x, np.float64)
+    return 1.0 / (np.mean(x * x, axis=-1) + eps)
+
+
+def _no_gamma(x, gamma, eps):
+    x = np.asarray(x, np.float64)
+    return x * o.rms_inverse(x, eps)[:, None]
+
+
+def _freq_half_exponent(head_dim, theta):
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return np.power(float(theta), -1.0 * i / head_dim)
+
+
+def _freq_off_by_one(head_dim, theta):
+    i = np.arange(1, head_dim // 2 + 1, dtype=np.float64)
+    return np.power(float(theta), -2.0 * i / head_dim)
+
+
+_real_rotate = o.rope_rotate
+
+
+def _rotate_wrong_sign(y, positions, head_dim, theta, inverse=False):
+    return _real_rotate(y, positions, head_dim, theta, inverse=not inverse)
+
+
+def _rotate_interleaved(y, positions, head_dim, theta, inverse=False):
+    # pairs (2i, 2i+1) instead of (i, i + D/2)
+    y = np.asarray(y, np.float64)
+    T, n = y.shape
+    phi = o.rope_angles(positions, head_dim, theta) * (-1 if inverse else 1)
+    c, s = np.cos(phi)[:, None, :], np.sin(phi)[:, None, :]
+    hh = y.reshape(T, n // head_dim, head_dim // 2, 2)
+    a, b = hh[..., 0], hh[..., 1]
+    out = np.stack([a * c - b * s, b * c + a * s], axis=-1)
+    return out.reshape(T, n)
+
+
+def _rotated_all(self):
+    return 0, self.n_out
+
+
+def _rotated_q_only(self):
+    return 0, self.n_q_heads * self.head_dim
+
+
+def _scale_alpha(self):
+    return self.lora_alpha
+
+
+def _lora_on_x(spec, h, a, b):
+    # LoRA applied to a rescaled input instead of h (drops gamma)
+    out = {}
+    for c in o.TARGETS:
+        if spec.lora_targets & c:
+            hh = h / np.sqrt(np.mean(h * h, axis=1, keepdims=True))
+            out[c] = spec.lora_scale * ((hh @ np.asarray(a[c]).T) @ np.asarray(b[c]).T)
+    return out
+
+
+def _lora_wrong_block(self, target):
+    D = self.head_dim
+    nq, nkv = self.n_q_heads * D, self.n_kv_heads * D
+    # v adapter lands on the k block
+    return {o.TARGET_Q: (0, nq), o.TARGET_K: (nq, nq + nkv), o.TARGET_V: (nq, nq + nkv)}[target]
+
+
+_real_backward = o.backward
+
+
+def _bwd_drop_inv3(spec, x, gamma, w, bias, a, b, positions, dy, dx_rows=None):
+    # dx = inv * gamma * dh only: the RMSNorm term through the row statistic is dropped
+    _, dA, dB = _real_backward(spec, x, gamma, w, bias, a, b, positions, dy, dx_rows)
+    x = np.asarray(x, np.float64)
+    rows = np.arange(x.shape[0]) if dx_rows is None else np.asarray(dx_rows)
+    G = o.unrotate_grad(spec, dy, positions)
+    dh = G @ np.asarray(w, np.float64)
+    for c in dA:
+        lo, hi = spec.columns(c)
+        dh += spec.lora_scale * ((G[:, lo:hi] @ np.asarray(b[c])) @ np.asarray(a[c]))
+    inv = o.rms_inverse(x, spec.eps)
+    return (inv[:, None] * np.asarray(gamma)[None, :] * dh)[rows], dA, dB
+
+
+def _bwd_db_with_h(spec, x, gamma, w, bias, a, b, positions, dy, dx_rows=None):
+    dx, dA, dB = _real_backward(spec, x, gamma, w, bias, a, b, positions, dy, dx_rows)
+    G = o.unrotate_grad(spec, dy, positions)
+    h = o.rms_normalise(x, gamma, spec.eps)
+    for c in dB:
+        lo, hi = spec.columns(c)
+        dB[c] = spec.lora_scale * (G[:, lo:hi].T @ h[:, :dB[c].shape[1]])
+    return dx, dA, dB
+
+
+def _bwd_no_unrotate(spec, dy, positions):
+    return np.asarray(dy, np.float64).copy()
+
+
+MUTANTS = {
+    "eps outside sqrt": ("rms_inverse", _eps_outside),
+    "sum instead of mean": ("rms_inverse", _sum_not_mean),
+    "missing sqrt": ("rms_inverse", _no_sqrt),
+    "gamma dropped": ("rms_normalise", _no_gamma),
+    "frequency exponent -i/D": ("rope_frequencies", _freq_half_exponent),
+    "frequency index off by one": ("rope_frequencies", _freq_off_by_one),
+    "rotation sign flipped": ("rope_rotate", _rotate_wrong_sign),
+    "interleaved pairs": ("rope_rotate", _rotate_interleaved),
+    "v rotated too": ("Spec.rotated_columns", _rotated_all),
+    "k not rotated": ("Spec.rotated_columns", _rotated_q_only),
+    "scale alpha not alpha/r": ("Spec.lora_scale", property(_scale_alpha)),
+    "LoRA input without gamma": ("lora_update", _lora_on_x),
+    "adapter on wrong block": ("Spec.columns", _lora_wrong_block),
+    "dx missing inv^3 term": ("backward", _bwd_drop_inv3),
+    "dB uses h instead of U": ("backward", _bwd_db_with_h),
+    "gradient not un-rotated": ("unrotate_grad", _bwd_no_unrotate),
+}
+
+
+def _failures(checks):
+    failed = []
+    for chk in checks:
+        try:
+            chk(o)
+        except Exception:  # noqa: BLE001 - any failure counts as "caught"
+            failed.append(chk.__name__)
+    return failed
+
+
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    where, repl = MUTANTS[name]
+    if where.startswith("Spec."):
+        monkeypatch.setattr(o.Spec, where[5:], repl)
+    else:
+        monkeypatch.setattr(o, where, repl)
+    failed = _failures(pins.ALL_CHECKS)
+    assert failed, f"no pin caught the planted mistake '{name}'"
