@@ -1,0 +1,162 @@
+/*
+ * lrq.h -- C ABI of liblrq: the fused attention-input projection of a LoRA-adapted
+ * transformer layer, on AMD Instinct MI355X (gfx950).
+ *
+ *   out = RoPE( W_qkv . h + b + (alpha / r) . B (A . h) ),   h = RMSNorm(x) . gamma
+ *
+ * for every token row of x, computed in one pass per token tile: neither the
+ * normalised activations h nor the rank-r intermediate A . h is written to memory.
+ *
+ * Where the operation is defined (web pages on Liger-Kernel, cited by title and section):
+ *  - RMSNorm (mean of squares over the hidden size, eps inside the square root, then
+ *    times the norm weight) and the projection with bias before the rotary step:
+ *    "Liger-Kernel底层优化：新一代内核级推理加速引擎深度解析", fused-kernel pseudocode,
+ *    Step 1 (RMSNorm) and Step 2 (QKV Projection).
+ *  - The chain normalise -> project to q, k, v -> rotate q and k (v is not rotated), which
+ *    the fused kernel replaces: "Swift-All一文详解：如何用Liger-Kernel提升训练效率",
+ *    section 2.2 (1), RMSNorm + Rotary Embedding + Attention QKV fusion.
+ *  - LoRA: frozen projection plus up(down(x)), with down A [r, d_in] and up B [d_out, r]:
+ *    "Liger-Kernel内核级优化：GPU利用率飙升至90%以上", section on why conventional
+ *    fine-tuning stalls (the y = Wx + B(Ax) formula and its unfused F.linear steps);
+ *    rank r, alpha and the q/k/v target modules are the LoRA configuration fields shown
+ *    on the same pages.  The scale alpha / r is the standard LoRA scale (the formula on the
+ *    pages prints none).
+ *  - RoPE: rotate-half (GPT-NeoX) pairing -- the pseudocode's frequency index is the
+ *    feature index modulo head_dim / 2 -- with omega_i = theta^(-2i/D), i < D/2, angle
+ *    pos * omega_i, pair (y[i], y[i + D/2]) -> (a cos - b sin, b cos + a sin).  The rest of
+ *    that pseudocode's rotation (it pairs k with v) is not used.
+ *  - Backward with recomputation instead of stored activations: "Liger-Kernel内核级优化",
+ *    system architecture and workflow section (backward also fused, with recompute).
+ *
+ * Layouts (all row-major, dense):
+ *   x, dx      [T, d]            activations (dtype)
+ *   gamma      [d]               RMSNorm weight (dtype)
+ *   w_qkv      [N, d]            N = (Hq + 2 Hkv) * D; rows are the q heads, then the k heads,
+ *                                then the v heads; each head's D rows are contiguous
+ *   bias       [N]               optional (dtype)
+ *   lora_a[t]  [r, d]            down projection of target t (t = 0 q, 1 k, 2 v)
+ *   lora_b[t]  [N_t, r]          up projection; N_q = Hq * D, N_k = N_v = Hkv * D
+ *   positions  [T] int32         absolute RoPE position of each token, >= 0
+ *   out, y, dy [T, N]            q | k | v column blocks
+ *   d_lora_a[t] [r, d], d_lora_b[t] [N_t, r]   float32 gradients
+ * Every array pointer must be 16-byte aligned.
+ *
+ * Ownership: every pointer is a device pointer owned by the caller; the library keeps no
+ * reference after a call returns.  Work is enqueued asynchronously on `stream` (a
+ * hipStream_t; NULL = the null stream) and nothing is synchronised.  The library allocates
+ * no device memory; scratch space is the caller's `workspace` of at least
+ * lrq_workspace_size() bytes (256-byte aligned), used only until the enqueued work ends.
+ * Calls that share a workspace must be ordered on one stream.
+ *
+ * Errors: every entry point validates its arguments on the host before enqueuing
+ * anything; on error nothing is launched and a message is kept for lrq_last_error()
+ * (per thread).
+ *   LRQ_ERR_INVALID_ARG  malformed descriptor or a required pointer is NULL (see below)
+ *   LRQ_ERR_UNSUPPORTED  well-formed but outside what the kernels cover (alignment,
+ *                        rank > LRQ_MAX_LORA_RANK, a forced variant that cannot run)
+ *   LRQ_ERR_HIP          a HIP call failed (message holds the HIP error string)
+ * Positions are not range-checked on the device; a negative position is rotated by a
+ * negative angle.
+ */
+#ifndef LRQ_H_
+#define LRQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LRQ_ABI_VERSION 1
+#define LRQ_MAX_LORA_RANK 64
+
+typedef enum lrq_status {
+  LRQ_OK = 0,
+  LRQ_ERR_INVALID_ARG = 1,
+  LRQ_ERR_UNSUPPORTED = 2,
+  LRQ_ERR_HIP = 3
+} lrq_status;
+
+/* Element type of x, gamma, w_qkv, bias, lora_a, lora_b, out, y, dy and dx.  Arithmetic
+ * is float32 throughout for LRQ_F32; for LRQ_BF16 the matrix products take bfloat16
+ * operands with float32 accumulation, and the row statistics, bias, LoRA scale and
+ * rotation are applied in float32 before one round-to-nearest-even store. */
+typedef enum lrq_dtype { LRQ_F32 = 0, LRQ_BF16 = 1 } lrq_dtype;
+
+enum { LRQ_TARGET_Q = 1, LRQ_TARGET_K = 2, LRQ_TARGET_V = 4 };
+
+/* Kernel families; LRQ_VARIANT_AUTO lets the library choose. */
+typedef enum lrq_variant {
+  LRQ_VARIANT_AUTO = 0,
+  LRQ_VARIANT_GENERIC = 1, /* any shape, fp32 or bf16, scalar FMA tiles */
+  LRQ_VARIANT_TILED = 2,   /* bf16, head_dim 128: MFMA tiles for many tokens */
+  LRQ_VARIANT_DECODE = 3   /* bf16, head_dim 128: few tokens, streams W from HBM */
+} lrq_variant;
+
+typedef struct lrq_desc {
+  int64_t n_tokens;      /* T >= 0; T == 0 is a no-op                                 */
+  int64_t d_model;       /* d >= 1                                                    */
+  int32_t n_q_heads;     /* Hq >= 1                                                   */
+  int32_t n_kv_heads;    /* Hkv >= 1, Hq % Hkv == 0                                   */
+  int32_t head_dim;      /* D >= 2, even                                              */
+  int32_t dtype;         /* lrq_dtype                                                 */
+  float eps;             /* RMSNorm epsilon, finite and >= 0, added to the mean square */
+  float rope_theta;      /* RoPE base, finite and > 0                                 */
+  int32_t lora_rank;     /* r; 1..LRQ_MAX_LORA_RANK when lora_targets != 0            */
+  float lora_alpha;      /* LoRA alpha (finite); the update is scaled by alpha / r    */
+  uint32_t lora_targets; /* OR of LRQ_TARGET_*; 0 = no adapters                       */
+  int32_t has_bias;      /* 0 or 1                                                    */
+  int32_t variant;       /* lrq_variant; LRQ_VARIANT_AUTO (0) normally                 */
+} lrq_desc;
+
+/* Forward: out = RoPE(W h + b + (alpha/r) B (A h)), h = x * inv_rms(x) * gamma.
+ *   lora_a / lora_b: arrays of 3 pointers (q, k, v); entries of non-targets are ignored
+ *   and may be NULL, and the arrays themselves may be NULL when lora_targets == 0.
+ *   bias is ignored (may be NULL) when has_bias == 0.
+ * INVALID_ARG when: desc is NULL; T < 0; d < 1; Hq < 1; Hkv < 1; Hq % Hkv != 0; D < 2
+ *   or odd; dtype unknown; eps < 0 or not finite; theta <= 0 or not finite; lora_targets
+ *   has bits other than q|k|v; targets set with r < 1 or alpha not finite; has_bias not
+ *   0/1; variant unknown; x, gamma, w_qkv, positions or out NULL (T > 0); bias NULL with
+ *   has_bias; a target's lora_a / lora_b NULL; workspace_bytes below
+ *   lrq_workspace_size(desc, 0) or workspace NULL when that size is > 0. */
+lrq_status lrq_forward(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,
+                       const void* bias, const void* const* lora_a, const void* const* lora_b,
+                       const int32_t* positions, void* out, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Backward of the forward above with W, gamma and bias frozen.  Given dy = dL/d(out),
+ * writes dx = dL/dx (dtype) and, for every target t, d_lora_a[t] = dL/dA_t and
+ * d_lora_b[t] = dL/dB_t (float32, overwritten, not accumulated).  h and A h are
+ * recomputed from x.  `y` must be the forward output for the same inputs (it provides the
+ * row statistic <dy, y - R b> that the RMSNorm backward needs without a second pass).
+ * Same INVALID_ARG rules as lrq_forward, plus y, dy, dx NULL (T > 0) or a target's
+ * d_lora_a / d_lora_b NULL.  With T == 0 the LoRA gradients are set to zero. */
+lrq_status lrq_backward(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,
+                        const void* bias, const void* const* lora_a, const void* const* lora_b,
+                        const int32_t* positions, const void* y, const void* dy, void* dx,
+                        float* const* d_lora_a, float* const* d_lora_b, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace the call needs (0 if none); 0 for an invalid descriptor. */
+size_t lrq_workspace_size(const lrq_desc* desc, int for_backward);
+
+/* The kernel family lrq_forward (for_backward = 0) or lrq_backward (1) would run for this
+ * descriptor (an lrq_variant value), or -1 when the descriptor is invalid or the forced
+ * variant cannot run.  Host-only; enqueues nothing. */
+int lrq_select_variant(const lrq_desc* desc, int for_backward);
+
+/* Static name of a status code ("LRQ_OK", ...). */
+const char* lrq_status_string(lrq_status status);
+
+/* Message describing the last error returned on the calling thread ("" if none). */
+const char* lrq_last_error(void);
+
+/* LRQ_ABI_VERSION of the loaded library. */
+int lrq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LRQ_H_ */

@@ -1,0 +1,158 @@
+"""Thin ctypes binding of liblrq (include/lrq.h): argument marshalling only.
+
+Every function has the name of the C entry point it calls.  Array arguments may be
+torch tensors (their ``data_ptr()`` is passed) or plain integers (raw device
+addresses; 0 = NULL).  A non-OK status raises :class:`LrqError` carrying the
+library's message.  There is no fallback: if ``liblrq.so`` is missing, loading it
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblrq.so")
+
+LRQ_OK, LRQ_ERR_INVALID_ARG, LRQ_ERR_UNSUPPORTED, LRQ_ERR_HIP = 0, 1, 2, 3
+LRQ_F32, LRQ_BF16 = 0, 1
+LRQ_TARGET_Q, LRQ_TARGET_K, LRQ_TARGET_V = 1, 2, 4
+LRQ_VARIANT_AUTO, LRQ_VARIANT_GENERIC, LRQ_VARIANT_TILED, LRQ_VARIANT_DECODE = 0, 1, 2, 3
+VARIANT_NAMES = {LRQ_VARIANT_GENERIC: "generic", LRQ_VARIANT_TILED: "tiled", LRQ_VARIANT_DECODE: "decode"}
+
+# every symbol include/lrq.h declares
+EXPORTED = ("lrq_forward", "lrq_backward", "lrq_workspace_size", "lrq_select_variant",
+            "lrq_status_string", "lrq_last_error", "lrq_abi_version")
+
+
+class LrqDesc(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int64), ("d_model", ctypes.c_int64),
+                ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                ("lora_rank", ctypes.c_int32), ("lora_alpha", ctypes.c_float),
+                ("lora_targets", ctypes.c_uint32), ("has_bias", ctypes.c_int32),
+                ("variant", ctypes.c_int32)]
+
+
+class LrqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_STATUS = {0: "LRQ_OK", 1: "LRQ_ERR_INVALID_ARG", 2: "LRQ_ERR_UNSUPPORTED", 3: "LRQ_ERR_HIP"}
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load liblrq.so once (raises OSError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise OSError(f"{path} not found: build it with `python -m layer_rmsnorm_qkv_amd.build`")
+        lib = ctypes.CDLL(path)
+        P, S = ctypes.c_void_p, ctypes.c_size_t
+        PP = ctypes.POINTER(ctypes.c_void_p)
+        lib.lrq_forward.argtypes = [ctypes.POINTER(LrqDesc), P, P, P, P, PP, PP, P, P, P, S, P]
+        lib.lrq_forward.restype = ctypes.c_int
+        lib.lrq_backward.argtypes = [ctypes.POINTER(LrqDesc), P, P, P, P, PP, PP, P, P, P, P, PP, PP, P, S, P]
+        lib.lrq_backward.restype = ctypes.c_int
+        lib.lrq_workspace_size.argtypes = [ctypes.POINTER(LrqDesc), ctypes.c_int]
+        lib.lrq_workspace_size.restype = ctypes.c_size_t
+        lib.lrq_select_variant.argtypes = [ctypes.POINTER(LrqDesc), ctypes.c_int]
+        lib.lrq_select_variant.restype = ctypes.c_int
+        lib.lrq_status_string.argtypes = [ctypes.c_int]
+        lib.lrq_status_string.restype = ctypes.c_char_p
+        lib.lrq_last_error.argtypes = []
+        lib.lrq_last_error.restype = ctypes.c_char_p
+        lib.lrq_abi_version.argtypes = []
+        lib.lrq_abi_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def make_desc(n_tokens, d_model, n_q_heads, n_kv_heads, head_dim, dtype, eps=1e-6, rope_theta=10000.0,
+              lora_rank=0, lora_alpha=0.0, lora_targets=0, has_bias=0, variant=LRQ_VARIANT_AUTO) -> LrqDesc:
+    return LrqDesc(int(n_tokens), int(d_model), int(n_q_heads), int(n_kv_heads), int(head_dim), int(dtype),
+                   float(eps), float(rope_theta), int(lora_rank), float(lora_alpha), int(lora_targets),
+                   int(has_bias), int(variant))
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t or None
+    return t.data_ptr()
+
+
+def _ptr3(ts: Optional[Sequence]):
+    if ts is None:
+        return None
+    vals = [_ptr(t) for t in ts] + [None] * (3 - len(ts))
+    return (ctypes.c_void_p * 3)(*vals[:3])
+
+
+def _stream(stream, tensors) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    for t in tensors:
+        if t is not None and not isinstance(t, int) and getattr(t, "is_cuda", False):
+            import torch
+            return torch.cuda.current_stream(t.device).cuda_stream
+    return None
+
+
+def _ws_bytes(workspace, workspace_bytes) -> int:
+    if workspace_bytes is not None:
+        return int(workspace_bytes)
+    if workspace is None or isinstance(workspace, int):
+        return 0
+    return workspace.numel() * workspace.element_size()
+
+
+def _check(st: int):
+    if st != LRQ_OK:
+        raise LrqError(st, load().lrq_last_error().decode())
+
+
+def lrq_forward(desc: LrqDesc, x, gamma, w_qkv, bias, lora_a, lora_b, positions, out,
+                workspace=None, workspace_bytes: Optional[int] = None, stream=None) -> None:
+    lib = load()
+    workspace_bytes = _ws_bytes(workspace, workspace_bytes)
+    st = lib.lrq_forward(ctypes.byref(desc), _ptr(x), _ptr(gamma), _ptr(w_qkv), _ptr(bias),
+                         _ptr3(lora_a), _ptr3(lora_b), _ptr(positions), _ptr(out), _ptr(workspace),
+                         int(workspace_bytes), _stream(stream, (x, out)))
+    _check(st)
+
+
+def lrq_backward(desc: LrqDesc, x, gamma, w_qkv, bias, lora_a, lora_b, positions, y, dy, dx,
+                 d_lora_a, d_lora_b, workspace=None, workspace_bytes: Optional[int] = None, stream=None) -> None:
+    lib = load()
+    workspace_bytes = _ws_bytes(workspace, workspace_bytes)
+    st = lib.lrq_backward(ctypes.byref(desc), _ptr(x), _ptr(gamma), _ptr(w_qkv), _ptr(bias),
+                          _ptr3(lora_a), _ptr3(lora_b), _ptr(positions), _ptr(y), _ptr(dy), _ptr(dx),
+                          _ptr3(d_lora_a), _ptr3(d_lora_b), _ptr(workspace), int(workspace_bytes),
+                          _stream(stream, (x, dx)))
+    _check(st)
+
+
+def lrq_workspace_size(desc: LrqDesc, for_backward: bool = False) -> int:
+    return int(load().lrq_workspace_size(ctypes.byref(desc), int(bool(for_backward))))
+
+
+def lrq_select_variant(desc: LrqDesc, for_backward: bool = False) -> int:
+    return int(load().lrq_select_variant(ctypes.byref(desc), int(bool(for_backward))))
+
+
+def lrq_status_string(status: int) -> str:
+    return load().lrq_status_string(int(status)).decode()
+
+
+def lrq_last_error() -> str:
+    return load().lrq_last_error().decode()
+
+
+def lrq_abi_version() -> int:
+    return int(load().lrq_abi_version())

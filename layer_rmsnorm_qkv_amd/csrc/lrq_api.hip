@@ -1,0 +1,271 @@
+// liblrq C ABI: host-side validation, kernel-family selection and launch.
+// Every check happens before anything is enqueued; see include/lrq.h for the contract.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "lrq.h"
+#include "lrq_internal.h"
+
+namespace lrq {
+bool bwd_generic_supports(const FwdParams& p);
+bool tiled_supports(const FwdParams& p);
+bool decode_supports(const FwdParams& p);
+bool bwd_tiled_supports(const FwdParams& p);
+size_t tiled_workspace_bytes(const FwdParams& p);
+size_t decode_workspace_bytes(const FwdParams& p);
+size_t bwd_tiled_workspace_bytes(const FwdParams& p);
+hipError_t launch_fwd_tiled(const FwdParams& p, hipStream_t s);
+hipError_t launch_fwd_decode(const FwdParams& p, hipStream_t s);
+hipError_t launch_bwd_tiled(const BwdParams& p, hipStream_t s);
+}  // namespace lrq
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+lrq_status fail(lrq_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+lrq_status ok() {
+  g_err[0] = '\0';
+  return LRQ_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Largest token count sent to the decode family when the choice is automatic.
+constexpr int64_t kDecodeMaxTokens = 256;
+
+// Checks the descriptor and fills the shape part of FwdParams.
+lrq_status check_desc(const lrq_desc* d, lrq::FwdParams& p) {
+  if (!d) return fail(LRQ_ERR_INVALID_ARG, "desc is NULL");
+  if (d->n_tokens < 0) return fail(LRQ_ERR_INVALID_ARG, "n_tokens < 0");
+  if (d->d_model < 1) return fail(LRQ_ERR_INVALID_ARG, "d_model < 1");
+  if (d->n_q_heads < 1 || d->n_kv_heads < 1) return fail(LRQ_ERR_INVALID_ARG, "head counts must be >= 1");
+  if (d->n_q_heads % d->n_kv_heads != 0) return fail(LRQ_ERR_INVALID_ARG, "n_q_heads %% n_kv_heads != 0");
+  if (d->head_dim < 2 || (d->head_dim & 1)) return fail(LRQ_ERR_INVALID_ARG, "head_dim must be even and >= 2");
+  if (d->dtype != LRQ_F32 && d->dtype != LRQ_BF16) return fail(LRQ_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
+  if (!std::isfinite(d->eps) || d->eps < 0.f) return fail(LRQ_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!std::isfinite(d->rope_theta) || d->rope_theta <= 0.f)
+    return fail(LRQ_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
+  if (d->lora_targets & ~7u) return fail(LRQ_ERR_INVALID_ARG, "lora_targets has unknown bits");
+  if (d->lora_targets) {
+    if (d->lora_rank < 1) return fail(LRQ_ERR_INVALID_ARG, "lora_rank < 1 with targets set");
+    if (!std::isfinite(d->lora_alpha)) return fail(LRQ_ERR_INVALID_ARG, "lora_alpha not finite");
+  }
+  if (d->has_bias != 0 && d->has_bias != 1) return fail(LRQ_ERR_INVALID_ARG, "has_bias must be 0 or 1");
+  if (d->variant < LRQ_VARIANT_AUTO || d->variant > LRQ_VARIANT_DECODE)
+    return fail(LRQ_ERR_INVALID_ARG, "unknown variant %d", d->variant);
+  const int64_t N = static_cast<int64_t>(d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim;
+  if (N > (1 << 24) || d->d_model > (1 << 24) || d->n_tokens > (int64_t{1} << 31) - 1)
+    return fail(LRQ_ERR_UNSUPPORTED, "sizes beyond the supported range");
+  if (d->lora_targets && d->lora_rank > LRQ_MAX_LORA_RANK)
+    return fail(LRQ_ERR_UNSUPPORTED, "lora_rank %d > %d", d->lora_rank, LRQ_MAX_LORA_RANK);
+
+  std::memset(&p, 0, sizeof p);
+  p.T = d->n_tokens;
+  p.d = d->d_model;
+  p.Hq = d->n_q_heads;
+  p.Hkv = d->n_kv_heads;
+  p.D = d->head_dim;
+  p.N = static_cast<int>(N);
+  p.col_k = d->n_q_heads * d->head_dim;
+  p.col_v = (d->n_q_heads + d->n_kv_heads) * d->head_dim;
+  p.rot_end = p.col_v;
+  p.eps = d->eps;
+  p.theta = static_cast<double>(d->rope_theta);
+  p.targets = d->lora_targets;
+  p.r = d->lora_targets ? d->lora_rank : 0;
+  p.scale = d->lora_targets ? d->lora_alpha / static_cast<float>(d->lora_rank) : 0.f;
+  p.has_bias = d->has_bias;
+  return LRQ_OK;
+}
+
+// Kernel family for a valid descriptor, or -1 (message set) if the forced one cannot run.
+int select(const lrq_desc* d, const lrq::FwdParams& p, bool backward) {
+  if (backward) {
+    const bool tiled = d->dtype == LRQ_BF16 && lrq::bwd_tiled_supports(p);
+    if (d->variant == LRQ_VARIANT_AUTO) {
+      if (tiled) return LRQ_VARIANT_TILED;
+      if (lrq::bwd_generic_supports(p)) return LRQ_VARIANT_GENERIC;
+      fail(LRQ_ERR_UNSUPPORTED, "no backward kernel covers this shape");
+      return -1;
+    }
+    if (d->variant == LRQ_VARIANT_GENERIC && lrq::bwd_generic_supports(p)) return LRQ_VARIANT_GENERIC;
+    if (d->variant == LRQ_VARIANT_TILED && tiled) return LRQ_VARIANT_TILED;
+    fail(LRQ_ERR_UNSUPPORTED, "backward variant %d cannot run this shape", d->variant);
+    return -1;
+  }
+  const bool bf16 = d->dtype == LRQ_BF16;
+  const bool tiled = bf16 && lrq::tiled_supports(p);
+  const bool decode = bf16 && lrq::decode_supports(p);
+  switch (d->variant) {
+    case LRQ_VARIANT_AUTO:
+      if (decode && p.T <= kDecodeMaxTokens) return LRQ_VARIANT_DECODE;
+      if (tiled) return LRQ_VARIANT_TILED;
+      return LRQ_VARIANT_GENERIC;
+    case LRQ_VARIANT_GENERIC:
+      return LRQ_VARIANT_GENERIC;
+    case LRQ_VARIANT_TILED:
+      if (tiled) return LRQ_VARIANT_TILED;
+      break;
+    case LRQ_VARIANT_DECODE:
+      if (decode) return LRQ_VARIANT_DECODE;
+      break;
+  }
+  fail(LRQ_ERR_UNSUPPORTED, "forward variant %d cannot run this shape", d->variant);
+  return -1;
+}
+
+size_t workspace_for(int variant, const lrq::FwdParams& p, bool backward) {
+  if (backward) return variant == LRQ_VARIANT_TILED ? lrq::bwd_tiled_workspace_bytes(p) : 0;
+  if (variant == LRQ_VARIANT_TILED) return lrq::tiled_workspace_bytes(p);
+  if (variant == LRQ_VARIANT_DECODE) return lrq::decode_workspace_bytes(p);
+  return 0;
+}
+
+lrq_status check_common_ptrs(const lrq_desc* d, lrq::FwdParams& p, const void* x, const void* gamma,
+                             const void* w, const void* bias, const void* const* a, const void* const* b,
+                             const int32_t* pos) {
+  if (p.T > 0 && (!x || !gamma || !w || !pos)) return fail(LRQ_ERR_INVALID_ARG, "x, gamma, w_qkv and positions are required");
+  if (d->has_bias && !bias) return fail(LRQ_ERR_INVALID_ARG, "bias is NULL with has_bias");
+  if (d->lora_targets && (!a || !b)) return fail(LRQ_ERR_INVALID_ARG, "lora_a / lora_b arrays are NULL");
+  for (int t = 0; t < 3; ++t)
+    if ((d->lora_targets & (1u << t)) && (!a[t] || !b[t]))
+      return fail(LRQ_ERR_INVALID_ARG, "lora_a[%d] / lora_b[%d] is NULL for a target", t, t);
+  const void* all[] = {x, gamma, w, d->has_bias ? bias : nullptr, pos};
+  for (const void* q : all)
+    if (q && !aligned16(q)) return fail(LRQ_ERR_UNSUPPORTED, "array pointers must be 16-byte aligned");
+  p.x = x;
+  p.gamma = gamma;
+  p.w = w;
+  p.bias = d->has_bias ? bias : nullptr;
+  p.pos = pos;
+  for (int t = 0; t < 3; ++t) {
+    if (!(d->lora_targets & (1u << t))) continue;
+    if (!aligned16(a[t]) || !aligned16(b[t])) return fail(LRQ_ERR_UNSUPPORTED, "LoRA pointers must be 16-byte aligned");
+    p.a[t] = a[t];
+    p.b[t] = b[t];
+  }
+  return LRQ_OK;
+}
+
+lrq_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(LRQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int lrq_abi_version(void) { return LRQ_ABI_VERSION; }
+
+const char* lrq_status_string(lrq_status s) {
+  switch (s) {
+    case LRQ_OK: return "LRQ_OK";
+    case LRQ_ERR_INVALID_ARG: return "LRQ_ERR_INVALID_ARG";
+    case LRQ_ERR_UNSUPPORTED: return "LRQ_ERR_UNSUPPORTED";
+    case LRQ_ERR_HIP: return "LRQ_ERR_HIP";
+  }
+  return "LRQ_UNKNOWN_STATUS";
+}
+
+const char* lrq_last_error(void) { return g_err; }
+
+int lrq_select_variant(const lrq_desc* desc, int for_backward) {
+  lrq::FwdParams p;
+  if (check_desc(desc, p) != LRQ_OK) return -1;
+  return select(desc, p, for_backward != 0);
+}
+
+size_t lrq_workspace_size(const lrq_desc* desc, int for_backward) {
+  lrq::FwdParams p;
+  if (check_desc(desc, p) != LRQ_OK) return 0;
+  const int v = select(desc, p, for_backward != 0);
+  if (v < 0) return 0;
+  return workspace_for(v, p, for_backward != 0);
+}
+
+lrq_status lrq_forward(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,
+                       const void* bias, const void* const* lora_a, const void* const* lora_b,
+                       const int32_t* positions, void* out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  lrq::FwdParams p;
+  lrq_status st = check_desc(desc, p);
+  if (st != LRQ_OK) return st;
+  st = check_common_ptrs(desc, p, x, gamma, w_qkv, bias, lora_a, lora_b, positions);
+  if (st != LRQ_OK) return st;
+  if (p.T > 0 && !out) return fail(LRQ_ERR_INVALID_ARG, "out is NULL");
+  if (out && !aligned16(out)) return fail(LRQ_ERR_UNSUPPORTED, "out must be 16-byte aligned");
+  const int v = select(desc, p, false);
+  if (v < 0) return LRQ_ERR_UNSUPPORTED;
+  const size_t need = workspace_for(v, p, false);
+  if (workspace_bytes < need) return fail(LRQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", workspace_bytes, need);
+  if (need > 0 && !workspace) return fail(LRQ_ERR_INVALID_ARG, "workspace is NULL");
+  if (p.T == 0) return ok();
+  p.out = out;
+  p.ws = workspace;
+  p.ws_bytes = workspace_bytes;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (v) {
+    case LRQ_VARIANT_TILED: e = lrq::launch_fwd_tiled(p, s); break;
+    case LRQ_VARIANT_DECODE: e = lrq::launch_fwd_decode(p, s); break;
+    default:
+      e = desc->dtype == LRQ_F32 ? lrq::launch_fwd_generic_f32(p, s) : lrq::launch_fwd_generic_bf16(p, s);
+  }
+  return hip_status(e, "forward launch");
+}
+
+lrq_status lrq_backward(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,
+                        const void* bias, const void* const* lora_a, const void* const* lora_b,
+                        const int32_t* positions, const void* y, const void* dy, void* dx,
+                        float* const* d_lora_a, float* const* d_lora_b, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  lrq::BwdParams bp;
+  std::memset(&bp, 0, sizeof bp);
+  lrq_status st = check_desc(desc, bp.f);
+  if (st != LRQ_OK) return st;
+  st = check_common_ptrs(desc, bp.f, x, gamma, w_qkv, bias, lora_a, lora_b, positions);
+  if (st != LRQ_OK) return st;
+  if (bp.f.T > 0 && (!y || !dy || !dx)) return fail(LRQ_ERR_INVALID_ARG, "y, dy and dx are required");
+  for (const void* q : {y, dy, static_cast<const void*>(dx)})
+    if (q && !aligned16(q)) return fail(LRQ_ERR_UNSUPPORTED, "y, dy, dx must be 16-byte aligned");
+  if (desc->lora_targets && (!d_lora_a || !d_lora_b)) return fail(LRQ_ERR_INVALID_ARG, "d_lora_a / d_lora_b arrays are NULL");
+  for (int t = 0; t < 3; ++t) {
+    if (!(desc->lora_targets & (1u << t))) continue;
+    if (!d_lora_a[t] || !d_lora_b[t]) return fail(LRQ_ERR_INVALID_ARG, "d_lora_a[%d] / d_lora_b[%d] is NULL", t, t);
+    if (!aligned16(d_lora_a[t]) || !aligned16(d_lora_b[t]))
+      return fail(LRQ_ERR_UNSUPPORTED, "LoRA gradient pointers must be 16-byte aligned");
+    bp.da[t] = d_lora_a[t];
+    bp.db[t] = d_lora_b[t];
+  }
+  const int v = select(desc, bp.f, true);
+  if (v < 0) return LRQ_ERR_UNSUPPORTED;
+  const size_t need = workspace_for(v, bp.f, true);
+  if (workspace_bytes < need) return fail(LRQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", workspace_bytes, need);
+  if (need > 0 && !workspace) return fail(LRQ_ERR_INVALID_ARG, "workspace is NULL");
+  if (bp.f.T == 0 && !desc->lora_targets) return ok();
+  bp.y = y;
+  bp.dy = dy;
+  bp.dx = dx;
+  bp.f.ws = workspace;
+  bp.f.ws_bytes = workspace_bytes;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (v == LRQ_VARIANT_TILED)
+    e = lrq::launch_bwd_tiled(bp, s);
+  else
+    e = desc->dtype == LRQ_F32 ? lrq::launch_bwd_generic_f32(bp, s) : lrq::launch_bwd_generic_bf16(bp, s);
+  return hip_status(e, "backward launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Internal declarations shared by the liblrq translation units (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lrq {
+
+constexpr int kMaxRank = 64;  // LRQ_MAX_LORA_RANK
+
+// Everything a forward launch needs, resolved on the host from lrq_desc.
+struct FwdParams {
+  int64_t T;        // tokens
+  int64_t d;        // model dim
+  int Hq, Hkv, D;   // heads and head size
+  int N;            // (Hq + 2 Hkv) * D
+  int col_k;        // first k column = Hq * D
+  int col_v;        // first v column = (Hq + Hkv) * D
+  int rot_end;      // columns [0, rot_end) are rotated = col_v
+  float eps;
+  float scale;      // alpha / r (0 without targets)
+  double theta;
+  int r;            // LoRA rank (0 without targets)
+  uint32_t targets; // bit t set: target t (0 q, 1 k, 2 v) has an adapter
+  int has_bias;
+  const void* x;
+  const void* gamma;
+  const void* w;
+  const void* bias;
+  const void* a[3];
+  const void* b[3];
+  const int32_t* pos;
+  void* out;
+  void* ws;
+  size_t ws_bytes;
+};
+
+struct BwdParams {
+  FwdParams f;      // out unused
+  const void* y;
+  const void* dy;
+  void* dx;
+  float* da[3];
+  float* db[3];
+};
+
+// Column range [lo, hi) of target t.
+__host__ __device__ inline void target_cols(const FwdParams& p, int t, int& lo, int& hi) {
+  lo = t == 0 ? 0 : (t == 1 ? p.col_k : p.col_v);
+  hi = t == 0 ? p.col_k : (t == 1 ? p.col_v : p.N);
+}
+
+// ---- launchers (defined in the kernel translation units) ----
+hipError_t launch_fwd_generic_f32(const FwdParams& p, hipStream_t s);
+hipError_t launch_fwd_generic_bf16(const FwdParams& p, hipStream_t s);
+hipError_t launch_bwd_generic_f32(const BwdParams& p, hipStream_t s);
+hipError_t launch_bwd_generic_bf16(const BwdParams& p, hipStream_t s);
+bool bwd_generic_supports(const FwdParams& p);
+
+// ---- device helpers ----
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t u) {
+  return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+// Round-to-nearest-even float -> bfloat16 (hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+__device__ __forceinline__ float round_bf16(float f) { return bf16_bits_to_f32(f32_to_bf16_bits(f)); }
+
+__device__ __forceinline__ float load_elem(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_elem(const uint16_t* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+__device__ __forceinline__ void store_elem(float* p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void store_elem(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16_bits(v); }
+
+// RoPE frequency omega_i = theta^(-2i/D) in double precision.
+__device__ __forceinline__ double rope_omega(double theta, int i, int D) {
+  return exp2(-(2.0 * i / D) * log2(theta));
+}
+
+// cos/sin of pos * omega.  The angle is formed and reduced to [-pi, pi] in double
+// precision, so large positions lose no accuracy before the float32 sincos.
+__device__ __forceinline__ void rope_cos_sin(int pos, double omega, float& c, float& s) {
+  const double two_pi = 6.283185307179586476925286766559;
+  double phi = static_cast<double>(pos) * omega;
+  double k = rint(phi * (1.0 / two_pi));
+  double red = fma(-k, two_pi, phi);
+  sincosf(static_cast<float>(red), &s, &c);
+}
+
+}  // namespace lrq

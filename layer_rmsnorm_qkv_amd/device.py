@@ -1,0 +1,75 @@
+"""Device buffers for one call of the operator (torch for memory and streams only).
+
+``DeviceProblem`` uploads the host arrays of a workload (see ``workloads``) to torch
+device tensors of the workload dtype -- the values are exactly representable, so the
+cast is exact -- builds the ``lrq_desc`` and calls the binding.  No arithmetic of the
+operator happens here.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+
+from . import binding as B
+from .workloads import TARGET_K, TARGET_Q, TARGET_V, Workload
+
+
+def torch_dtype(w: Workload):
+    import torch
+    return torch.float32 if w.dtype == "f32" else torch.bfloat16
+
+
+def desc_for(w: Workload, n_tokens: Optional[int] = None, variant: int = B.LRQ_VARIANT_AUTO) -> B.LrqDesc:
+    return B.make_desc(w.n_tokens if n_tokens is None else n_tokens, w.d_model, w.n_q_heads, w.n_kv_heads,
+                       w.head_dim, B.LRQ_F32 if w.dtype == "f32" else B.LRQ_BF16, w.eps, w.rope_theta,
+                       w.lora_rank if w.lora_targets else 0, w.lora_alpha, w.lora_targets,
+                       1 if w.has_bias else 0, variant)
+
+
+class DeviceProblem:
+    """All device tensors of one forward (+ backward) call."""
+
+    def __init__(self, w: Workload, inputs: Dict[str, object], device: str = "cuda",
+                 variant: int = B.LRQ_VARIANT_AUTO, backward: bool = False):
+        import torch
+        self.w = w
+        dt = torch_dtype(w)
+        T = inputs["x"].shape[0]
+        self.T = T
+        self.desc = desc_for(w, T, variant)
+
+        def up(a):
+            return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dt)
+
+        self.x = up(inputs["x"])
+        self.gamma = up(inputs["gamma"])
+        self.w_qkv = up(inputs["w"])
+        self.bias = up(inputs["bias"])
+        self.a = [up(inputs["a"].get(t)) for t in (TARGET_Q, TARGET_K, TARGET_V)]
+        self.b = [up(inputs["b"].get(t)) for t in (TARGET_Q, TARGET_K, TARGET_V)]
+        self.positions = torch.from_numpy(np.ascontiguousarray(inputs["positions"], dtype=np.int32)).to(device)
+        self.out = torch.empty((T, w.n_out), dtype=dt, device=device)
+        self.variant = B.lrq_select_variant(self.desc, False)
+        ws = B.lrq_workspace_size(self.desc, False)
+        self.dy = self.dx = None
+        self.da = self.db = None
+        if backward:
+            self.dy = up(inputs["dy"])
+            self.dx = torch.empty((T, w.d_model), dtype=dt, device=device)
+            self.da = [torch.empty_like(a, dtype=torch.float32) if a is not None else None for a in self.a]
+            self.db = [torch.empty_like(b, dtype=torch.float32) if b is not None else None for b in self.b]
+            self.bwd_variant = B.lrq_select_variant(self.desc, True)
+            ws = max(ws, B.lrq_workspace_size(self.desc, True))
+        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device) if ws > 0 else None
+
+    def forward(self, stream=None, out=None):
+        B.lrq_forward(self.desc, self.x, self.gamma, self.w_qkv, self.bias, self.a, self.b, self.positions,
+                      self.out if out is None else out, self.workspace, stream=stream)
+        return self.out if out is None else out
+
+    def backward(self, y=None, stream=None):
+        B.lrq_backward(self.desc, self.x, self.gamma, self.w_qkv, self.bias, self.a, self.b, self.positions,
+                       self.out if y is None else y, self.dy, self.dx, self.da, self.db, self.workspace,
+                       stream=stream)
+        return self.dx, self.da, self.db

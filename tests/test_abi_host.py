@@ -1,0 +1,149 @@
+"""The C-ABI library on the host: it loads, exports every symbol include/lrq.h declares,
+its descriptor layout matches the header, and every argument check fires before any
+launch.  No call here reaches a kernel launch (every call with non-NULL addresses is
+invalid by construction), and these tests are skipped where a GPU is visible so that a
+regression in validation can never turn into a launch with made-up addresses."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from layer_rmsnorm_qkv_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lrq.h")
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:  # noqa: BLE001
+        return False
+
+
+pytestmark = [pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="liblrq.so not built"),
+              pytest.mark.skipif(_gpu_visible(), reason="host-only checks use made-up addresses")]
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lrq_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = B.load()
+    syms = declared_symbols()
+    assert set(syms) == set(B.EXPORTED), syms
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert B.lrq_abi_version() == 1
+
+
+def test_desc_layout_matches_header(tmp_path):
+    fields = [f for f, _ in B.LrqDesc._fields_]
+    src = tmp_path / "layout.c"
+    body = "\n".join(f'  printf("{f} %zu\\n", offsetof(lrq_desc, {f}));' for f in fields)
+    src.write_text(f'#include <stdio.h>\n#include <stddef.h>\n#include "lrq.h"\n'
+                   f'int main(void) {{\n{body}\n  printf("size %zu\\n", sizeof(lrq_desc));\n  return 0;\n}}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src),
+                    "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                       check=True).stdout.splitlines())
+    for f in fields:
+        assert int(got[f]) == getattr(B.LrqDesc, f).offset, f
+    assert int(got["size"]) == ctypes.sizeof(B.LrqDesc)
+
+
+def test_status_strings():
+    assert [B.lrq_status_string(i) for i in range(4)] == \
+        ["LRQ_OK", "LRQ_ERR_INVALID_ARG", "LRQ_ERR_UNSUPPORTED", "LRQ_ERR_HIP"]
+    assert B.lrq_status_string(99) == "LRQ_UNKNOWN_STATUS"
+
+
+def good_desc(**kw):
+    base = dict(n_tokens=8, d_model=64, n_q_heads=4, n_kv_heads=2, head_dim=16, dtype=B.LRQ_F32, eps=1e-6,
+                rope_theta=1e4, lora_rank=4, lora_alpha=8.0, lora_targets=B.LRQ_TARGET_Q | B.LRQ_TARGET_V,
+                has_bias=0)
+    base.update(kw)
+    return B.make_desc(**base)
+
+
+def fwd(desc, **over):
+    args = dict(x=FAKE, gamma=FAKE, w_qkv=FAKE, bias=None, lora_a=[FAKE, None, FAKE], lora_b=[FAKE, None, FAKE],
+                positions=FAKE, out=FAKE, workspace=None, stream=None)
+    args.update(over)
+    B.lrq_forward(desc, **args)
+
+
+def expect(status, fn, *a, **k):
+    with pytest.raises(B.LrqError) as ei:
+        fn(*a, **k)
+    assert ei.value.status == status, str(ei.value)
+    assert B.lrq_last_error() != ""
+
+
+@pytest.mark.parametrize("field,value", [
+    ("n_tokens", -1), ("d_model", 0), ("n_q_heads", 0), ("n_kv_heads", 0), ("n_q_heads", 3),
+    ("head_dim", 15), ("head_dim", 0), ("dtype", 7), ("eps", -1.0), ("eps", float("nan")),
+    ("rope_theta", 0.0), ("rope_theta", float("inf")), ("lora_targets", 8), ("lora_rank", 0),
+    ("lora_alpha", float("nan")), ("has_bias", 2), ("variant", 9)])
+def test_invalid_descriptor(field, value):
+    expect(B.LRQ_ERR_INVALID_ARG, fwd, good_desc(**{field: value}))
+    assert B.lrq_workspace_size(good_desc(**{field: value})) == 0
+    assert B.lrq_select_variant(good_desc(**{field: value})) == -1
+
+
+@pytest.mark.parametrize("over", [dict(x=None), dict(gamma=None), dict(w_qkv=None), dict(positions=None),
+                                  dict(out=None), dict(lora_a=None), dict(lora_b=[FAKE, None, None]),
+                                  dict(lora_a=[None, None, FAKE])])
+def test_missing_pointer(over):
+    expect(B.LRQ_ERR_INVALID_ARG, fwd, good_desc(), **over)
+
+
+def test_bias_required_and_alignment():
+    expect(B.LRQ_ERR_INVALID_ARG, fwd, good_desc(has_bias=1), bias=None)
+    expect(B.LRQ_ERR_UNSUPPORTED, fwd, good_desc(n_tokens=8, has_bias=1, eps=-1.0 + 1.0), bias=FAKE + 2,
+           x=FAKE + 2)
+    expect(B.LRQ_ERR_UNSUPPORTED, fwd, good_desc(lora_rank=65))
+
+
+def test_forced_variant_that_cannot_run():
+    # fp32 cannot use the bf16 MFMA families
+    for v in (B.LRQ_VARIANT_TILED, B.LRQ_VARIANT_DECODE):
+        assert B.lrq_select_variant(good_desc(variant=v)) == -1
+        expect(B.LRQ_ERR_UNSUPPORTED, fwd, good_desc(variant=v))
+    assert B.lrq_select_variant(good_desc()) == B.LRQ_VARIANT_GENERIC
+    assert B.lrq_select_variant(good_desc(), for_backward=True) == B.LRQ_VARIANT_GENERIC
+
+
+def test_zero_tokens_is_a_noop():
+    # T == 0: valid, nothing is launched, pointers may be NULL
+    B.lrq_forward(good_desc(n_tokens=0), None, None, None, None, [FAKE, None, FAKE], [FAKE, None, FAKE],
+                  None, None)
+    B.lrq_forward(good_desc(n_tokens=0, lora_targets=0), None, None, None, None, None, None, None, None)
+
+
+def test_backward_checks():
+    def bwd(desc, **over):
+        args = dict(x=FAKE, gamma=FAKE, w_qkv=FAKE, bias=None, lora_a=[FAKE, None, FAKE],
+                    lora_b=[FAKE, None, FAKE], positions=FAKE, y=FAKE, dy=FAKE, dx=FAKE,
+                    d_lora_a=[FAKE, None, FAKE], d_lora_b=[FAKE, None, FAKE])
+        args.update(over)
+        B.lrq_backward(desc, **args)
+    for over in (dict(y=None), dict(dy=None), dict(dx=None), dict(d_lora_a=None),
+                 dict(d_lora_b=[FAKE, None, None])):
+        expect(B.LRQ_ERR_INVALID_ARG, bwd, good_desc(), **over)
+    expect(B.LRQ_ERR_INVALID_ARG, bwd, good_desc(head_dim=3))
+    expect(B.LRQ_ERR_UNSUPPORTED, bwd, good_desc(), dy=FAKE + 4)
+
+
+def test_workspace_queries():
+    assert B.lrq_workspace_size(good_desc()) == 0  # the generic family needs none
+    assert B.lrq_workspace_size(good_desc(), True) == 0
