@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused RMSNorm -> QKV(+LoRA) -> RoPE operator on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama3|llama2|decode|train|tiny]
+
+A step is one call of the whole operator on one batch of synthetic, seeded input that is
+already resident in HBM: the forward for the layer and decode workloads, forward then
+backward for the training workload.  W untimed warm-up steps, then K timed steps between
+two device synchronisations; one JSON line is printed.
+
+* ``value``: tokens per second of the whole job (one GPU).
+* ``roofline``: the dominant kernel's algorithmic FLOPs (or bytes, for the bandwidth-bound
+  decode workload) per launch over its average launch duration, timed with HIP events on
+  the stream it is launched on, against MI355X's published peak (bf16 dense MFMA
+  2500 TFLOP/s, HBM 8000 GB/s).  ``traffic`` comes from rocprofv3 FETCH_SIZE/WRITE_SIZE
+  counters recorded under profiles/ for the same kernel source (null if the source changed).
+* ``cpu_baseline``: the CPU oracle (float64 numpy, untuned) timed on this host on a bounded
+  sample of the same workload's rows.
+
+``--copy-probe`` instead runs a plain device copy of known size (the calibration kernel for
+the FETCH_SIZE / WRITE_SIZE counters).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused RMSNorm+LoRA-QKV+RoPE tokens/s, TFLOP/s (% MFMA peak) on 1×MI355X"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def algorithmic_work(w, T=None):
+    """Matmul FLOPs (forward, backward) and forward bytes of one call; RMSNorm, bias and RoPE
+    are O(T (d + N)) and not counted, nor is any recomputation."""
+    T = w.n_tokens if T is None else T
+    d, N, r = w.d_model, w.n_out, w.lora_rank
+    cols = w.target_columns()
+    f_fwd = 2.0 * T * d * N
+    f_bwd = 2.0 * T * N * d
+    lora_bytes = 0
+    for t, (lo, hi) in cols.items():
+        if w.lora_targets & t:
+            nt = hi - lo
+            f_fwd += 2.0 * T * d * r + 2.0 * T * r * nt
+            # V = G B, dh += s V A, U recompute, dB = G^T U, dA = V^T h
+            f_bwd += 2.0 * T * nt * r + 2.0 * T * r * d + 2.0 * T * d * r + 2.0 * T * nt * r + 2.0 * T * r * d
+            lora_bytes += (r * d + nt * r)
+    eb = 4 if w.dtype == "f32" else 2
+    bytes_fwd = eb * (T * d + d + N * d + (N if w.has_bias else 0) + lora_bytes + T * N) + 4 * T
+    return f_fwd, f_bwd, bytes_fwd
+
+
+def kernel_source_digest(variant_name: str) -> str:
+    """sha256 of the sources that define a kernel family (for matching stored counters)."""
+    files = {"tiled": ["fwd_tiled.hip"], "decode": ["fwd_decode.hip"], "generic": ["fwd_generic.hip"],
+             "bwd_tiled": ["bwd_tiled.hip"], "bwd_generic": ["bwd_generic.hip"]}[variant_name]
+    h = hashlib.sha256()
+    for f in files + ["lrq_internal.h"]:
+        p = os.path.join(ROOT, "layer_rmsnorm_qkv_amd", "csrc", f)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, kernel: str):
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    rec = data.get(f"{workload}:{kernel}")
+    if not rec or rec.get("source_sha") != kernel_source_digest(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, budget_s: float, rows_cap: int, gpu_rows_fn=None):
+    """Time the float64 oracle on a bounded, seeded sample of rows of the same workload."""
+    import numpy as np
+    import oracle.lrq_oracle as o
+    try:
+        import threadpoolctl
+        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001
+        threads = 1
+    spec = o.Spec(d_model=w.d_model, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
+                  lora_rank=w.lora_rank if w.lora_targets else 0, lora_alpha=w.lora_alpha,
+                  lora_targets=w.lora_targets, eps=w.eps, rope_theta=w.rope_theta)
+    T = w.n_tokens
+    rng = np.random.default_rng(12345)
+    order = rng.permutation(T)
+
+    def run(rows):
+        t0 = time.perf_counter()
+        out = o.forward_rows(spec, rows, inp["x"], inp["gamma"], inp["w"], inp["bias"], inp["a"], inp["b"],
+                             inp["positions"])
+        if w.backward:
+            o.backward(spec, inp["x"][rows], inp["gamma"], inp["w"], inp["bias"], inp["a"], inp["b"],
+                       inp["positions"][rows], inp["dy"][rows])
+        return time.perf_counter() - t0, out
+
+    probe = min(T, 32)
+    dt, _ = run(np.sort(order[:probe]))
+    n = int(min(T, rows_cap, max(probe, probe * budget_s / max(dt, 1e-6))))
+    rows = np.sort(order[:n])
+    dt, out = run(rows)
+    res = {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n} of {T} rows (seeded), {'forward+backward' if w.backward else 'forward'}, "
+                     f"float64 numpy, {dt:.2f} s"}
+    if gpu_rows_fn is not None:  # the same rows from the GPU forward, for a parity figure
+        res["gpu_parity_rel_fro"] = o.rel_frobenius(gpu_rows_fn(rows), out)
+    return res
+
+
+def copy_probe(nbytes: int, reps: int):
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3", choices=["tiny", "llama3", "llama2", "decode", "train"])
+    ap.add_argument("--variant", default="auto", choices=["auto", "generic", "tiled", "decode"])
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--w-copies", type=int, default=0,
+                    help="rotate among this many W_qkv copies (defeats the 256 MB MALL; default 4 for decode)")
+    ap.add_argument("--copy-probe", type=int, default=0, help="run a device copy of this many bytes and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this operator is measured on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path shards by tokens with no communication in the forward).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe, 5)
+        return
+
+    from layer_rmsnorm_qkv_amd import binding as B
+    from layer_rmsnorm_qkv_amd import workloads as wl
+    from layer_rmsnorm_qkv_amd.device import DeviceProblem, desc_for
+
+    B.load()
+    w = wl.get(args.workload)
+    variant = {"auto": B.LRQ_VARIANT_AUTO, "generic": B.LRQ_VARIANT_GENERIC, "tiled": B.LRQ_VARIANT_TILED,
+               "decode": B.LRQ_VARIANT_DECODE}[args.variant]
+    inp = wl.make_inputs(w, with_dy=w.backward)
+    prob = DeviceProblem(w, inp, variant=variant, backward=w.backward)
+    vname = B.VARIANT_NAMES[prob.variant]
+    stream = torch.cuda.current_stream()
+
+    n_copies = args.w_copies or (4 if w.name == "decode" else 1)
+    w_list = [prob.w_qkv] + [prob.w_qkv.clone() for _ in range(n_copies - 1)]
+
+    def step(i):
+        prob.w_qkv = w_list[i % n_copies]
+        prob.forward(stream=stream)
+        if w.backward:
+            prob.backward(stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # per-call HIP events on the launch stream: the forward call is one kernel launch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        e0, e1, e2 = ev[i]
+        prob.w_qkv = w_list[i % n_copies]
+        e0.record(stream)
+        prob.forward(stream=stream)
+        e1.record(stream)
+        if w.backward:
+            prob.backward(stream=stream)
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    bwd_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev])) if w.backward else 0.0
+
+    ms_per_step = wall * 1e3 / args.steps
+    tokens = w.n_tokens
+    f_fwd, f_bwd, bytes_fwd = algorithmic_work(w)
+    result = {
+        "metric": METRIC, "value": tokens / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32" if w.dtype == "f32" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "tokens": tokens, "d_model": w.d_model,
+                   "n_out": w.n_out, "lora_rank": w.lora_rank, "lora_targets": w.lora_targets,
+                   "kernel_family": vname, "parallelism": "none (1 GPU)",
+                   "pass": "forward+backward" if w.backward else "forward"},
+    }
+    # dominant kernel: the forward kernel (layer / decode workloads) or the larger of the two calls
+    tflops_fwd = f_fwd / (fwd_ms * 1e-3) / 1e12
+    result["tflops_forward"] = tflops_fwd
+    if w.backward:
+        result["tflops_backward"] = f_bwd / (bwd_ms * 1e-3) / 1e12
+        result["tflops_step"] = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
+    if w.name == "decode":
+        gbs = bytes_fwd / (fwd_ms * 1e-3) / 1e9
+        traffic = stored_traffic(w.name, vname)
+        result["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": gbs / PEAK_HBM_GBS, "traffic": traffic, "kernel": f"lrq forward ({vname})",
+                              "launch_ms": fwd_ms, "algorithmic_bytes": bytes_fwd}
+    else:
+        dom_ms, dom_f, dom_name = fwd_ms, f_fwd, vname
+        if w.backward and bwd_ms > fwd_ms:
+            dom_ms, dom_f, dom_name = bwd_ms, f_bwd, "bwd_" + B.VARIANT_NAMES[prob.bwd_variant]
+        ach = dom_f / (dom_ms * 1e-3) / 1e12
+        peak = PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+        result["roofline"] = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                              "frac": ach / peak, "traffic": stored_traffic(w.name, dom_name),
+                              "kernel": f"lrq {'backward' if dom_name.startswith('bwd') else 'forward'} ({dom_name})",
+                              "launch_ms": dom_ms, "algorithmic_flop": dom_f}
+    if not args.no_cpu_baseline:
+        prob.w_qkv = w_list[0]
+        got = prob.forward(stream=stream)
+        torch.cuda.synchronize()
+        got = got.float().cpu().numpy().astype(np.float64)
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, rows_cap=w.n_tokens,
+                                              gpu_rows_fn=lambda rows: got[rows])
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
