@@ -51,6 +51,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(path):
             raise OSError(f"{path} not found: build it with `python -m layer_rmsnorm_qkv_amd.build`")
+        # The library must bind to the HIP runtime that owns the caller's device memory and
+        # streams.  PyTorch-ROCm ships its own libamdhip64.so.7; loading torch first makes the
+        # dynamic linker resolve liblrq's libamdhip64.so.7 to that same copy.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         lib = ctypes.CDLL(path)
         P, S = ctypes.c_void_p, ctypes.c_size_t
         PP = ctypes.POINTER(ctypes.c_void_p)
