@@ -52,9 +52,8 @@ constexpr int kSlices = BK / 16;             // 16-wide MFMA K slices per step
 constexpr int kLdsMax = 160 * 1024;
 
 // LDS map for RB blocks of 32 LoRA ranks.  The stage ring holds two steps of x and W'.
-// The U pass stages the rows of A'_t in the W' half (it does not read W').  After a tile's
-// K-loop the x half is free until the next tile starts; the epilogue keeps the rows' inv
-// and positions there.
+// The U pass stages the rows of A'_t in the W' half (it does not read W').  The rows' inv
+// and positions live in registers (two per lane, for the wave pair's 128 rows).
 template <int RB>
 struct Lay {
   static constexpr int X = 0;                          // 2 x [256][64] bf16, x
@@ -63,8 +62,7 @@ struct Lay {
   static constexpr int kLStage = RB * 32 * kRowBytes;
   static constexpr int U = 4 * kTileBytes;             // [256][32 RB] bf16, bf16(s U)
   static constexpr int kUStride = RB * 32;
-  static constexpr int INV = X;                        // float [256] (epilogue only)
-  static constexpr int POS = X + BM * 4;               // int [256] (epilogue only)
+  static constexpr int TMP = X;                        // float [256]: row sums, once per run
   static constexpr int kBytes = U + BM * kUStride * 2;
   static_assert(kBytes <= kLdsMax, "LDS budget");
   static_assert(2 * kLStage <= 2 * kTileBytes, "A' stages fit in the W' half");
@@ -153,7 +151,7 @@ __device__ __forceinline__ void sumsq8(const bf16x8& x, float& ss) {
 // Per-wave state of one tile.
 struct TileAcc {
   floatx16 acc[4][4];
-  float ss[2];  // sum(x^2) halves of rows 32 (2 wn + i) + lane % 32 of the wave pair
+  float ss[4];  // sum(x^2) halves of rows 32 i + lane % 32 of the wave pair
 };
 
 // Fragments of one 16-wide K slice: x rows (A operand) and W' rows (B operand).
@@ -178,15 +176,11 @@ __device__ __forceinline__ void mfma_row(TileAcc& ta, const Frags& f, int i) {
     ta.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], ta.acc[i][j], 0, 0, 0);
 }
 
-// Row sums of squares of the wave's two row blocks (2 wn, 2 wn + 1) of one slice.
-__device__ __forceinline__ void slice_stats(TileAcc& ta, const Frags& f, int wn) {
-  if (wn == 0) {
-    sumsq8(f.a[0], ta.ss[0]);
-    sumsq8(f.a[1], ta.ss[1]);
-  } else {
-    sumsq8(f.a[2], ta.ss[0]);
-    sumsq8(f.a[3], ta.ss[1]);
-  }
+// Row sums of squares of the wave's four row blocks of one slice (both waves of a pair
+// gather the same sums; selecting half of the blocks per wave costs more than it saves).
+__device__ __forceinline__ void slice_stats(TileAcc& ta, const Frags& f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sumsq8(f.a[i], ta.ss[i]);
 }
 
 // Per-lane DMA sources.  Instruction c (0..7) of wave w fills rows R = 64 w + 8 c + lane / 8
@@ -197,15 +191,18 @@ struct DmaSrc {
   const uint16_t* w[2];  // W' row 64 w + lane / 8 of column tile 0, for even / odd c
 };
 
-// One tile's K-loop: acc = x W'_tile^T over all of d, and the rows' sums of squares.
+// One tile's K-loop: acc = x W'_tile^T over all of d; with STATS also the rows' sums of
+// squares.
 //
 //   prologue: DMA stages 0 and 1; wait for stage 0; read slice (0, 0)
 //   step ks:  read (ks, 1) | MFMA (ks, 0) | read (ks, 2) | MFMA (ks, 1) | read (ks, 3) |
-//             MFMA (ks, 2) | wait for stage ks + 1, barrier | MFMA (ks, 3) interleaved
-//             with the DMA of stage ks + 2 into buffer ks % 2 and the read of (ks + 1, 0)
+//             MFMA (ks, 2) | wait for stage ks + 1, barrier | MFMA (ks, 3) with the 16 DMA
+//             instructions of stage ks + 2 (into buffer ks % 2) spread between its rows
+//             and the read of (ks + 1, 0)
 // After the barrier of step ks every wave holds the rest of stage ks in registers, so that
-// buffer is free.  sched_fence() pins the interleaving.
-template <int RB>
+// buffer is free.  Spreading the DMA keeps the wave from stalling on a full address queue
+// while the matrix core waits.  sched_fence() pins the interleaving.
+template <int RB, bool STATS>
 __device__ __forceinline__ void kloop(const TiledArgs& p, unsigned char* smem, TileAcc& ta, const DmaSrc& src,
                                       int64_t col0, int wave, int lane) {
   using L = Lay<RB>;
@@ -229,6 +226,17 @@ __device__ __forceinline__ void kloop(const TiledArgs& p, unsigned char* smem, T
     for (int c = c0; c < c0 + 4; ++c)
       dma16(((c & 1) ? w1 : w0) + static_cast<int64_t>(8 * c) * d + ks * BK, ws + c * 1024);
   };
+  // instructions c0, c0 + 1 of the x / W' loads of step ks
+  auto issue_x2 = [&](int ks, int c0) {
+    const uint32_t xs = sbase + L::X + (ks & 1) * kTileBytes + wave * 8192;
+    dma16(src.x[c0] + ks * BK, xs + c0 * 1024);
+    dma16(src.x[c0 + 1] + ks * BK, xs + (c0 + 1) * 1024);
+  };
+  auto issue_w2 = [&](int ks, int c0) {
+    const uint32_t ws = sbase + L::W + (ks & 1) * kTileBytes + wave * 8192;
+    dma16(w0 + static_cast<int64_t>(8 * c0) * d + ks * BK, ws + c0 * 1024);
+    dma16(w1 + static_cast<int64_t>(8 * (c0 + 1)) * d + ks * BK, ws + (c0 + 1) * 1024);
+  };
   auto sx = [&](int ks) { return smem + L::X + (ks & 1) * kTileBytes; };
   auto sw = [&](int ks) { return smem + L::W + (ks & 1) * kTileBytes; };
 
@@ -245,9 +253,8 @@ __device__ __forceinline__ void kloop(const TiledArgs& p, unsigned char* smem, T
   } else {
     wait_barrier<0>();
   }
-  Frags fa, fb;
-  read_frags(fa, sx(0), sw(0), 0, wm, wn, l32, h32);
-  for (int ks = 0; ks < nk; ++ks) {
+  // slices 0..2 of step ks: MFMAs on (fa, fb, fa) with the next slice read ahead
+  auto first3 = [&](int ks, Frags& fa, Frags& fb) {
     const unsigned char* xs = sx(ks);
     const unsigned char* ws = sw(ks);
     sched_fence();
@@ -255,48 +262,66 @@ __device__ __forceinline__ void kloop(const TiledArgs& p, unsigned char* smem, T
     sched_fence();
 #pragma unroll
     for (int i = 0; i < 4; ++i) mfma_row(ta, fa, i);
-    slice_stats(ta, fa, wn);
+    if (STATS) slice_stats(ta, fa);
     sched_fence();
     read_frags(fa, xs, ws, 2, wm, wn, l32, h32);
     sched_fence();
 #pragma unroll
     for (int i = 0; i < 4; ++i) mfma_row(ta, fb, i);
-    slice_stats(ta, fb, wn);
+    if (STATS) slice_stats(ta, fb);
     sched_fence();
     read_frags(fb, xs, ws, 3, wm, wn, l32, h32);
     sched_fence();
 #pragma unroll
     for (int i = 0; i < 4; ++i) mfma_row(ta, fa, i);
-    slice_stats(ta, fa, wn);
+    if (STATS) slice_stats(ta, fa);
     sched_fence();
-    if (ks + 1 < nk) {
-      wait_barrier<0>();  // stage ks + 1 landed (nothing later is in flight)
-      sched_fence();
-      mfma_row(ta, fb, 0);
-      sched_fence();
-      if (ks + 2 < nk) {
-        issue_x(ks + 2, 0);
-        issue_x(ks + 2, 4);
-      }
-      sched_fence();
-      mfma_row(ta, fb, 1);
-      sched_fence();
-      if (ks + 2 < nk) {
-        issue_w(ks + 2, 0);
-        issue_w(ks + 2, 4);
-      }
-      sched_fence();
-      read_frags(fa, sx(ks + 1), sw(ks + 1), 0, wm, wn, l32, h32);
-      sched_fence();
+  };
+
+  Frags fa, fb;
+  read_frags(fa, sx(0), sw(0), 0, wm, wn, l32, h32);
+  // all steps but the last (the last has no barrier, DMA or read-ahead; peeling it keeps
+  // every accumulator update out of conditional code)
+  for (int ks = 0; ks + 1 < nk; ++ks) {
+    first3(ks, fa, fb);
+    wait_barrier<0>();  // stage ks + 1 landed (nothing later is in flight)
+    const bool more = ks + 2 < nk;
+    sched_fence();
+    mfma_row(ta, fb, 0);
+    sched_fence();
+    if (more) {
+      issue_x2(ks + 2, 0);
+      issue_w2(ks + 2, 0);
     }
+    sched_fence();
+    mfma_row(ta, fb, 1);
+    sched_fence();
+    if (more) {
+      issue_x2(ks + 2, 2);
+      issue_w2(ks + 2, 2);
+    }
+    sched_fence();
     mfma_row(ta, fb, 2);
-    mfma_row(ta, fb, 3);
-    if (ks + 1 >= nk) {
-      mfma_row(ta, fb, 0);
-      mfma_row(ta, fb, 1);
+    sched_fence();
+    if (more) {
+      issue_x2(ks + 2, 4);
+      issue_w2(ks + 2, 4);
     }
-    slice_stats(ta, fb, wn);
+    sched_fence();
+    read_frags(fa, sx(ks + 1), sw(ks + 1), 0, wm, wn, l32, h32);
+    sched_fence();
+    mfma_row(ta, fb, 3);
+    sched_fence();
+    if (more) {
+      issue_x2(ks + 2, 6);
+      issue_w2(ks + 2, 6);
+    }
+    if (STATS) slice_stats(ta, fb);
   }
+  first3(nk - 1, fa, fb);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mfma_row(ta, fb, i);
+  if (STATS) slice_stats(ta, fb);
   sched_fence();
   barrier_all();  // every wave is done with the stage ring
 }
@@ -373,14 +398,16 @@ __device__ __forceinline__ void upass(const TiledArgs& p, unsigned char* smem, c
   barrier_all();
 }
 
-// Row addressing of one wave's part of the output tile in the epilogue: lane rows start
-// at `inv` / `pos` (LDS) and `out` (global), consecutive rows `stride` elements apart.
+// Row data of one wave's part of the output tile in the epilogue.  inv / pos of the wave
+// pair's row q * 64 + l are held by lane l in inv[q] / pos[q]; out points at the lane's
+// first row, consecutive rows `stride` elements apart.
 struct EpiRows {
-  const float* inv;
-  const int* pos;
+  float inv[2];
+  int pos[2];
   uint16_t* out;
   int64_t stride;
   int64_t rows_left;  // rows of this lane's block still below T
+  int h32;
 };
 
 // y = acc * inv + bias, rotate-half on the pairs (j, j + 2) when ROT (turns per position
@@ -394,13 +421,14 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[4][4], const Ep
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int ro = i * 32 + (v >> 2) * 8 + (v & 3);
-      const float inv = er.inv[ro];
+      const int src_lane = (i & 1) * 32 + (v >> 2) * 8 + er.h32 * 4 + (v & 3);
+      const float inv = __shfl(er.inv[i >> 1], src_lane);
       float y0 = fmaf(acc[i][0][v], inv, bias[0]);
       float y1 = fmaf(acc[i][1][v], inv, bias[1]);
       float y2 = fmaf(acc[i][2][v], inv, bias[2]);
       float y3 = fmaf(acc[i][3][v], inv, bias[3]);
       if (ROT) {
-        const double pos = static_cast<double>(er.pos[ro]);
+        const double pos = static_cast<double>(__shfl(er.pos[i >> 1], src_lane));
         const double t0 = pos * om0, t1 = pos * om1;
         const float f0 = static_cast<float>(t0 - rint(t0));
         const float f1 = static_cast<float>(t1 - rint(t1));
@@ -425,8 +453,7 @@ template <int RB>
 __global__ __launch_bounds__(kThreads, 1) void fwd_tiled_kernel(TiledArgs p) {
   using L = Lay<RB>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[L::kBytes];
-  float* s_inv = reinterpret_cast<float*>(smem + L::INV);
-  int* s_pos = reinterpret_cast<int*>(smem + L::POS);
+  float* s_tmp = reinterpret_cast<float*>(smem + L::TMP);
   uint16_t* s_u = reinterpret_cast<uint16_t*>(smem + L::U);
 
   const int tid = threadIdx.x;
@@ -459,6 +486,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiled_kernel(TiledArgs p) {
   src.w[1] = p.wg + static_cast<int64_t>(64 * wave + rsub) * d + (pc ^ rsub ^ 1) * 8;
 
   int u_target = -1;
+  float inv_reg[2] = {0.f, 0.f};  // rows 64 q + lane of the wave pair
+  int pos_reg[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) pos_reg[q] = p.pos[min(row0 + wm * 128 + q * 64 + lane, T - 1)];
 
   for (int nt = nt0; nt < nt1; ++nt) {
     const int head0 = 2 * nt;
@@ -483,21 +514,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiled_kernel(TiledArgs p) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) ta.acc[i][j] = floatx16{};
-    ta.ss[0] = ta.ss[1] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ta.ss[i] = 0.f;
 
-    kloop<RB>(p, smem, ta, src, col0, wave, lane);
-
-    // ---- rows' inv and positions into the (now idle) x half of the stage ring
-    {
+    if (nt == nt0) {
+      kloop<RB, true>(p, smem, ta, src, col0, wave, lane);
+      // rows' inv, once per run: the wave pair's row sums meet in the idle x half
       const float inv_d = 1.0f / static_cast<float>(p.d);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < 4; ++i) {
         const float s = ta.ss[i] + __shfl_xor(ta.ss[i], 32);
-        if (h32 == 0) s_inv[wm * 128 + (2 * wn + i) * 32 + l32] = 1.0f / sqrtf(s * inv_d + p.eps);
+        if (h32 == 0 && wn == 0) s_tmp[wm * 128 + i * 32 + l32] = 1.0f / sqrtf(s * inv_d + p.eps);
       }
-      s_pos[tid] = row0 + tid < T ? p.pos[row0 + tid] : 0;
+      barrier_all();
+#pragma unroll
+      for (int q = 0; q < 2; ++q) inv_reg[q] = s_tmp[wm * 128 + q * 64 + lane];
+      barrier_all();
+    } else {
+      kloop<RB, false>(p, smem, ta, src, col0, wave, lane);
     }
-    barrier_all();
 
     // ---- LoRA up projection: acc += bf16(s U) B_t^T over K = r rounded up to 16
     if (RB > 0 && lora) {
@@ -542,8 +577,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiled_kernel(TiledArgs p) {
     int lrow = wm * 128 + h32 * 4;
     int64_t n_stride = p.N;
     asm volatile("" : "+v"(lrow), "+s"(n_stride));
-    const EpiRows er{s_inv + lrow, s_pos + lrow, p.out + (row0 + lrow) * n_stride + colw + l32, n_stride,
-                     T - (row0 + lrow)};
+    const EpiRows er{{inv_reg[0], inv_reg[1]}, {pos_reg[0], pos_reg[1]},
+                     p.out + (row0 + lrow) * n_stride + colw + l32, n_stride, T - (row0 + lrow), h32};
     const bool full = row0 + BM <= T;
     if (t < 2) {
       double om0 = exp2(-(2.0 * l32 / 128.0) * p.log2_theta) * 0.15915494309189533577;
@@ -558,7 +593,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiled_kernel(TiledArgs p) {
       else
         store_tile<false, false>(ta.acc, er, bias, 0.0, 0.0);
     }
-    barrier_all();  // the next tile's loads overwrite inv and positions
   }
 }
 
