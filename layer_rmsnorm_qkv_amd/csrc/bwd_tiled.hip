@@ -1,0 +1,665 @@
+// MFMA family of the backward (bf16, fp32 accumulation): gradients of
+//
+//   out = RoPE( W h + b + s B (A h) ),   h = x * inv * gamma,   inv = 1/rms(x)
+//
+// with W, gamma and b frozen, given dy = dL/d(out):
+//
+//   G   = RoPE^-1(dy) on the q and k heads, dy on v         (transpose of the rotation)
+//   V_t = s G_t B_t                                         [T, r] per target
+//   dh  = G W + sum_t V_t A_t                               [T, d]
+//   dx  = inv * gamma * dh - m * x,  m = inv^2 <dy, y - R b> / d
+//   dA_t = sum_tokens V_t^T h,   dB_t = s sum_tokens G_t^T U_t,   U_t = A_t h
+//
+// The row scalar uses <gamma x, dh> = <dy, y - R b> / inv (R is orthogonal and y - R b is
+// the rotated W_eff h), so the RMSNorm backward needs no second pass over dh.
+//
+// Kernels, in launch order (all on the caller's stream):
+//   prep_weights  WT = [W^T | A_q^T | A_k^T | A_v^T | 0] [d][K] with K = N + (sum r rounded
+//                 up to 64), B_t^T [r][N_t] and A'_t = bf16(A_t * gamma) [r][d]
+//   rows          per token: inv, m, G (bf16) into Gcat[:, 0:N)
+//   rank (V)      V'_t = bf16(s G_t B_t) into Gcat[:, N + off_t ...) (+ zero padding)
+//   rank (U)      U_t = bf16(inv * x A'_t^T) into U[T][R]
+//   main          dh = Gcat WT^T over K (shared tile pipeline), epilogue dx
+//   lora_partial  per chunk of 512 tokens: sum V'^T h (all targets) and G_t^T U_t
+//   lora_reduce   dA_t, dB_t = sums over chunks (deterministic order), dB scaled by s
+// h and U are recomputed from x; G and V' live only in the workspace of this call.
+#include <algorithm>
+
+#include "lrq_internal.h"
+#include "tile_common.h"
+
+namespace lrq {
+namespace {
+
+using namespace tile;
+
+constexpr int kChunk = 512;  // tokens per LoRA-gradient partial sum
+
+// Workspace of one backward call (byte offsets, 256-aligned) and derived sizes.
+struct BwdLayout {
+  int R;        // sum of the targets' ranks
+  int Rp;       // R rounded up to 64 (0 without targets)
+  int64_t K;    // N + Rp: inner size of the main product
+  int off[3];   // first LoRA column (within the R block) of each target
+  int chunks;   // token chunks of the LoRA-gradient partial sums
+  size_t wt, bt[3], ap[3], gcat, u, inv, m, pda, pdb[3], total;
+};
+
+size_t al256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+BwdLayout bwd_layout(const FwdParams& p) {
+  BwdLayout L{};
+  int R = 0;
+  for (int t = 0; t < 3; ++t) {
+    L.off[t] = R;
+    if (p.targets & (1u << t)) R += p.r;
+  }
+  L.R = R;
+  L.Rp = (R + 63) / 64 * 64;
+  L.K = p.N + L.Rp;
+  L.chunks = static_cast<int>((p.T + kChunk - 1) / kChunk);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += al256(bytes);
+    return at;
+  };
+  L.wt = take(static_cast<size_t>(p.d) * L.K * 2);
+  for (int t = 0; t < 3; ++t) {
+    int lo, hi;
+    target_cols(p, t, lo, hi);
+    const bool on = p.targets & (1u << t);
+    L.bt[t] = take(on ? static_cast<size_t>(p.r) * (hi - lo) * 2 : 0);
+    L.ap[t] = take(on ? static_cast<size_t>(p.r) * p.d * 2 : 0);
+  }
+  L.gcat = take(static_cast<size_t>(p.T) * L.K * 2);
+  L.u = take(static_cast<size_t>(p.T) * std::max(R, 1) * 2);
+  L.inv = take(static_cast<size_t>(p.T) * 4);
+  L.m = take(static_cast<size_t>(p.T) * 4);
+  L.pda = take(static_cast<size_t>(L.chunks) * R * p.d * 4);
+  for (int t = 0; t < 3; ++t) {
+    int lo, hi;
+    target_cols(p, t, lo, hi);
+    L.pdb[t] = take((p.targets & (1u << t)) ? static_cast<size_t>(L.chunks) * p.r * (hi - lo) * 4 : 0);
+  }
+  L.total = o;
+  return L;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<unsigned char*>(base) + off);
+}
+
+// ---------------------------------------------------------------- prep_weights
+// WT[j][n] = W[n][j] (n < N), WT[j][N + off_t + k] = A_t[k][j] (k < r), WT[j][N + R ..) = 0;
+// BT_t[k][n] = B_t[n][k]; AP_t[k][j] = bf16(A_t[k][j] * gamma[j]).
+// 64 x 64 tiles of the [N + Rp, d] source through LDS; the small B^T / A' products are
+// done by the blocks past the WT grid.
+struct PrepArgs {
+  const uint16_t* w;
+  const uint16_t* a[3];
+  const uint16_t* b[3];
+  const uint16_t* gamma;
+  uint16_t* wt;
+  uint16_t* bt[3];
+  uint16_t* ap[3];
+  int N, d, r, K, R;
+  int off[3], lo[3], nt[3];  // per target: LoRA column offset, first output column, width
+  uint32_t targets;
+  int wt_blocks;  // blocks of the transpose part
+};
+
+__global__ __launch_bounds__(256) void prep_weights_kernel(PrepArgs a) {
+  __shared__ uint16_t tile_s[64][65];
+  const int tid = threadIdx.x;
+  if (static_cast<int>(blockIdx.x) < a.wt_blocks) {
+    // transpose a 64 x 64 block: source rows q (LoRA-extended K index) x columns j
+    const int jb = a.d / 64;
+    const int kb = static_cast<int>(blockIdx.x) / jb, cb = static_cast<int>(blockIdx.x) % jb;
+    const int q0 = kb * 64, j0 = cb * 64;
+    for (int e = tid; e < 64 * 64; e += 256) {
+      const int qi = e / 64, ji = e % 64;
+      const int q = q0 + qi, j = j0 + ji;
+      uint16_t v = 0;
+      if (q < a.N) {
+        v = a.w[static_cast<int64_t>(q) * a.d + j];
+      } else if (q - a.N < a.R) {
+        const int c = q - a.N;
+        for (int t = 0; t < 3; ++t)
+          if (((a.targets >> t) & 1u) && c >= a.off[t] && c < a.off[t] + a.r)
+            v = a.a[t][static_cast<int64_t>(c - a.off[t]) * a.d + j];
+      }
+      tile_s[qi][ji] = v;
+    }
+    __syncthreads();
+    for (int e = tid; e < 64 * 64; e += 256) {
+      const int ji = e / 64, qi = e % 64;
+      a.wt[static_cast<int64_t>(j0 + ji) * a.K + q0 + qi] = tile_s[qi][ji];
+    }
+    return;
+  }
+  // B_t^T and A'_t: one thread per output element, grid-stride over all targets
+  const int64_t gid = (static_cast<int64_t>(blockIdx.x) - a.wt_blocks) * 256 + tid;
+  const int64_t stride = static_cast<int64_t>(gridDim.x - a.wt_blocks) * 256;
+  for (int t = 0; t < 3; ++t) {
+    if (!((a.targets >> t) & 1u)) continue;
+    const int64_t nbt = static_cast<int64_t>(a.r) * a.nt[t];
+    for (int64_t e = gid; e < nbt; e += stride) {
+      const int64_t k = e / a.nt[t], n = e % a.nt[t];
+      a.bt[t][e] = a.b[t][n * a.r + k];
+    }
+    const int64_t nap = static_cast<int64_t>(a.r) * a.d;
+    for (int64_t e = gid; e < nap; e += stride) {
+      const int j = static_cast<int>(e % a.d);
+      a.ap[t][e] = f32_to_bf16_bits(bf16_bits_to_f32(a.a[t][e]) * bf16_bits_to_f32(a.gamma[j]));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- rows
+// One wavefront per token row: inv from sum(x^2); G = inverse rotation of dy (q, k heads) or
+// dy (v), rounded once to bf16 into Gcat; m = inv^2 (<dy, y> - <G, b>) / d.  Lane l handles
+// the rotation pairs (i, i + D/2) with i = l, l + 64, ...
+struct RowsArgs {
+  const uint16_t* x;
+  const uint16_t* y;
+  const uint16_t* dy;
+  const uint16_t* bias;  // nullptr without bias
+  const int32_t* pos;
+  uint16_t* gcat;
+  float* inv;
+  float* m;
+  int64_t T;
+  int d, N, D, rot_end;
+  int64_t K;
+  float eps;
+  double log2_theta;
+};
+
+__global__ __launch_bounds__(256) void rows_kernel(RowsArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const uint16_t* xr = a.x + t * a.d;
+  float ss = 0.f;
+  for (int j = lane * 8; j < a.d; j += 512) {
+    const uint4 v = *reinterpret_cast<const uint4*>(xr + j);
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = __uint_as_float(w4[e] << 16), hi = __uint_as_float(w4[e] & 0xffff0000u);
+      ss = fmaf(lo, lo, fmaf(hi, hi, ss));
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  const float inv = 1.0f / sqrtf(ss / static_cast<float>(a.d) + a.eps);
+
+  const int half = a.D / 2;
+  // turns per position of the lane's frequencies i = lane + 64 q (D <= 512)
+  double om[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) om[q] = exp2(-(2.0 * (lane + 64 * q) / a.D) * a.log2_theta) * 0.15915494309189533577;
+  const double pos = static_cast<double>(a.pos[t]);
+  const uint16_t* dyr = a.dy + t * a.N;
+  const uint16_t* yr = a.y + t * a.N;
+  uint16_t* gr = a.gcat + t * a.K;
+  float dot_y = 0.f, dot_b = 0.f;
+  for (int c0 = 0; c0 < a.N; c0 += a.D) {
+    const bool rot = c0 < a.rot_end;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = lane + 64 * q;
+      if (i >= half) break;
+      const int ca = c0 + i, cb = c0 + i + half;
+      const float da = bf16_bits_to_f32(dyr[ca]), db = bf16_bits_to_f32(dyr[cb]);
+      dot_y = fmaf(da, bf16_bits_to_f32(yr[ca]), fmaf(db, bf16_bits_to_f32(yr[cb]), dot_y));
+      float ga = da, gb = db;
+      if (rot) {
+        // angle pos * omega_i as a fraction of a turn, reduced in double precision
+        const double turns = pos * om[q];
+        const float f = static_cast<float>(turns - rint(turns));
+        const float s = __builtin_amdgcn_sinf(f), c = __builtin_amdgcn_cosf(f);
+        ga = da * c + db * s;
+        gb = db * c - da * s;
+      }
+      if (a.bias) dot_b = fmaf(ga, bf16_bits_to_f32(a.bias[ca]), fmaf(gb, bf16_bits_to_f32(a.bias[cb]), dot_b));
+      gr[ca] = f32_to_bf16_bits(ga);
+      gr[cb] = f32_to_bf16_bits(gb);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    dot_y += __shfl_xor(dot_y, o);
+    dot_b += __shfl_xor(dot_b, o);
+  }
+  if (lane == 0) {
+    a.inv[t] = inv;
+    a.m[t] = inv * inv * (dot_y - dot_b) / static_cast<float>(a.d);
+  }
+}
+
+// ---------------------------------------------------------------- rank (V and U)
+// One workgroup per 256-token tile and target: u = A_panel Bs^T with the tile pipeline's
+// rank pass, then out[row][col0 + k] = bf16(scale(row) * u) for k < r and 0 for k in
+// [r, pad_to) (the zero padding of Gcat's LoRA columns is written by the last target).
+struct RankJob {
+  const uint16_t* a;  // A panel source: element (row, kk) at a[row * lda + kk]
+  const uint16_t* bs; // small operand rows [r][nk * 64]
+  int64_t ldb;        // row stride of bs
+  int nk;             // K steps of 64
+  int col0;           // first output column
+  int pad_to;         // output columns [col0 + r, pad_to) are written as 0
+};
+
+struct RankArgs {
+  RankJob job[3];
+  int njobs;
+  int64_t lda;
+  int64_t T;
+  int r;
+  uint16_t* out;
+  int64_t ldo;
+  float scale;         // constant factor
+  const float* inv;    // nullptr, or per-row factor
+};
+
+template <int RB>
+__global__ __launch_bounds__(kThreads, 1) void rank_kernel(RankArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kRingBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, h32 = lane >> 5;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * BM;
+  for (int jb = 0; jb < a.njobs; ++jb) {
+    const RankJob& j = a.job[jb];
+    const Src src = make_src(j.a, a.lda, row0, a.T, j.bs, j.ldb, wave, lane);
+    floatx16 u[RB == 2 ? 4 : 2];
+    rankpass<RB>(smem, src, make_rank_src(j.bs, j.ldb, a.r, RB, wave, lane), j.nk, wave, lane, u);
+    const int k = rank_col<RB>(wn, l32);
+#pragma unroll
+    for (int i = 0; i < (RB == 2 ? 4 : 2); ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = row0 + rank_row<RB>(i, v, wm, wn, h32);
+        if (row >= a.T) continue;
+        uint16_t* o = a.out + row * a.ldo + j.col0;
+        if (k < a.r) {
+          const float f = a.inv ? a.inv[row] * a.scale : a.scale;
+          o[k] = f32_to_bf16_bits(f * u[i][v]);
+        } else if (j.col0 + k < j.pad_to) {
+          o[k] = 0;
+        }
+      }
+    }
+    // columns beyond the rank blocks up to pad_to (only when pad_to - col0 > 32 RB)
+    for (int64_t e = tid; e < static_cast<int64_t>(BM) * (j.pad_to - j.col0 - 32 * RB); e += kThreads) {
+      const int w = j.pad_to - j.col0 - 32 * RB;
+      const int64_t row = row0 + e / w;
+      if (row < a.T) a.out[row * a.ldo + j.col0 + 32 * RB + e % w] = 0;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- main: dh and dx
+struct MainArgs {
+  const uint16_t* gcat;  // [T][K]
+  const uint16_t* wt;    // [d][K]
+  const uint16_t* x;
+  const uint16_t* gamma;
+  const float* inv;
+  const float* m;
+  uint16_t* dx;
+  int64_t T;
+  int d;
+  int64_t K;
+  int n_nt;   // column tiles of d
+  int items;  // grid size
+  int remap;
+};
+
+__global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(MainArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kRingBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, h32 = lane >> 5;
+  int item = blockIdx.x;
+  if (a.remap) item = (blockIdx.x & 7) * (a.items >> 3) + (blockIdx.x >> 3);
+  const int mt = item / a.n_nt;
+  const int nt = item - mt * a.n_nt;
+  const int64_t row0 = static_cast<int64_t>(mt) * BM;
+  const int64_t col0 = static_cast<int64_t>(nt) * BN;
+
+  Acc ta;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ta.acc[i][j] = floatx16{};
+  const Src src = make_src(a.gcat, a.K, row0, a.T, a.wt, a.K, wave, lane);
+  kloop<false>(smem, ta, src, col0, static_cast<int>(a.K / BK), wave, lane);
+
+  // epilogue: dx = inv * gamma * dh - m * x for the lane's rows and columns
+  // (lane rows: 128 wm + 32 i + 8 (v / 4) + 4 h32 + v % 4; columns 128 wn + 32 j + l32)
+  float gam[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) gam[j] = bf16_bits_to_f32(a.gamma[col0 + wn * 128 + j * 32 + l32]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t row = row0 + wm * 128 + i * 32 + (v >> 2) * 8 + h32 * 4 + (v & 3);
+      if (row >= a.T) continue;
+      const float inv = a.inv[row], mm = a.m[row];
+      const uint16_t* xr = a.x + row * a.d + col0 + wn * 128 + l32;
+      uint16_t* o = a.dx + row * a.d + col0 + wn * 128 + l32;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float xv = bf16_bits_to_f32(xr[j * 32]);
+        o[j * 32] = f32_to_bf16_bits(inv * gam[j] * ta.acc[i][j][v] - mm * xv);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- LoRA gradients
+// Partial sums over one chunk of tokens: out[k][col] = sum_t P[t][k] * M[t][col] for the
+// job's columns, one thread per column, ranks in groups of 32.  P rows are staged in LDS.
+//   dA job:  M = h = bf16(x * inv * gamma) (columns of d), P = V' (all targets' ranks)
+//   dB job:  M = G_t (columns of target t), P = U_t
+struct PartialJob {
+  const uint16_t* mat;  // M source: element (t, c) at mat[t * ldm + c]
+  int64_t ldm;
+  int cols;
+  const uint16_t* pv;   // P source: element (t, k) at pv[t * ldp + k]
+  int64_t ldp;
+  int ranks;
+  float* out;           // [chunks][ranks][cols]
+  int is_h;             // M is h, recomputed from x
+};
+
+struct PartialArgs {
+  PartialJob job[4];
+  int njobs;
+  int col_blocks[4];  // column blocks of 256 per job (prefix layout over blockIdx.y)
+  const uint16_t* gamma;
+  const float* inv;
+  int64_t T;
+};
+
+__global__ __launch_bounds__(256) void lora_partial_kernel(PartialArgs a) {
+  __shared__ float p_s[kChunk][33];
+  int by = blockIdx.y, jb = 0;
+  while (jb < a.njobs - 1 && by >= a.col_blocks[jb]) by -= a.col_blocks[jb++];
+  const PartialJob& j = a.job[jb];
+  const int chunk = blockIdx.x;
+  const int64_t t0 = static_cast<int64_t>(chunk) * kChunk;
+  const int nt = static_cast<int>(std::min<int64_t>(kChunk, a.T - t0));
+  const int col = by * 256 + threadIdx.x;
+  const bool active = col < j.cols;
+  const float g = (j.is_h && active) ? bf16_bits_to_f32(a.gamma[col]) : 0.f;
+  for (int k0 = 0; k0 < j.ranks; k0 += 32) {
+    const int kn = std::min(32, j.ranks - k0);
+    __syncthreads();
+    for (int e = threadIdx.x; e < nt * 32; e += 256) {
+      const int tt = e / 32, k = e % 32;
+      p_s[tt][k] = k < kn ? bf16_bits_to_f32(j.pv[(t0 + tt) * j.ldp + k0 + k]) : 0.f;
+    }
+    __syncthreads();
+    float acc[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) acc[k] = 0.f;
+    if (active) {
+      for (int tt = 0; tt < nt; ++tt) {
+        float mv = bf16_bits_to_f32(j.mat[(t0 + tt) * j.ldm + col]);
+        if (j.is_h) mv = round_bf16(mv * a.inv[t0 + tt] * g);
+#pragma unroll
+        for (int k = 0; k < 32; ++k) acc[k] = fmaf(p_s[tt][k], mv, acc[k]);
+      }
+      float* o = j.out + (static_cast<int64_t>(chunk) * j.ranks + k0) * j.cols + col;
+      for (int k = 0; k < kn; ++k) o[static_cast<int64_t>(k) * j.cols] = acc[k];
+    }
+  }
+}
+
+// dA_t[k][j] = sum_chunks PdA[c][off_t + k][j];  dB_t[n][k] = s sum_chunks PdB_t[c][k][n].
+struct ReduceArgs {
+  const float* pda;
+  const float* pdb[3];
+  float* da[3];
+  float* db[3];
+  int off[3], nt[3];
+  int R, r, d, chunks;
+  float scale;
+  uint32_t targets;
+};
+
+__global__ __launch_bounds__(256) void lora_reduce_kernel(ReduceArgs a) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  for (int t = 0; t < 3; ++t) {
+    if (!((a.targets >> t) & 1u)) continue;
+    const int64_t na = static_cast<int64_t>(a.r) * a.d;
+    for (int64_t e = gid; e < na; e += stride) {
+      const int64_t k = e / a.d, j = e % a.d;
+      float s = 0.f;
+      for (int c = 0; c < a.chunks; ++c) s += a.pda[(static_cast<int64_t>(c) * a.R + a.off[t] + k) * a.d + j];
+      a.da[t][e] = s;
+    }
+    const int64_t nb = static_cast<int64_t>(a.nt[t]) * a.r;
+    for (int64_t e = gid; e < nb; e += stride) {
+      const int64_t n = e / a.r, k = e % a.r;
+      float s = 0.f;
+      for (int c = 0; c < a.chunks; ++c) s += a.pdb[t][(static_cast<int64_t>(c) * a.r + k) * a.nt[t] + n];
+      a.db[t][e] = a.scale * s;
+    }
+  }
+}
+
+int cu_count_bwd() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  return n;
+}
+
+}  // namespace
+
+bool bwd_tiled_supports(const FwdParams& p) {
+  return p.D % 2 == 0 && p.D <= 512 && (p.Hq * p.D) % 64 == 0 && (p.Hkv * p.D) % 64 == 0 && p.d % 256 == 0 &&
+         p.d <= (1 << 20) && p.r <= kMaxRank && p.T <= (int64_t{1} << 24);
+}
+
+size_t bwd_tiled_workspace_bytes(const FwdParams& p) { return bwd_layout(p).total; }
+
+hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
+  const FwdParams& p = bp.f;
+  const BwdLayout L = bwd_layout(p);
+  void* ws = p.ws;
+  const bool lora = p.targets != 0;
+  int lo[3], nt[3];
+  for (int t = 0; t < 3; ++t) {
+    int l, h;
+    target_cols(p, t, l, h);
+    lo[t] = l;
+    nt[t] = h - l;
+  }
+
+  if (p.T > 0) {
+    // ---- weights
+    PrepArgs pa{};
+    pa.w = static_cast<const uint16_t*>(p.w);
+    pa.gamma = static_cast<const uint16_t*>(p.gamma);
+    pa.wt = at<uint16_t>(ws, L.wt);
+    for (int t = 0; t < 3; ++t) {
+      pa.a[t] = static_cast<const uint16_t*>(p.a[t]);
+      pa.b[t] = static_cast<const uint16_t*>(p.b[t]);
+      pa.bt[t] = at<uint16_t>(ws, L.bt[t]);
+      pa.ap[t] = at<uint16_t>(ws, L.ap[t]);
+      pa.off[t] = L.off[t];
+      pa.lo[t] = lo[t];
+      pa.nt[t] = nt[t];
+    }
+    pa.N = p.N;
+    pa.d = static_cast<int>(p.d);
+    pa.r = p.r;
+    pa.K = static_cast<int>(L.K);
+    pa.R = L.R;
+    pa.targets = p.targets;
+    pa.wt_blocks = static_cast<int>(L.K / 64) * static_cast<int>(p.d / 64);
+    hipLaunchKernelGGL(prep_weights_kernel, dim3(pa.wt_blocks + (lora ? 256 : 0)), dim3(256), 0, s, pa);
+
+    // ---- rows
+    RowsArgs ra{};
+    ra.x = static_cast<const uint16_t*>(p.x);
+    ra.y = static_cast<const uint16_t*>(bp.y);
+    ra.dy = static_cast<const uint16_t*>(bp.dy);
+    ra.bias = p.has_bias ? static_cast<const uint16_t*>(p.bias) : nullptr;
+    ra.pos = p.pos;
+    ra.gcat = at<uint16_t>(ws, L.gcat);
+    ra.inv = at<float>(ws, L.inv);
+    ra.m = at<float>(ws, L.m);
+    ra.T = p.T;
+    ra.d = static_cast<int>(p.d);
+    ra.N = p.N;
+    ra.D = p.D;
+    ra.rot_end = p.rot_end;
+    ra.K = L.K;
+    ra.eps = p.eps;
+    ra.log2_theta = log2(p.theta);
+    hipLaunchKernelGGL(rows_kernel, dim3(static_cast<unsigned>((p.T + 3) / 4)), dim3(256), 0, s, ra);
+
+    if (lora) {
+      // ---- V' = bf16(s G_t B_t) into Gcat's LoRA columns; U_t = bf16(inv x A'_t^T)
+      RankArgs va{};
+      RankArgs ua{};
+      va.lda = L.K;
+      va.T = ua.T = p.T;
+      va.r = ua.r = p.r;
+      va.out = at<uint16_t>(ws, L.gcat);
+      va.ldo = L.K;
+      va.scale = p.scale;
+      va.inv = nullptr;
+      ua.lda = p.d;
+      ua.out = at<uint16_t>(ws, L.u);
+      ua.ldo = L.R;
+      ua.scale = 1.0f;
+      ua.inv = at<float>(ws, L.inv);
+      int nj = 0;
+      int last_t = -1;
+      for (int t = 0; t < 3; ++t)
+        if (p.targets & (1u << t)) last_t = t;
+      for (int t = 0; t < 3; ++t) {
+        if (!(p.targets & (1u << t))) continue;
+        RankJob& vj = va.job[nj];
+        vj.a = at<uint16_t>(ws, L.gcat) + lo[t];
+        vj.bs = at<uint16_t>(ws, L.bt[t]);
+        vj.ldb = nt[t];
+        vj.nk = nt[t] / BK;
+        vj.col0 = p.N + L.off[t];
+        vj.pad_to = t == last_t ? static_cast<int>(L.K) : vj.col0 + p.r;
+        RankJob& uj = ua.job[nj];
+        uj.a = static_cast<const uint16_t*>(p.x);
+        uj.bs = at<uint16_t>(ws, L.ap[t]);
+        uj.ldb = p.d;
+        uj.nk = static_cast<int>(p.d / BK);
+        uj.col0 = L.off[t];
+        uj.pad_to = uj.col0 + p.r;
+        ++nj;
+      }
+      va.njobs = ua.njobs = nj;
+      const dim3 grid(static_cast<unsigned>((p.T + BM - 1) / BM));
+      if (p.r <= 32) {
+        hipLaunchKernelGGL(rank_kernel<1>, grid, dim3(kThreads), 0, s, va);
+        hipLaunchKernelGGL(rank_kernel<1>, grid, dim3(kThreads), 0, s, ua);
+      } else {
+        hipLaunchKernelGGL(rank_kernel<2>, grid, dim3(kThreads), 0, s, va);
+        hipLaunchKernelGGL(rank_kernel<2>, grid, dim3(kThreads), 0, s, ua);
+      }
+    }
+
+    // ---- dh and dx
+    MainArgs ma{};
+    ma.gcat = at<uint16_t>(ws, L.gcat);
+    ma.wt = at<uint16_t>(ws, L.wt);
+    ma.x = static_cast<const uint16_t*>(p.x);
+    ma.gamma = static_cast<const uint16_t*>(p.gamma);
+    ma.inv = at<float>(ws, L.inv);
+    ma.m = at<float>(ws, L.m);
+    ma.dx = static_cast<uint16_t*>(bp.dx);
+    ma.T = p.T;
+    ma.d = static_cast<int>(p.d);
+    ma.K = L.K;
+    ma.n_nt = static_cast<int>(p.d / BN);
+    const int n_mt = static_cast<int>((p.T + BM - 1) / BM);
+    ma.items = n_mt * ma.n_nt;
+    ma.remap = ma.items % 8 == 0;
+    (void)cu_count_bwd;
+    hipLaunchKernelGGL(bwd_main_kernel, dim3(ma.items), dim3(kThreads), 0, s, ma);
+
+    if (lora) {
+      // ---- LoRA gradient partial sums
+      PartialArgs pa2{};
+      int nj = 0, ycount = 0;
+      PartialJob& ja = pa2.job[nj];
+      ja.mat = static_cast<const uint16_t*>(p.x);
+      ja.ldm = p.d;
+      ja.cols = static_cast<int>(p.d);
+      ja.pv = at<uint16_t>(ws, L.gcat) + p.N;
+      ja.ldp = L.K;
+      ja.ranks = L.R;
+      ja.out = at<float>(ws, L.pda);
+      ja.is_h = 1;
+      pa2.col_blocks[nj] = (ja.cols + 255) / 256;
+      ycount += pa2.col_blocks[nj];
+      ++nj;
+      for (int t = 0; t < 3; ++t) {
+        if (!(p.targets & (1u << t))) continue;
+        PartialJob& jb = pa2.job[nj];
+        jb.mat = at<uint16_t>(ws, L.gcat) + lo[t];
+        jb.ldm = L.K;
+        jb.cols = nt[t];
+        jb.pv = at<uint16_t>(ws, L.u) + L.off[t];
+        jb.ldp = L.R;
+        jb.ranks = p.r;
+        jb.out = at<float>(ws, L.pdb[t]);
+        jb.is_h = 0;
+        pa2.col_blocks[nj] = (jb.cols + 255) / 256;
+        ycount += pa2.col_blocks[nj];
+        ++nj;
+      }
+      pa2.njobs = nj;
+      pa2.gamma = static_cast<const uint16_t*>(p.gamma);
+      pa2.inv = at<float>(ws, L.inv);
+      pa2.T = p.T;
+      hipLaunchKernelGGL(lora_partial_kernel, dim3(L.chunks, ycount), dim3(256), 0, s, pa2);
+    }
+  }
+
+  if (lora) {
+    // ---- dA, dB (zero when T == 0: no chunks)
+    ReduceArgs rd{};
+    rd.pda = at<float>(ws, L.pda);
+    for (int t = 0; t < 3; ++t) {
+      rd.pdb[t] = at<float>(ws, L.pdb[t]);
+      rd.da[t] = bp.da[t];
+      rd.db[t] = bp.db[t];
+      rd.off[t] = L.off[t];
+      rd.nt[t] = nt[t];
+    }
+    rd.R = L.R;
+    rd.r = p.r;
+    rd.d = static_cast<int>(p.d);
+    rd.chunks = L.chunks;
+    rd.scale = p.scale;
+    rd.targets = p.targets;
+    hipLaunchKernelGGL(lora_reduce_kernel, dim3(512), dim3(256), 0, s, rd);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lrq

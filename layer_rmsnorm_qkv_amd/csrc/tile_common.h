@@ -1,0 +1,377 @@
+// Shared tile pipeline of the MFMA kernels (tiled forward and tiled backward): a 256 x 256
+// output tile of bf16 x bf16 -> fp32 products with K = 64 per step.
+//
+//   * 256 threads = 4 wavefronts, one per SIMD; wavefront (wm, wn) owns rows 128 wm .. +128
+//     and columns 128 wn .. +128 of the tile: 4 x 4 accumulators of
+//     v_mfma_f32_32x32x16_bf16 (256 fp32 per lane, in the accumulation registers).
+//   * Both operands are K-major ("A[M][K] times B[N][K]^T").  A 256-row panel of A and a
+//     256-row tile of B go from global memory straight into LDS (global_load_lds_dwordx4,
+//     no registers) through a ring of two 64 KB stages; every staged row of a step is one
+//     whole 128-byte line.  Each lane picks its global source so that the 16-byte chunks
+//     land XOR-swizzled by row (conflict-free ds_read_b128).
+//   * Stage map: A half at [0, 64 KB), B half at [64 KB, 128 KB).
+#pragma once
+
+#include "lrq_internal.h"
+
+namespace lrq {
+namespace tile {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int BM = 256;
+constexpr int BN = 256;
+constexpr int BK = 64;
+constexpr int kRowBytes = BK * 2;            // one staged row: 64 bf16 = 128 bytes
+constexpr int kTileBytes = BM * kRowBytes;   // 32 KB per operand per stage
+constexpr int kSlices = BK / 16;             // 16-wide MFMA K slices per step
+constexpr int kStageA = 0;                   // 2 x [256][64] bf16
+constexpr int kStageB = 2 * kTileBytes;      // 2 x [256][64] bf16
+constexpr int kRingBytes = 4 * kTileBytes;   // 128 KB
+constexpr int kLdsMax = 160 * 1024;
+
+// XOR pattern of the 16-byte chunks of staged row `row`.  Any 16 consecutive rows read at
+// one logical chunk hit 16 distinct 16-byte bank groups of a 256-byte window
+// (ds_read_b128 serves 16 lanes per cycle from 64 banks), and any 8 consecutive rows hit 8
+// distinct groups of a 128-byte window.
+__device__ __forceinline__ int chunk_xor(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// byte offset of logical 16-byte chunk `chunk` (0..7) of row `row` in a [rows][64] bf16 tile
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ chunk_xor(row)) << 4); }
+
+__device__ __forceinline__ float lo_bf16(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// 16 bytes per lane from global memory into LDS at byte address lds + 16 * lane (lds is
+// wave-uniform).  Written as inline assembly on purpose: the compiler then neither counts
+// these loads nor makes every later LDS read wait for all of them; the stage ring waits
+// for exactly the stage it needs (wait_barrier).  Loads the compiler does not know about
+// can only make its own vmcnt waits longer, never too short.  The destination goes in M0
+// (the compiler sets it); M0 needs one wait state after it is written.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+
+// LDS byte address of a pointer into a __shared__ array (the low half of its flat address).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0), then a workgroup barrier; the empty asm statements keep
+// the compiler from moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Barrier once this wave's LDS reads have completed (its DMA may stay in flight).
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void barrier_all() { wait_barrier<0>(); }
+
+// Keeps the compiler's scheduler from moving instructions across this point.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// ss += sum of squares of the 8 bf16 values of a fragment (products exact, fp32 sums)
+__device__ __forceinline__ void sumsq8(const bf16x8& x, float& ss) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16x2 v = {x[2 * e], x[2 * e + 1]};
+    ss = __builtin_amdgcn_fdot2_f32_bf16(v, v, ss, false);
+  }
+}
+
+// Per-wave state of one tile.
+struct Acc {
+  floatx16 acc[4][4];
+  float ss[4];  // sums of squares (halves) of A rows 32 i + lane % 32 of the wave pair
+};
+
+// Fragments of one 16-wide K slice: rows of the A panel and of the B tile.
+struct Frags {
+  bf16x8 a[4], b[4];
+};
+
+__device__ __forceinline__ void read_frags(Frags& f, const unsigned char* xs, const unsigned char* ws, int kk, int wm,
+                                           int wn, int l32, int h32) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    f.a[i] = *reinterpret_cast<const bf16x8*>(xs + swz(wm * 128 + i * 32 + l32, kk * 2 + h32));
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    f.b[j] = *reinterpret_cast<const bf16x8*>(ws + swz(wn * 128 + j * 32 + l32, kk * 2 + h32));
+}
+
+// The four MFMAs of row block i of one slice.
+__device__ __forceinline__ void mfma_row(Acc& ta, const Frags& f, int i) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    ta.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], ta.acc[i][j], 0, 0, 0);
+}
+
+// Sums of squares of the wave's four A row blocks of one slice (both waves of a pair
+// gather the same sums; selecting half of the blocks per wave costs more than it saves).
+__device__ __forceinline__ void slice_stats(Acc& ta, const Frags& f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sumsq8(f.a[i], ta.ss[i]);
+}
+
+// Per-lane DMA sources.  Instruction c (0..7) of wave w fills rows R = 64 w + 8 c + lane / 8
+// of a stage; the lane's 16 bytes land in physical chunk lane % 8, which holds logical
+// chunk (lane % 8) ^ chunk_xor(R) = (lane % 8) ^ (lane / 8) ^ (c & 1).
+struct Src {
+  const uint16_t* a[8];  // A row per instruction; rows past the panel's end re-read its last row
+  const uint16_t* b[2];  // B row 64 w + lane / 8 of column tile 0, for even / odd c
+  int64_t ldb;           // row stride of B (elements)
+};
+
+// Sources for the A panel rows [row0, row0 + 256) of A (stride lda; rows >= rows_valid
+// re-read row rows_valid - 1, whose results are never stored) and the B rows (stride ldb).
+__device__ __forceinline__ Src make_src(const uint16_t* A, int64_t lda, int64_t row0, int64_t rows_valid,
+                                        const uint16_t* B, int64_t ldb, int wave, int lane) {
+  Src s;
+  const int pc = lane & 7;
+  const int rsub = lane >> 3;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int R = 64 * wave + 8 * c + rsub;
+    const int64_t row = min(row0 + R, rows_valid - 1);
+    s.a[c] = A + row * lda + (pc ^ chunk_xor(R)) * 8;
+  }
+  // chunk_xor(64 w + 8 c + rsub) = rsub ^ (c & 1)
+  s.b[0] = B + static_cast<int64_t>(64 * wave + rsub) * ldb + (pc ^ rsub) * 8;
+  s.b[1] = B + static_cast<int64_t>(64 * wave + rsub) * ldb + (pc ^ rsub ^ 1) * 8;
+  s.ldb = ldb;
+  return s;
+}
+
+// One tile's K-loop over nk steps: acc = A_panel B_tile^T, B_tile = B rows [col0, col0 + 256);
+// with STATS also the A rows' sums of squares.
+//
+//   prologue: DMA stages 0 and 1; wait for stage 0; read slice (0, 0)
+//   step ks:  read (ks, 1) | MFMA (ks, 0) | read (ks, 2) | MFMA (ks, 1) | read (ks, 3) |
+//             MFMA (ks, 2) | wait for stage ks + 1, barrier | MFMA (ks, 3) with the 16 DMA
+//             instructions of stage ks + 2 (into buffer ks % 2) spread between its rows
+//             and the read of (ks + 1, 0)
+// After the barrier of step ks every wave holds the rest of stage ks in registers, so that
+// buffer is free.  Spreading the DMA keeps the wave from stalling on a full address queue
+// while the matrix core waits.  sched_fence() pins the interleaving.
+template <bool STATS>
+__device__ __forceinline__ void kloop(unsigned char* smem, Acc& ta, const Src& src, int64_t col0, int nk, int wave,
+                                      int lane) {
+  constexpr int kLoads = 16;  // DMA instructions per stage and wave
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, h32 = lane >> 5;
+  const int64_t d = src.ldb;
+  const uint32_t sbase = lds_addr(smem);
+  const uint16_t* w0 = src.b[0] + col0 * d;
+  const uint16_t* w1 = src.b[1] + col0 * d;
+
+  auto issue_x = [&](int ks, int c0) {
+    const uint32_t xs = sbase + kStageA + (ks & 1) * kTileBytes + wave * 8192;
+#pragma unroll
+    for (int c = c0; c < c0 + 4; ++c) dma16(src.a[c] + ks * BK, xs + c * 1024);
+  };
+  auto issue_w = [&](int ks, int c0) {
+    const uint32_t ws = sbase + kStageB + (ks & 1) * kTileBytes + wave * 8192;
+#pragma unroll
+    for (int c = c0; c < c0 + 4; ++c)
+      dma16(((c & 1) ? w1 : w0) + static_cast<int64_t>(8 * c) * d + ks * BK, ws + c * 1024);
+  };
+  // instructions c0, c0 + 1 of the x / W' loads of step ks
+  auto issue_x2 = [&](int ks, int c0) {
+    const uint32_t xs = sbase + kStageA + (ks & 1) * kTileBytes + wave * 8192;
+    dma16(src.a[c0] + ks * BK, xs + c0 * 1024);
+    dma16(src.a[c0 + 1] + ks * BK, xs + (c0 + 1) * 1024);
+  };
+  auto issue_w2 = [&](int ks, int c0) {
+    const uint32_t ws = sbase + kStageB + (ks & 1) * kTileBytes + wave * 8192;
+    dma16(w0 + static_cast<int64_t>(8 * c0) * d + ks * BK, ws + c0 * 1024);
+    dma16(w1 + static_cast<int64_t>(8 * (c0 + 1)) * d + ks * BK, ws + (c0 + 1) * 1024);
+  };
+  auto sx = [&](int ks) { return smem + kStageA + (ks & 1) * kTileBytes; };
+  auto sw = [&](int ks) { return smem + kStageB + (ks & 1) * kTileBytes; };
+
+  issue_x(0, 0);
+  issue_x(0, 4);
+  issue_w(0, 0);
+  issue_w(0, 4);
+  if (nk > 1) {
+    issue_x(1, 0);
+    issue_x(1, 4);
+    issue_w(1, 0);
+    issue_w(1, 4);
+    wait_barrier<kLoads>();
+  } else {
+    wait_barrier<0>();
+  }
+  // slices 0..2 of step ks: MFMAs on (fa, fb, fa) with the next slice read ahead
+  auto first3 = [&](int ks, Frags& fa, Frags& fb) {
+    const unsigned char* xs = sx(ks);
+    const unsigned char* ws = sw(ks);
+    sched_fence();
+    read_frags(fb, xs, ws, 1, wm, wn, l32, h32);
+    sched_fence();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mfma_row(ta, fa, i);
+    if (STATS) slice_stats(ta, fa);
+    sched_fence();
+    read_frags(fa, xs, ws, 2, wm, wn, l32, h32);
+    sched_fence();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mfma_row(ta, fb, i);
+    if (STATS) slice_stats(ta, fb);
+    sched_fence();
+    read_frags(fb, xs, ws, 3, wm, wn, l32, h32);
+    sched_fence();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mfma_row(ta, fa, i);
+    if (STATS) slice_stats(ta, fa);
+    sched_fence();
+  };
+
+  Frags fa, fb;
+  read_frags(fa, sx(0), sw(0), 0, wm, wn, l32, h32);
+  // all steps but the last (the last has no barrier, DMA or read-ahead; peeling it keeps
+  // every accumulator update out of conditional code)
+  for (int ks = 0; ks + 1 < nk; ++ks) {
+    first3(ks, fa, fb);
+    wait_barrier<0>();  // stage ks + 1 landed (nothing later is in flight)
+    const bool more = ks + 2 < nk;
+    sched_fence();
+    mfma_row(ta, fb, 0);
+    sched_fence();
+    if (more) {
+      issue_x2(ks + 2, 0);
+      issue_w2(ks + 2, 0);
+    }
+    sched_fence();
+    mfma_row(ta, fb, 1);
+    sched_fence();
+    if (more) {
+      issue_x2(ks + 2, 2);
+      issue_w2(ks + 2, 2);
+    }
+    sched_fence();
+    mfma_row(ta, fb, 2);
+    sched_fence();
+    if (more) {
+      issue_x2(ks + 2, 4);
+      issue_w2(ks + 2, 4);
+    }
+    sched_fence();
+    read_frags(fa, sx(ks + 1), sw(ks + 1), 0, wm, wn, l32, h32);
+    sched_fence();
+    mfma_row(ta, fb, 3);
+    sched_fence();
+    if (more) {
+      issue_x2(ks + 2, 6);
+      issue_w2(ks + 2, 6);
+    }
+    if (STATS) slice_stats(ta, fb);
+  }
+  first3(nk - 1, fa, fb);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mfma_row(ta, fb, i);
+  if (STATS) slice_stats(ta, fb);
+  sched_fence();
+  barrier_all();  // every wave is done with the stage ring
+}
+
+// Rows of a small B operand (up to 32 RB rows, K-major, stride ldr) for rankpass:
+// instruction q (0 .. RB - 1) of wave w fills rows R = 8 RB w + 8 q + lane / 8 of
+// [32 RB][64]; rows >= nrows re-read row nrows - 1.
+struct RankSrc {
+  const uint16_t* r[2];
+};
+
+__device__ __forceinline__ RankSrc make_rank_src(const uint16_t* Bs, int64_t ldr, int nrows, int rb, int wave,
+                                                 int lane) {
+  RankSrc s;
+  const int pc = lane & 7;
+  const int rsub = lane >> 3;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int R = 8 * rb * wave + 8 * q + rsub;
+    s.r[q] = Bs + static_cast<int64_t>(min(R, nrows - 1)) * ldr + (pc ^ chunk_xor(R)) * 8;
+  }
+  return s;
+}
+
+// Skinny product of the 256-row A panel with up to 32 RB rows of a small K-major operand:
+// u = A_panel Bs^T over nk steps of 64 (A through the A half of the stage ring, Bs rows
+// through the B half).  RB == 1: wave (wm, wn) gets columns 0..31 of row blocks 2 wn + i
+// (i = 0, 1) of its 128 rows in u[i]; RB == 2: columns 32 wn .. +32 of row blocks i
+// (i = 0..3).  Lane layout of u[i] is that of a 32x32 MFMA accumulator.  Leaves the stage
+// ring free (barrier at the end).
+//   step ks: DMA stage ks + 1 | wait for stage ks, barrier | MFMAs | barrier (reads done)
+template <int RB>
+__device__ __forceinline__ void rankpass(unsigned char* smem, const Src& src, const RankSrc& rs, int nk, int wave,
+                                         int lane, floatx16 (&u)[RB == 2 ? 4 : 2]) {
+  constexpr int kLoads = 8 + RB;       // DMA instructions per stage and wave
+  constexpr int NB = RB == 2 ? 4 : 2;  // row blocks per wave
+  constexpr int kRStage = RB * 32 * kRowBytes;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, h32 = lane >> 5;
+  const uint32_t sbase = lds_addr(smem);
+
+  auto issue = [&](int ks) {
+    const uint32_t as = sbase + kStageA + (ks & 1) * kTileBytes + wave * 8192;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) dma16(src.a[c] + ks * BK, as + c * 1024);
+    const uint32_t rsl = sbase + kStageB + (ks & 1) * kRStage + wave * RB * 1024;
+#pragma unroll
+    for (int q = 0; q < RB; ++q) dma16(rs.r[q] + ks * BK, rsl + q * 1024);
+  };
+
+#pragma unroll
+  for (int i = 0; i < NB; ++i) u[i] = floatx16{};
+  issue(0);
+  for (int ks = 0; ks < nk; ++ks) {
+    if (ks + 1 < nk) {
+      issue(ks + 1);
+      wait_barrier<kLoads>();  // stage ks landed
+    } else {
+      wait_barrier<0>();
+    }
+    const unsigned char* as = smem + kStageA + (ks & 1) * kTileBytes;
+    const unsigned char* rsl = smem + kStageB + (ks & 1) * kRStage;
+#pragma unroll
+    for (int kk = 0; kk < kSlices; ++kk) {
+      const bf16x8 lf = *reinterpret_cast<const bf16x8*>(rsl + swz((RB == 2 ? wn * 32 : 0) + l32, kk * 2 + h32));
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int rb = RB == 2 ? i : 2 * wn + i;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(as + swz(wm * 128 + rb * 32 + l32, kk * 2 + h32));
+        u[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, lf, u[i], 0, 0, 0);
+      }
+    }
+    barrier_lds();  // every wave is done with stage ks before the DMA of step ks + 2
+  }
+}
+
+// Row (within the 256-row tile) and column of element v of u[i] of rankpass for this lane.
+template <int RB>
+__device__ __forceinline__ int rank_row(int i, int v, int wm, int wn, int h32) {
+  const int rb = RB == 2 ? i : 2 * wn + i;
+  return wm * 128 + rb * 32 + (v >> 2) * 8 + h32 * 4 + (v & 3);
+}
+template <int RB>
+__device__ __forceinline__ int rank_col(int wn, int l32) {
+  return (RB == 2 ? wn * 32 : 0) + l32;
+}
+
+}  // namespace tile
+}  // namespace lrq

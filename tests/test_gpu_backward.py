@@ -26,6 +26,12 @@ CASES = {
     "bf16_train_small": TRAIN.replace(n_tokens=300, d_model=512, n_q_heads=8, n_kv_heads=2),
     "bf16_allt_bias": wl.get("decode").replace(n_tokens=129, d_model=384, n_q_heads=3, n_kv_heads=3,
                                                lora_rank=16),
+    # shapes the MFMA family covers: ragged token counts, rank above one 32-block, bias
+    "bf16_allt_bias_t300_r64": wl.get("decode").replace(n_tokens=300, d_model=512, n_q_heads=4, n_kv_heads=4,
+                                                        lora_rank=64),
+    "bf16_gqa_t513_r24": TRAIN.replace(n_tokens=513, d_model=768, n_q_heads=4, n_kv_heads=2, lora_rank=24,
+                                       lora_targets=TQ | TK, seq_len=0, max_position=9000),
+    "bf16_noadapt_t77": TRAIN.replace(n_tokens=77, d_model=256, n_q_heads=2, n_kv_heads=2, lora_targets=0),
 }
 
 
