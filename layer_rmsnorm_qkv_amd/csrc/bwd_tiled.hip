@@ -20,7 +20,7 @@
 //   rank (V)      V'_t = bf16(s G_t B_t) into Gcat[:, N + off_t ...) (+ zero padding)
 //   rank (U)      U_t = bf16(inv * x A'_t^T) into U[T][R]
 //   main          dh = Gcat WT^T over K (shared tile pipeline), epilogue dx
-//   lora_partial  per chunk of 512 tokens: sum V'^T h (all targets) and G_t^T U_t
+//   lora_partial  per chunk of tokens: sum V'^T h (all targets) and G_t^T U_t (MFMA)
 //   lora_reduce   dA_t, dB_t = sums over chunks (deterministic order), dB scaled by s
 // h and U are recomputed from x; G and V' live only in the workspace of this call.
 #include <algorithm>
@@ -33,7 +33,7 @@ namespace {
 
 using namespace tile;
 
-constexpr int kChunk = 512;  // tokens per LoRA-gradient partial sum
+constexpr int kLoraItems = 1152;  // target number of one-wave LoRA-gradient work items
 
 // Workspace of one backward call (byte offsets, 256-aligned) and derived sizes.
 struct BwdLayout {
@@ -41,6 +41,10 @@ struct BwdLayout {
   int Rp;       // R rounded up to 64 (0 without targets)
   int64_t K;    // N + Rp: inner size of the main product
   int off[3];   // first LoRA column (within the R block) of each target
+  int cpl;      // LoRA gradients: columns per lane (8 when R <= 32, else 4)
+  int rpass;    // ranks per pass over M (32 or 64)
+  int groups[4];  // work groups per LoRA-gradient job (dA, then each target's dB)
+  int chunk;    // tokens per partial sum (multiple of 16)
   int chunks;   // token chunks of the LoRA-gradient partial sums
   size_t wt, bt[3], ap[3], gcat, u, inv, m, pda, pdb[3], total;
 };
@@ -57,7 +61,22 @@ BwdLayout bwd_layout(const FwdParams& p) {
   L.R = R;
   L.Rp = (R + 63) / 64 * 64;
   L.K = p.N + L.Rp;
-  L.chunks = static_cast<int>((p.T + kChunk - 1) / kChunk);
+  L.cpl = R <= 32 ? 8 : 4;
+  L.rpass = L.cpl == 8 ? 32 : 64;
+  const int colw = 32 * L.cpl;
+  int G = 0;
+  L.groups[0] = static_cast<int>((p.d + colw - 1) / colw) * ((R + L.rpass - 1) / L.rpass);
+  G += L.groups[0];
+  for (int t = 0; t < 3; ++t) {
+    int lo, hi;
+    target_cols(p, t, lo, hi);
+    L.groups[t + 1] = (p.targets & (1u << t)) ? (hi - lo + colw - 1) / colw * ((p.r + L.rpass - 1) / L.rpass) : 0;
+    G += L.groups[t + 1];
+  }
+  // chunks as long as the work items stay near the target count (fewer partial sums to add)
+  L.chunk = 64;
+  while (L.chunk < 2048 && (p.T + L.chunk - 1) / L.chunk * G > kLoraItems) L.chunk *= 2;
+  L.chunks = static_cast<int>((p.T + L.chunk - 1) / L.chunk);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -241,28 +260,27 @@ __global__ __launch_bounds__(256) void rows_kernel(RowsArgs a) {
 }
 
 // ---------------------------------------------------------------- rank (V and U)
-// One workgroup per 256-token tile and target: u = A_panel Bs^T with the tile pipeline's
-// rank pass, then out[row][col0 + k] = bf16(scale(row) * u) for k < r and 0 for k in
-// [r, pad_to) (the zero padding of Gcat's LoRA columns is written by the last target).
+// One workgroup per (256-token tile, job): u = A_panel Bs^T with the tile pipeline's rank
+// pass, then out[row][col0 + k] = bf16(scale(row) * u) for k < r and 0 for k in
+// [r, pad_to - col0) (the zero padding of Gcat's LoRA columns comes with the last V job).
 struct RankJob {
-  const uint16_t* a;  // A panel source: element (row, kk) at a[row * lda + kk]
-  const uint16_t* bs; // small operand rows [r][nk * 64]
-  int64_t ldb;        // row stride of bs
-  int nk;             // K steps of 64
-  int col0;           // first output column
-  int pad_to;         // output columns [col0 + r, pad_to) are written as 0
+  const uint16_t* a;   // A panel source: element (row, kk) at a[row * lda + kk]
+  int64_t lda;
+  const uint16_t* bs;  // small operand rows [r][nk * 64]
+  int64_t ldb;
+  int nk;              // K steps of 64
+  uint16_t* out;
+  int64_t ldo;
+  int col0;            // first output column
+  int pad_to;          // output columns [col0 + r, pad_to) are written as 0
+  float scale;         // constant factor
+  const float* inv;    // nullptr, or per-row factor
 };
 
 struct RankArgs {
-  RankJob job[3];
-  int njobs;
-  int64_t lda;
+  RankJob job[6];
   int64_t T;
   int r;
-  uint16_t* out;
-  int64_t ldo;
-  float scale;         // constant factor
-  const float* inv;    // nullptr, or per-row factor
 };
 
 template <int RB>
@@ -274,33 +292,31 @@ __global__ __launch_bounds__(kThreads, 1) void rank_kernel(RankArgs a) {
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, h32 = lane >> 5;
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * BM;
-  for (int jb = 0; jb < a.njobs; ++jb) {
-    const RankJob& j = a.job[jb];
-    const Src src = make_src(j.a, a.lda, row0, a.T, j.bs, j.ldb, wave, lane);
-    floatx16 u[RB == 2 ? 4 : 2];
-    rankpass<RB>(smem, src, make_rank_src(j.bs, j.ldb, a.r, RB, wave, lane), j.nk, wave, lane, u);
-    const int k = rank_col<RB>(wn, l32);
+  const RankJob& j = a.job[blockIdx.y];
+  const Src src = make_src(j.a, j.lda, row0, a.T, j.bs, j.ldb, wave, lane);
+  floatx16 u[RB == 2 ? 4 : 2];
+  rankpass<RB>(smem, src, make_rank_src(j.bs, j.ldb, a.r, RB, wave, lane), j.nk, wave, lane, u);
+  const int k = rank_col<RB>(wn, l32);
 #pragma unroll
-    for (int i = 0; i < (RB == 2 ? 4 : 2); ++i) {
+  for (int i = 0; i < (RB == 2 ? 4 : 2); ++i) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = row0 + rank_row<RB>(i, v, wm, wn, h32);
-        if (row >= a.T) continue;
-        uint16_t* o = a.out + row * a.ldo + j.col0;
-        if (k < a.r) {
-          const float f = a.inv ? a.inv[row] * a.scale : a.scale;
-          o[k] = f32_to_bf16_bits(f * u[i][v]);
-        } else if (j.col0 + k < j.pad_to) {
-          o[k] = 0;
-        }
+    for (int v = 0; v < 16; ++v) {
+      const int64_t row = row0 + rank_row<RB>(i, v, wm, wn, h32);
+      if (row >= a.T) continue;
+      uint16_t* o = j.out + row * j.ldo + j.col0;
+      if (k < a.r) {
+        const float f = j.inv ? j.inv[row] * j.scale : j.scale;
+        o[k] = f32_to_bf16_bits(f * u[i][v]);
+      } else if (j.col0 + k < j.pad_to) {
+        o[k] = 0;
       }
     }
-    // columns beyond the rank blocks up to pad_to (only when pad_to - col0 > 32 RB)
-    for (int64_t e = tid; e < static_cast<int64_t>(BM) * (j.pad_to - j.col0 - 32 * RB); e += kThreads) {
-      const int w = j.pad_to - j.col0 - 32 * RB;
-      const int64_t row = row0 + e / w;
-      if (row < a.T) a.out[row * a.ldo + j.col0 + 32 * RB + e % w] = 0;
-    }
+  }
+  // padding columns beyond the rank blocks (only when pad_to - col0 > 32 RB)
+  const int w = j.pad_to - j.col0 - 32 * RB;
+  for (int64_t e = tid; e < static_cast<int64_t>(BM) * w; e += kThreads) {
+    const int64_t row = row0 + e / w;
+    if (row < a.T) j.out[row * j.ldo + j.col0 + 32 * RB + e % w] = 0;
   }
 }
 
@@ -367,69 +383,215 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(MainArgs a) {
 }
 
 // ---------------------------------------------------------------- LoRA gradients
-// Partial sums over one chunk of tokens: out[k][col] = sum_t P[t][k] * M[t][col] for the
-// job's columns, one thread per column, ranks in groups of 32.  P rows are staged in LDS.
-//   dA job:  M = h = bf16(x * inv * gamma) (columns of d), P = V' (all targets' ranks)
-//   dB job:  M = G_t (columns of target t), P = U_t
-struct PartialJob {
-  const uint16_t* mat;  // M source: element (t, c) at mat[t * ldm + c]
+// Partial sums over one chunk of tokens, out[k][c] = sum_t P[t][k] M[t][c], as MFMA products
+// whose inner dimension is the token index:
+//   dA job:  M = x, P = bf16(V' * inv) over all targets' ranks (gamma is applied by the reduce,
+//            since h[t][c] = x[t][c] * inv[t] * gamma[c]),
+//   dB job:  M = G_t, P = U_t (s is applied by the reduce).
+// One wave per work item (job, 32*CPL columns, a pass of 32*RB ranks, one chunk of tokens).
+// In each 16-token step lane l reads CPL consecutive columns of 8 tokens (the lane half's
+// share of the step) with one vector load per token and transposes them in registers:
+// fragment j then holds, for column c0 + CPL*(l%32) + j, the 8 token values that one lane
+// feeds the MFMA.  The MFMA's rows are therefore every CPL-th column; the epilogue maps them
+// back.  Loads of the next step are issued before the current step's MFMAs.
+struct LoraJob {
+  const uint16_t* mat;  // M: element (t, c) at mat[t * ldm + c]; rows 16-byte aligned
   int64_t ldm;
-  int cols;
-  const uint16_t* pv;   // P source: element (t, k) at pv[t * ldp + k]
+  int cols;             // multiple of CPL
+  const uint16_t* pv;   // P: element (t, k) at pv[t * ldp + k]
   int64_t ldp;
   int ranks;
+  const float* inv;     // per-token factor folded into P, or nullptr
   float* out;           // [chunks][ranks][cols]
-  int is_h;             // M is h, recomputed from x
+  int col_groups;       // column groups of 32 * CPL
+  int groups;           // col_groups * rank passes
 };
 
-struct PartialArgs {
-  PartialJob job[4];
+struct LoraArgs {
+  LoraJob job[4];
   int njobs;
-  int col_blocks[4];  // column blocks of 256 per job (prefix layout over blockIdx.y)
-  const uint16_t* gamma;
-  const float* inv;
+  int chunk;   // tokens per chunk, a multiple of 16
+  int chunks;
   int64_t T;
 };
 
-__global__ __launch_bounds__(256) void lora_partial_kernel(PartialArgs a) {
-  __shared__ float p_s[kChunk][33];
-  int by = blockIdx.y, jb = 0;
-  while (jb < a.njobs - 1 && by >= a.col_blocks[jb]) by -= a.col_blocks[jb++];
-  const PartialJob& j = a.job[jb];
-  const int chunk = blockIdx.x;
-  const int64_t t0 = static_cast<int64_t>(chunk) * kChunk;
-  const int nt = static_cast<int>(std::min<int64_t>(kChunk, a.T - t0));
-  const int col = by * 256 + threadIdx.x;
-  const bool active = col < j.cols;
-  const float g = (j.is_h && active) ? bf16_bits_to_f32(a.gamma[col]) : 0.f;
-  for (int k0 = 0; k0 < j.ranks; k0 += 32) {
-    const int kn = std::min(32, j.ranks - k0);
-    __syncthreads();
-    for (int e = threadIdx.x; e < nt * 32; e += 256) {
-      const int tt = e / 32, k = e % 32;
-      p_s[tt][k] = k < kn ? bf16_bits_to_f32(j.pv[(t0 + tt) * j.ldp + k0 + k]) : 0.f;
+// Buffer loads: every source is addressed as (per-block descriptor, 32-bit byte offset),
+// and offsets at or past the descriptor's size read as zero.  That covers tokens past T in
+// the last chunk, ranks past the job's count and columns past the job's width without any
+// clamping in the loop.
+constexpr uint32_t kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kOutOfRange = 0x7fffffff;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+
+template <int CPL>
+struct LoraVec;
+template <>
+struct LoraVec<8> {
+  typedef uint32_t type __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  }
+};
+template <>
+struct LoraVec<4> {
+  typedef uint32_t type __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ type load(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  }
+};
+
+template <int CPL, int RB>
+struct LoraStep {
+  typename LoraVec<CPL>::type m[8];  // tokens 8 * h32 + u of the step, CPL columns each
+  uint16_t p[RB][8];                 // P of the lane's rank in each block, same tokens
+  float inv[8];
+};
+
+template <int RB>
+struct LoraSrc {
+  __amdgpu_buffer_rsrc_t m, p, inv;
+  int m_off;      // lane's byte offset at the step's first row (its half's row 0)
+  int m_row;      // bytes per M row
+  int p_off[RB];  // lane's byte offset of (row 0 of its half, its rank), or out of range
+  int p_row;
+  int inv_off;
+};
+
+template <int CPL, int RB, bool SCALED>
+__device__ __forceinline__ void lora_load(LoraStep<CPL, RB>& st, const LoraSrc<RB>& src, int row) {
+  // row: first token of the step relative to the chunk
+#pragma unroll
+  for (int u = 0; u < 8; ++u) st.m[u] = LoraVec<CPL>::load(src.m, src.m_off + (row + u) * src.m_row);
+#pragma unroll
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      st.p[b][i] = __builtin_amdgcn_raw_buffer_load_b16(src.p, src.p_off[b] + (row + i) * src.p_row, 0, 0);
+  if (SCALED) {
+    // into the named-component vector type: the builtin's own vector type, subscripted and
+    // bit-cast, reads element 0 for every index
+    const LoraVec<8>::type v0 = LoraVec<8>::load(src.inv, src.inv_off + row * 4);
+    const LoraVec<8>::type v1 = LoraVec<8>::load(src.inv, src.inv_off + row * 4 + 16);
+    st.inv[0] = __uint_as_float(v0.x);
+    st.inv[1] = __uint_as_float(v0.y);
+    st.inv[2] = __uint_as_float(v0.z);
+    st.inv[3] = __uint_as_float(v0.w);
+    st.inv[4] = __uint_as_float(v1.x);
+    st.inv[5] = __uint_as_float(v1.y);
+    st.inv[6] = __uint_as_float(v1.z);
+    st.inv[7] = __uint_as_float(v1.w);
+  }
+}
+
+template <int CPL, int RB, bool SCALED>
+__device__ __forceinline__ void lora_mfma(const LoraStep<CPL, RB>& st, floatx16 (&acc)[CPL][RB]) {
+  bf16x8 pf[RB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint16_t v = st.p[b][i];
+      if (SCALED) v = f32_to_bf16_bits(bf16_bits_to_f32(v) * st.inv[i]);
+      pf[b][i] = __builtin_bit_cast(__bf16, v);
     }
-    __syncthreads();
-    float acc[32];
+  }
 #pragma unroll
-    for (int k = 0; k < 32; ++k) acc[k] = 0.f;
-    if (active) {
-      for (int tt = 0; tt < nt; ++tt) {
-        float mv = bf16_bits_to_f32(j.mat[(t0 + tt) * j.ldm + col]);
-        if (j.is_h) mv = round_bf16(mv * a.inv[t0 + tt] * g);
+  for (int c = 0; c < CPL; ++c) {
+    // column c of the lane's CPL: half (c & 1) of dword c / 2 of each token's vector
+    uint32_t w[4];
 #pragma unroll
-        for (int k = 0; k < 32; ++k) acc[k] = fmaf(p_s[tt][k], mv, acc[k]);
-      }
-      float* o = j.out + (static_cast<int64_t>(chunk) * j.ranks + k0) * j.cols + col;
-      for (int k = 0; k < kn; ++k) o[static_cast<int64_t>(k) * j.cols] = acc[k];
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = st.m[2 * q][c >> 1], hi = st.m[2 * q + 1][c >> 1];
+      w[q] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    }
+    const bf16x8 af = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+    for (int b = 0; b < RB; ++b) acc[c][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, pf[b], acc[c][b], 0, 0, 0);
+  }
+}
+
+// Two register sets in turn: the loads of one step are in flight while the other computes.
+// Rows are taken 32 at a time; past the chunk's rows every load reads zero.
+template <int CPL, int RB, bool SCALED>
+__device__ __forceinline__ void lora_steps(const LoraSrc<RB>& src, int rows, floatx16 (&acc)[CPL][RB]) {
+  LoraStep<CPL, RB> s0, s1;
+  lora_load<CPL, RB, SCALED>(s0, src, 0);
+  for (int row = 0; row < rows; row += 32) {
+    lora_load<CPL, RB, SCALED>(s1, src, row + 16);
+    lora_mfma<CPL, RB, SCALED>(s0, acc);
+    lora_load<CPL, RB, SCALED>(s0, src, row + 32);
+    lora_mfma<CPL, RB, SCALED>(s1, acc);
+  }
+}
+
+template <int CPL, int RB>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void lora_partial_kernel(LoraArgs a) {
+  const int lane = threadIdx.x, l32 = lane & 31, h32 = lane >> 5;
+  const int chunk = blockIdx.x % a.chunks;
+  int g = blockIdx.x / a.chunks, jb = 0;
+  while (jb < a.njobs - 1 && g >= a.job[jb].groups) g -= a.job[jb++].groups;
+  const LoraJob& j = a.job[jb];
+  const int c0 = (g % j.col_groups) * 32 * CPL;
+  const int k0 = (g / j.col_groups) * 32 * RB;
+  const int col = c0 + CPL * l32;
+  const int64_t t_begin = static_cast<int64_t>(chunk) * a.chunk;
+  const int rows = static_cast<int>(min(static_cast<int64_t>(a.chunk), a.T - t_begin));
+  const bool scaled = j.inv != nullptr;
+
+  LoraSrc<RB> src;
+  src.m = make_rsrc(j.mat + t_begin * j.ldm, static_cast<int64_t>(rows) * j.ldm * 2);
+  src.m_row = static_cast<int>(j.ldm * 2);
+  src.m_off = col < j.cols ? (8 * h32 * src.m_row + col * 2) : kOutOfRange;
+  src.p = make_rsrc(j.pv + t_begin * j.ldp, static_cast<int64_t>(rows) * j.ldp * 2);
+  src.p_row = static_cast<int>(j.ldp * 2);
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int k = k0 + 32 * b + l32;
+    src.p_off[b] = k < j.ranks ? (8 * h32 * src.p_row + k * 2) : kOutOfRange;
+  }
+  src.inv = make_rsrc(scaled ? j.inv + t_begin : j.inv, scaled ? rows * 4 : 0);
+  src.inv_off = 8 * h32 * 4;
+
+  floatx16 acc[CPL][RB];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+#pragma unroll
+    for (int b = 0; b < RB; ++b) acc[c][b] = floatx16{};
+
+  if (scaled)
+    lora_steps<CPL, RB, true>(src, rows, acc);
+  else
+    lora_steps<CPL, RB, false>(src, rows, acc);
+
+  // lane: rank k0 + 32 b + l32; rows i of the 32x32 result are columns c0 + CPL * i + c
+  float* o = j.out + static_cast<int64_t>(chunk) * j.ranks * j.cols;
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int k = k0 + 32 * b + l32;
+    if (k >= j.ranks) continue;
+    float* orow = o + static_cast<int64_t>(k) * j.cols;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int c = c0 + CPL * ((v >> 2) * 8 + h32 * 4 + (v & 3));
+      if (c >= j.cols) continue;
+#pragma unroll
+      for (int q = 0; q < CPL; q += 4)
+        *reinterpret_cast<float4*>(orow + c + q) =
+            make_float4(acc[q][b][v], acc[q + 1][b][v], acc[q + 2][b][v], acc[q + 3][b][v]);
     }
   }
 }
 
-// dA_t[k][j] = sum_chunks PdA[c][off_t + k][j];  dB_t[n][k] = s sum_chunks PdB_t[c][k][n].
+// dA_t[k][c] = gamma[c] sum_chunks PdA[ch][off_t + k][c];  dB_t[n][k] = s sum_chunks PdB_t[ch][k][n].
+// Chunks are summed in a fixed order (four interleaved running sums), so results are
+// reproducible run to run.
 struct ReduceArgs {
   const float* pda;
   const float* pdb[3];
+  const uint16_t* gamma;
   float* da[3];
   float* db[3];
   int off[3], nt[3];
@@ -438,24 +600,37 @@ struct ReduceArgs {
   uint32_t targets;
 };
 
+__device__ __forceinline__ float sum_chunks(const float* p, int64_t stride, int chunks) {
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  int c = 0;
+  for (; c + 4 <= chunks; c += 4) {
+    s0 += p[(c + 0) * stride];
+    s1 += p[(c + 1) * stride];
+    s2 += p[(c + 2) * stride];
+    s3 += p[(c + 3) * stride];
+  }
+  for (; c < chunks; ++c) s0 += p[c * stride];
+  return (s0 + s1) + (s2 + s3);
+}
+
 __global__ __launch_bounds__(256) void lora_reduce_kernel(ReduceArgs a) {
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  const int64_t sa = static_cast<int64_t>(a.R) * a.d;
   for (int t = 0; t < 3; ++t) {
     if (!((a.targets >> t) & 1u)) continue;
     const int64_t na = static_cast<int64_t>(a.r) * a.d;
     for (int64_t e = gid; e < na; e += stride) {
-      const int64_t k = e / a.d, j = e % a.d;
-      float s = 0.f;
-      for (int c = 0; c < a.chunks; ++c) s += a.pda[(static_cast<int64_t>(c) * a.R + a.off[t] + k) * a.d + j];
-      a.da[t][e] = s;
+      const int64_t k = e / a.d, c = e % a.d;
+      const float s = a.chunks ? sum_chunks(a.pda + (a.off[t] + k) * a.d + c, sa, a.chunks) : 0.f;
+      a.da[t][e] = bf16_bits_to_f32(a.gamma[c]) * s;
     }
     const int64_t nb = static_cast<int64_t>(a.nt[t]) * a.r;
+    const int64_t sb = nb;
     for (int64_t e = gid; e < nb; e += stride) {
-      const int64_t n = e / a.r, k = e % a.r;
-      float s = 0.f;
-      for (int c = 0; c < a.chunks; ++c) s += a.pdb[t][(static_cast<int64_t>(c) * a.r + k) * a.nt[t] + n];
-      a.db[t][e] = a.scale * s;
+      const int64_t k = e / a.nt[t], n = e % a.nt[t];  // n fastest: coalesced partial reads
+      const float s = a.chunks ? sum_chunks(a.pdb[t] + k * a.nt[t] + n, sb, a.chunks) : 0.f;
+      a.db[t][n * a.r + k] = a.scale * s;
     }
   }
 }
@@ -471,7 +646,7 @@ int cu_count_bwd() {
 
 bool bwd_tiled_supports(const FwdParams& p) {
   return p.D % 2 == 0 && p.D <= 512 && (p.Hq * p.D) % 64 == 0 && (p.Hkv * p.D) % 64 == 0 && p.d % 256 == 0 &&
-         p.d <= (1 << 20) && p.r <= kMaxRank && p.T <= (int64_t{1} << 24);
+         p.d < (1 << 19) && p.N + 256 < (1 << 19) && p.r <= kMaxRank && p.T <= (int64_t{1} << 24);
 }
 
 size_t bwd_tiled_workspace_bytes(const FwdParams& p) { return bwd_layout(p).total; }
@@ -535,51 +710,44 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
 
     if (lora) {
       // ---- V' = bf16(s G_t B_t) into Gcat's LoRA columns; U_t = bf16(inv x A'_t^T)
-      RankArgs va{};
-      RankArgs ua{};
-      va.lda = L.K;
-      va.T = ua.T = p.T;
-      va.r = ua.r = p.r;
-      va.out = at<uint16_t>(ws, L.gcat);
-      va.ldo = L.K;
-      va.scale = p.scale;
-      va.inv = nullptr;
-      ua.lda = p.d;
-      ua.out = at<uint16_t>(ws, L.u);
-      ua.ldo = L.R;
-      ua.scale = 1.0f;
-      ua.inv = at<float>(ws, L.inv);
-      int nj = 0;
-      int last_t = -1;
+      RankArgs ra2{};
+      ra2.T = p.T;
+      ra2.r = p.r;
+      int nj = 0, last_t = -1;
       for (int t = 0; t < 3; ++t)
         if (p.targets & (1u << t)) last_t = t;
       for (int t = 0; t < 3; ++t) {
         if (!(p.targets & (1u << t))) continue;
-        RankJob& vj = va.job[nj];
+        RankJob& vj = ra2.job[nj++];
         vj.a = at<uint16_t>(ws, L.gcat) + lo[t];
+        vj.lda = L.K;
         vj.bs = at<uint16_t>(ws, L.bt[t]);
         vj.ldb = nt[t];
         vj.nk = nt[t] / BK;
+        vj.out = at<uint16_t>(ws, L.gcat);
+        vj.ldo = L.K;
         vj.col0 = p.N + L.off[t];
         vj.pad_to = t == last_t ? static_cast<int>(L.K) : vj.col0 + p.r;
-        RankJob& uj = ua.job[nj];
+        vj.scale = p.scale;
+        vj.inv = nullptr;
+        RankJob& uj = ra2.job[nj++];
         uj.a = static_cast<const uint16_t*>(p.x);
+        uj.lda = p.d;
         uj.bs = at<uint16_t>(ws, L.ap[t]);
         uj.ldb = p.d;
         uj.nk = static_cast<int>(p.d / BK);
+        uj.out = at<uint16_t>(ws, L.u);
+        uj.ldo = L.R;
         uj.col0 = L.off[t];
         uj.pad_to = uj.col0 + p.r;
-        ++nj;
+        uj.scale = 1.0f;
+        uj.inv = at<float>(ws, L.inv);
       }
-      va.njobs = ua.njobs = nj;
-      const dim3 grid(static_cast<unsigned>((p.T + BM - 1) / BM));
-      if (p.r <= 32) {
-        hipLaunchKernelGGL(rank_kernel<1>, grid, dim3(kThreads), 0, s, va);
-        hipLaunchKernelGGL(rank_kernel<1>, grid, dim3(kThreads), 0, s, ua);
-      } else {
-        hipLaunchKernelGGL(rank_kernel<2>, grid, dim3(kThreads), 0, s, va);
-        hipLaunchKernelGGL(rank_kernel<2>, grid, dim3(kThreads), 0, s, ua);
-      }
+      const dim3 grid(static_cast<unsigned>((p.T + BM - 1) / BM), nj);
+      if (p.r <= 32)
+        hipLaunchKernelGGL(rank_kernel<1>, grid, dim3(kThreads), 0, s, ra2);
+      else
+        hipLaunchKernelGGL(rank_kernel<2>, grid, dim3(kThreads), 0, s, ra2);
     }
 
     // ---- dh and dx
@@ -603,40 +771,45 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
 
     if (lora) {
       // ---- LoRA gradient partial sums
-      PartialArgs pa2{};
-      int nj = 0, ycount = 0;
-      PartialJob& ja = pa2.job[nj];
+      LoraArgs la{};
+      int nj = 0, items = 0;
+      LoraJob& ja = la.job[nj];
       ja.mat = static_cast<const uint16_t*>(p.x);
       ja.ldm = p.d;
       ja.cols = static_cast<int>(p.d);
       ja.pv = at<uint16_t>(ws, L.gcat) + p.N;
       ja.ldp = L.K;
       ja.ranks = L.R;
+      ja.inv = at<float>(ws, L.inv);
       ja.out = at<float>(ws, L.pda);
-      ja.is_h = 1;
-      pa2.col_blocks[nj] = (ja.cols + 255) / 256;
-      ycount += pa2.col_blocks[nj];
+      ja.groups = L.groups[0];
+      ja.col_groups = static_cast<int>(p.d / (32 * L.cpl));
+      items += ja.groups;
       ++nj;
       for (int t = 0; t < 3; ++t) {
         if (!(p.targets & (1u << t))) continue;
-        PartialJob& jb = pa2.job[nj];
+        LoraJob& jb = la.job[nj++];
         jb.mat = at<uint16_t>(ws, L.gcat) + lo[t];
         jb.ldm = L.K;
         jb.cols = nt[t];
         jb.pv = at<uint16_t>(ws, L.u) + L.off[t];
         jb.ldp = L.R;
         jb.ranks = p.r;
+        jb.inv = nullptr;
         jb.out = at<float>(ws, L.pdb[t]);
-        jb.is_h = 0;
-        pa2.col_blocks[nj] = (jb.cols + 255) / 256;
-        ycount += pa2.col_blocks[nj];
-        ++nj;
+        jb.groups = L.groups[t + 1];
+        jb.col_groups = (nt[t] + 32 * L.cpl - 1) / (32 * L.cpl);
+        items += jb.groups;
       }
-      pa2.njobs = nj;
-      pa2.gamma = static_cast<const uint16_t*>(p.gamma);
-      pa2.inv = at<float>(ws, L.inv);
-      pa2.T = p.T;
-      hipLaunchKernelGGL(lora_partial_kernel, dim3(L.chunks, ycount), dim3(256), 0, s, pa2);
+      la.njobs = nj;
+      la.chunk = L.chunk;
+      la.chunks = L.chunks;
+      la.T = p.T;
+      const dim3 grid(static_cast<unsigned>(items * L.chunks));
+      if (L.cpl == 8)
+        hipLaunchKernelGGL((lora_partial_kernel<8, 1>), grid, dim3(64), 0, s, la);
+      else
+        hipLaunchKernelGGL((lora_partial_kernel<4, 2>), grid, dim3(64), 0, s, la);
     }
   }
 
@@ -644,6 +817,7 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
     // ---- dA, dB (zero when T == 0: no chunks)
     ReduceArgs rd{};
     rd.pda = at<float>(ws, L.pda);
+    rd.gamma = static_cast<const uint16_t*>(p.gamma);
     for (int t = 0; t < 3; ++t) {
       rd.pdb[t] = at<float>(ws, L.pdb[t]);
       rd.da[t] = bp.da[t];
@@ -657,7 +831,11 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
     rd.chunks = L.chunks;
     rd.scale = p.scale;
     rd.targets = p.targets;
-    hipLaunchKernelGGL(lora_reduce_kernel, dim3(512), dim3(256), 0, s, rd);
+    int64_t n_out = 0;
+    for (int t = 0; t < 3; ++t)
+      if (p.targets & (1u << t)) n_out = std::max<int64_t>(n_out, static_cast<int64_t>(p.r) * std::max<int64_t>(p.d, nt[t]));
+    const unsigned rgrid = static_cast<unsigned>(std::min<int64_t>(std::max<int64_t>((n_out + 255) / 256, 1), 2048));
+    hipLaunchKernelGGL(lora_reduce_kernel, dim3(rgrid), dim3(256), 0, s, rd);
   }
   return hipGetLastError();
 }
