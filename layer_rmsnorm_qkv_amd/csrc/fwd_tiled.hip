@@ -397,9 +397,4 @@ hipError_t launch_fwd_tiled(const FwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// ---- the decode family is not built yet
-bool decode_supports(const FwdParams&) { return false; }
-size_t decode_workspace_bytes(const FwdParams&) { return 0; }
-hipError_t launch_fwd_decode(const FwdParams&, hipStream_t) { return hipErrorNotSupported; }
-
 }  // namespace lrq

@@ -40,6 +40,13 @@ SMALL_BF16 = {
     "dec_t64": DEC.replace(d_model=1024, n_q_heads=8, n_kv_heads=8),
     "l3_t1": L3.replace(n_tokens=1, d_model=256, n_q_heads=4, n_kv_heads=1),
     "l3_d64head": L3.replace(n_tokens=45, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64),
+    # decode-family shapes: one row, several 64-row groups with a ragged tail, GQA with a rank
+    # that is not a multiple of 16 on all targets plus bias, 64-wide heads with one target
+    "dec_t1": DEC.replace(n_tokens=1, d_model=512, n_q_heads=4, n_kv_heads=4),
+    "dec_t200_gqa_r24": L3.replace(n_tokens=200, d_model=1024, n_q_heads=8, n_kv_heads=2, lora_rank=24,
+                                   lora_targets=TQ | TK | TV, has_bias=True, bias_var=0.02),
+    "dec_d64head_konly": DEC.replace(n_tokens=33, d_model=512, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                                     lora_targets=TK, lora_rank=5),
 }
 
 
@@ -96,7 +103,7 @@ def test_forward_full_size_sampled(name, variant):
 def test_zero_b_equals_no_adapters_bitwise(variant):
     """B = 0 gives bit-for-bit the output of the same call without adapters."""
     import torch
-    w = SMALL_BF16["l2_t257_allt"]
+    w = SMALL_BF16["dec_t200_gqa_r24" if variant == "decode" else "l2_t257_allt"]
     inp = wl.make_inputs(w)
     if B.lrq_select_variant(desc_for(w, variant=VARIANTS[variant])) < 0:
         pytest.skip("variant does not cover this shape")
