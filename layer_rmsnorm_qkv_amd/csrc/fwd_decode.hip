@@ -1,239 +1,216 @@
 // Decode family of the forward (bf16, at most 256 rows): with so few rows, reading W_qkv
-// from HBM is the whole cost, so the kernels are built around streaming W once at full
-// bandwidth while the per-row work (RMSNorm, the rank-r down product) is done up front.
+// from HBM is the whole cost, so the work is arranged around streaming W once.
 //
-//   prep  one block per (slice of d, 32 LoRA ranks, 64 rows):
-//           xg = bf16(x * gamma)                       [Tp][d]   (written by rank block 0)
-//           ss[ks][row]   = sum over the slice of x^2             (partial row statistics)
-//           Up[ks][row][k] = sum over the slice of xg A^T (MFMA)   (partial LoRA-down)
-//   main  one block per 64 output columns (32 rotate-half pairs of one head) and 64 rows:
-//           acc = xg W^T with d split between the 4 waves (register prefetch ring), summed
-//           through LDS; then  y = inv * acc + B_t bf16(s * inv * U_t) + b,  rotate-half
-//           on q and k heads, bf16 store.
-// inv = 1 / sqrt(sum ss / d + eps) and U_t = sum Up are summed in a fixed order, so results
-// are the same run to run.  Operator reading: the fused operator computes
-// RoPE(W h + b + s B (A h)) with h = x * inv * gamma; here inv is applied after the
-// products (it is a per-row scalar), gamma before them.
+//   main    one block per 64 weight rows and 64 token rows.  A "W block" takes the W rows
+//           of 32 rotate-half pairs of one head (columns col0 + 0..31 and col0 + D/2 + 0..31);
+//           an "A block" (one per LoRA target) takes the 64 (padded) rows of A_t.  x and the
+//           weight rows stream through a 4-stage LDS ring (direct-to-LDS loads); each wave
+//           forms bf16(x * gamma) from the staged x and gamma, accumulates x^2 for the row
+//           statistics and multiplies its share of every stage (32x32x16 bf16 MFMA).  The four
+//           waves' partial products are summed through LDS, then
+//             W block:  y = RoPE(inv * acc + b): bf16 into out for columns without an
+//                       adapter, fp32 into the workspace for columns that get a LoRA term
+//             A block:  U_t = bf16(s * inv * acc) into the workspace
+//   finish  one block per 64 adapted columns and 64 rows:  out = bf16(y + RoPE(B_t U_t)),
+//           where RoPE is applied to the LoRA term on its own (the rotation is linear).
+//
+// The operator is RoPE(W h + b + s B (A h)) with h = x * inv * gamma; inv, a per-row scalar,
+// is applied after the products and gamma before them.  Every sum runs in a fixed order, so
+// results are the same run to run.
 #include "lrq_internal.h"
+#include "tile_common.h"
 
 namespace lrq {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRows = 64;     // rows per row group
-constexpr int kSlices = 8;    // slices of d in the prep kernel
-constexpr int kRing = 8;      // main-loop steps (16 columns of d each) in flight per wave
+constexpr int kRows = 64;                         // token rows per row group
+constexpr int kBK = 128;                          // columns of d per ring stage
+constexpr int kStages = 4;                        // ring depth
+constexpr int kPartBytes = kRows * kBK * 2;       // 16 KB: x or weight rows of one stage
+constexpr int kStageBytes = 2 * kPartBytes;       // x part, then weight part
+constexpr int kRingBytes = kStages * kStageBytes; // 128 KB
+constexpr int kMaxD = 8192;                       // gamma is staged whole in LDS
+constexpr int kChunks = kBK / 8;                  // 16-byte chunks per staged row
+constexpr int kLoads = 2 * kPartBytes / 4096;     // direct-to-LDS loads per thread per stage
 constexpr int kMaxTokens = 256;
 
 size_t al256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
 struct DecodeLayout {
-  int Tp;  // rows rounded up to the row group
-  int R;   // sum of the targets' ranks
-  int off[3];
-  size_t xg, up, ss, total;
+  int Tp;      // rows rounded up to the row group
+  int nt;      // number of LoRA targets
+  int tgt[3];  // target of A block i
+  size_t y, u, total;
 };
 
 DecodeLayout decode_layout(const FwdParams& p) {
   DecodeLayout L{};
   L.Tp = static_cast<int>((p.T + kRows - 1) / kRows * kRows);
-  int R = 0;
-  for (int t = 0; t < 3; ++t) {
-    L.off[t] = (p.targets & (1u << t)) ? R : -1;
-    if (p.targets & (1u << t)) R += p.r;
-  }
-  L.R = R;
+  for (int t = 0; t < 3; ++t)
+    if (p.targets & (1u << t)) L.tgt[L.nt++] = t;
   size_t o = 0;
-  L.xg = o;
-  o += al256(static_cast<size_t>(L.Tp) * p.d * 2);
-  L.up = o;
-  o += al256(static_cast<size_t>(kSlices) * L.Tp * (R > 0 ? R : 1) * 4);
-  L.ss = o;
-  o += al256(static_cast<size_t>(kSlices) * L.Tp * 4);
+  L.y = o;  // fp32 [Tp][N]: adapted columns before their LoRA term
+  o += al256(L.nt ? static_cast<size_t>(L.Tp) * p.N * 4 : 0);
+  L.u = o;  // bf16 [Tp][nt * 64]: s * inv * U_t, ranks padded to 64
+  o += al256(static_cast<size_t>(L.Tp) * L.nt * 64 * 2);
   L.total = o;
   return L;
 }
 
-__device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16_bits(a)) | (static_cast<uint32_t>(f32_to_bf16_bits(b)) << 16);
-}
-
-// ---------------------------------------------------------------- prep
-struct PrepArgs {
-  const uint16_t* x;
-  const uint16_t* gamma;
-  const uint16_t* a[3];
-  uint16_t* xg;
-  float* up;  // [kSlices][Tp][R]
-  float* ss;  // [kSlices][Tp]
-  int64_t T;
-  int d, R, r, Tp;
-  int off[3];
-};
-
-// Waves: row tile rt = wave & 1 (32 rows), half kh = wave >> 1 of the block's slice.
-// MFMA operands come straight from global memory: both x rows and A rows hold the 8
-// consecutive columns of d that one lane feeds the 32x32x16 product.
-__global__ __launch_bounds__(256) void decode_prep_kernel(PrepArgs a) {
-  __shared__ float red[2][17][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l32 = lane & 31, h32 = lane >> 5;
-  const int rt = wave & 1, kh = wave >> 1;
-  const int ks = blockIdx.x, g = blockIdx.y, rg = blockIdx.z;
-  const int tile_row = rg * kRows + rt * 32;
-  const int row = tile_row + l32;
-  const bool row_ok = row < a.T;
-  const int slice = a.d / kSlices;
-  const int k_begin = ks * slice + kh * (slice / 2) + 8 * h32;
-  const int steps = slice / 32;
-
-  // the lane's LoRA rank (B operand column) and its A row
-  const int kr = g * 32 + l32;
-  const uint16_t* arow = nullptr;
-#pragma unroll
-  for (int t = 0; t < 3; ++t)
-    if (a.off[t] >= 0 && kr >= a.off[t] && kr < a.off[t] + a.r) arow = a.a[t] + static_cast<int64_t>(kr - a.off[t]) * a.d;
-
-  const uint16_t* xrow = a.x + static_cast<int64_t>(row_ok ? row : 0) * a.d;
-  uint16_t* xgrow = a.xg + static_cast<int64_t>(row) * a.d;
-  const bool write_xg = g == 0;
-  const bool lora = a.R > 0;
-
-  floatx16 acc = {};
-  float ss = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < steps; ++s) {
-    const int k = k_begin + 16 * s;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    const u32x4 xv = row_ok ? *reinterpret_cast<const u32x4*>(xrow + k) : zero;
-    const u32x4 gv = *reinterpret_cast<const u32x4*>(a.gamma + k);
-    const u32x4 av = arow ? *reinterpret_cast<const u32x4*>(arow + k) : zero;
-    u32x4 xgv;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t xw = xv[q], gw = gv[q];
-      const float x0 = lo_f(xw), x1 = hi_f(xw);
-      ss = fmaf(x0, x0, ss);
-      ss = fmaf(x1, x1, ss);
-      xgv[q] = pack2(x0 * lo_f(gw), x1 * hi_f(gw));
-    }
-    if (write_xg) *reinterpret_cast<u32x4*>(xgrow + k) = xgv;
-    if (lora) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xgv),
-                                                            __builtin_bit_cast(bf16x8, av), acc, 0, 0, 0);
-  }
-
-  // the second half of the slice is added to the first through LDS (fixed order)
-  if (kh == 1) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) red[rt][v][lane] = acc[v];
-    red[rt][16][lane] = ss;
-  }
-  __syncthreads();
-  if (kh != 0) return;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] += red[rt][v][lane];
-  ss += red[rt][16][lane];
-  ss += __shfl_xor(ss, 32);  // lanes l and l + 32 cover the two halves of a step for one row
-  if (write_xg && h32 == 0) a.ss[static_cast<int64_t>(ks) * a.Tp + row] = ss;
-  if (lora && kr < a.R) {
-    float* up = a.up + static_cast<int64_t>(ks) * a.Tp * a.R + kr;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int rr = tile_row + (v >> 2) * 8 + h32 * 4 + (v & 3);
-      up[static_cast<int64_t>(rr) * a.R] = acc[v];
-    }
-  }
-}
-
 // ---------------------------------------------------------------- main
 struct MainArgs {
-  const uint16_t* xg;
+  const uint16_t* x;
+  const uint16_t* gamma;
   const uint16_t* w;
   const uint16_t* bias;
-  const uint16_t* b[3];
-  const float* up;
-  const float* ss;
+  const uint16_t* a[3];  // A of the targets in A-block order
   const int32_t* pos;
   uint16_t* out;
+  float* y;
+  uint16_t* u;
   int64_t T;
-  int d, N, D, Tp, R, r;
+  int d, N, D, r, nt, n_wblocks;
   int col_k, col_v, rot_end;
-  int off[3];
+  uint32_t targets;
   float scale, eps;
   double log2_theta;
 };
 
-struct Step {
-  bf16x8 a0, a1, b0, b1;  // xg rows l32 and 32 + l32; W columns (pair halves) l32
-};
+// XOR pattern of the chunks of staged row `row`: 16 consecutive rows read at one logical
+// chunk land in 16 distinct 16-byte bank groups (ds_read_b128 serves 16 lanes per cycle).
+__device__ __forceinline__ int sw(int row, int chunk) { return row * (kBK * 2) + ((chunk ^ (row & 15)) << 4); }
 
-__device__ __forceinline__ void load_step(Step& st, const uint16_t* xa, const uint16_t* wb, int64_t ld, int64_t half_ld,
-                                          int k) {
-  st.a0 = *reinterpret_cast<const bf16x8*>(xa + k);
-  st.a1 = *reinterpret_cast<const bf16x8*>(xa + 32 * ld + k);
-  st.b0 = *reinterpret_cast<const bf16x8*>(wb + k);
-  st.b1 = *reinterpret_cast<const bf16x8*>(wb + half_ld + k);
+// Waits for the last kStages - 1 stages (all issued) and computes them.
+template <int I, typename F>
+__device__ __forceinline__ void drain(F& compute, int st) {
+  if constexpr (I < kStages - 1) {
+    tile::wait_barrier<(kStages - 2 - I) * kLoads>();
+    compute(st + I);
+    drain<I + 1>(compute, st);
+  }
 }
 
-__device__ __forceinline__ void mfma_step(const Step& st, floatx16 (&acc)[2][2]) {
-  acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(st.a0, st.b0, acc[0][0], 0, 0, 0);
-  acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(st.a0, st.b1, acc[0][1], 0, 0, 0);
-  acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(st.a1, st.b0, acc[1][0], 0, 0, 0);
-  acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(st.a1, st.b1, acc[1][1], 0, 0, 0);
+// bf16(x * g) of 8 values, and ss += sum of x^2 (products exact, fp32 sums)
+__device__ __forceinline__ bf16x8 scale8(const bf16x8& x, const bf16x8& g, float& ss) {
+  bf16x8 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16x2 v = {x[2 * e], x[2 * e + 1]};
+    ss = __builtin_amdgcn_fdot2_f32_bf16(v, v, ss, false);
+    o[2 * e] = static_cast<__bf16>(static_cast<float>(x[2 * e]) * static_cast<float>(g[2 * e]));
+    o[2 * e + 1] = static_cast<__bf16>(static_cast<float>(x[2 * e + 1]) * static_cast<float>(g[2 * e + 1]));
+  }
+  return o;
 }
 
-// Tiles: rt = row tile (32 rows), ct = pair half (ct 0: columns col0 + l32, ct 1: the same
-// plus D/2), so both members of a rotate-half pair sit in the same lane and register.
+// Tiles: rt = token-row tile (32 rows), ct = weight-row tile (32 rows).  In a W block the
+// weight rows of ct 0 and ct 1 are the two members of rotate-half pairs, so a pair sits in
+// the same lane and register of the two tiles.
 __global__ __launch_bounds__(256, 1) void decode_main_kernel(MainArgs a) {
-  __shared__ float4 red[4][4][4][64];  // [wave][tile][quad of registers][lane]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kRingBytes + 2 * kMaxD];
+  unsigned char* gs = smem + kRingBytes;  // gamma, [d] bf16
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h32 = lane >> 5;
   const int nb = blockIdx.x, rg = blockIdx.y;
+  const bool wblock = nb < a.n_wblocks;
+  const int half = a.D / 2;
   const int per_head = a.D / 64;
   const int head = nb / per_head, sub = nb % per_head;
-  const int half = a.D / 2;
-  const int col0 = head * a.D + sub * 32;
+  const int col0 = head * a.D + sub * 32;  // W blocks
+  const int ab = nb - a.n_wblocks;         // A blocks
   const int64_t ld = a.d;
-  const int kq = a.d / 4;  // this wave's quarter of d
-  const int steps = kq / 16;
 
-  const uint16_t* xa = a.xg + static_cast<int64_t>(rg * kRows + l32) * ld + wave * kq + 8 * h32;
-  const uint16_t* wb = a.w + static_cast<int64_t>(col0 + l32) * ld + wave * kq + 8 * h32;
-  const int64_t half_ld = static_cast<int64_t>(half) * ld;
+  // gamma into LDS: 1 KB per load instruction, wave w takes chunks w, w + 4, ...
+  const uint32_t lds_g = tile::lds_addr(gs);
+  const int gchunks = a.d * 2 / 1024;
+  for (int c = wave; c < gchunks; c += 4)
+    tile::dma16(reinterpret_cast<const unsigned char*>(a.gamma) + c * 1024 + lane * 16, lds_g + c * 1024);
+
+  // direct-to-LDS sources: this thread fills slots p = (kLoads/2 * wave + j) * 64 + lane of
+  // each part; slot p is (staged row p / kChunks, physical chunk p % kChunks).  Token rows
+  // past T re-read row T - 1 and padded A rows re-read row r - 1 (never stored).
+  constexpr int kPer = kLoads / 2;
+  const uint16_t* xsrc[kPer];
+  const uint16_t* wsrc[kPer];
+  const uint16_t* arows = a.a[0];
+#pragma unroll
+  for (int i = 1; i < 3; ++i)
+    if (i == ab) arows = a.a[i];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int p = (wave * kPer + j) * 64 + lane;
+    const int row = p / kChunks, chunk = (p % kChunks) ^ (row & 15);
+    const int64_t trow = min(static_cast<int64_t>(rg * kRows + row), a.T - 1);
+    xsrc[j] = a.x + trow * ld + chunk * 8;
+    const int64_t wrow = wblock ? col0 + (row >> 5) * half + (row & 31) : min(row, a.r - 1);
+    wsrc[j] = (wblock ? a.w : arows) + wrow * ld + chunk * 8;
+  }
+  const uint32_t lds0 = tile::lds_addr(smem) + wave * kPer * 1024;
+  auto issue = [&](int st) {
+    const uint32_t base = lds0 + (st % kStages) * kStageBytes;
+    const int k = st * kBK;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) tile::dma16(xsrc[j] + k, base + j * 1024);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) tile::dma16(wsrc[j] + k, base + kPartBytes + j * 1024);
+  };
+  const int nst = a.d / kBK;  // >= kStages - 1
+#pragma unroll
+  for (int st = 0; st < kStages - 1; ++st) issue(st);
 
   floatx16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
-
-  Step ring[kRing];
+  float ss[2] = {0.f, 0.f};  // token rows l32 and 32 + l32, this lane's columns
+  auto compute = [&](int st) {
+    const unsigned char* xs = smem + (st % kStages) * kStageBytes;
+    const unsigned char* ws = xs + kPartBytes;
 #pragma unroll
-  for (int q = 0; q < kRing; ++q) load_step(ring[q], xa, wb, ld, half_ld, 16 * q);
-  int s = 0;
-  for (; s + kRing < steps; s += kRing) {
-#pragma unroll
-    for (int q = 0; q < kRing; ++q) {
-      mfma_step(ring[q], acc);
-      load_step(ring[q], xa, wb, ld, half_ld, 16 * (s + q + kRing));
+    for (int i = 0; i < kBK / 64; ++i) {
+      const int c = (kBK / 64 * wave + i) * 2 + h32;
+      const bf16x8 g = *reinterpret_cast<const bf16x8*>(gs + (st * kChunks + c) * 16);
+      const bf16x8 a0 = scale8(*reinterpret_cast<const bf16x8*>(xs + sw(l32, c)), g, ss[0]);
+      const bf16x8 a1 = scale8(*reinterpret_cast<const bf16x8*>(xs + sw(32 + l32, c)), g, ss[1]);
+      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(ws + sw(l32, c));
+      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(ws + sw(32 + l32, c));
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
     }
+  };
+  // stage st lives in slot st % kStages; each thread has kLoads loads per stage (gamma's
+  // were issued first), so "stage st has landed" is vmcnt <= kLoads * (stages issued after
+  // st).  The barrier also tells every wave that the others are done with stage st - 1,
+  // whose slot is refilled next.
+  int st = 0;
+  for (; st + kStages - 1 < nst; ++st) {
+    tile::wait_barrier<(kStages - 2) * kLoads>();
+    issue(st + kStages - 1);
+    compute(st);
   }
-#pragma unroll
-  for (int q = 0; q < kRing; ++q) mfma_step(ring[q], acc);
+  drain<0>(compute, st);
+  tile::barrier_lds();  // the ring is reused below
 
-  // sum of the four quarters of d, in wave order
+  // ---- sums of the four waves' column subsets, in wave order: products, then x^2
+  float4(*red)[4][4][64] = reinterpret_cast<float4(*)[4][4][64]>(smem);
+  float(*rss)[2][64] = reinterpret_cast<float(*)[2][64]>(smem + 4 * 4 * 4 * 64 * 16);
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const floatx16& v = acc[t >> 1][t & 1];
-      red[wave][t][q][lane] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      const floatx16& v = acc[tt >> 1][tt & 1];
+      red[wave][tt][q][lane] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
     }
+  rss[wave][0][lane] = ss[0];
+  rss[wave][1][lane] = ss[1];
   __syncthreads();
   if (wave >= 2) return;
   const int rt = wave;
@@ -256,62 +233,45 @@ __global__ __launch_bounds__(256, 1) void decode_main_kernel(MainArgs a) {
       y[ct][4 * q + 2] = sum.z;
       y[ct][4 * q + 3] = sum.w;
     }
-
-  // per-row values for row (tile row + l32); other lanes' rows are fetched with __shfl
-  const int row_l = rg * kRows + rt * 32 + l32;
+  // row statistics of token row rt * 32 + l32 (lanes l32 and 32 + l32 held its two halves)
   float ssum = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < kSlices; ++ks) ssum += a.ss[static_cast<int64_t>(ks) * a.Tp + row_l];
+  for (int w = 0; w < 4; ++w) ssum += rss[w][rt][l32] + rss[w][rt][32 + l32];
   const float inv_l = 1.0f / sqrtf(ssum / static_cast<float>(a.d) + a.eps);
-  const int pos_l = row_l < a.T ? a.pos[row_l] : 0;
 
-  // LoRA up: the block's columns lie in one target
-  const int t = col0 < a.col_k ? 0 : (col0 < a.col_v ? 1 : 2);
-  floatx16 lo[2] = {floatx16{}, floatx16{}};
-  if (a.off[t] >= 0) {
-    const int lo_t = t == 0 ? 0 : (t == 1 ? a.col_k : a.col_v);
-    const float su = a.scale * inv_l;
-    for (int kk = 0; kk < a.r; kk += 16) {
-      bf16x8 uf;
+  if (!wblock) {
+    // U_t: lane holds rank ct * 32 + l32 of token rows (v / 4) * 8 + h32 * 4 + v % 4
+    uint16_t* ub = a.u + ab * 64;
+    const int64_t ldu = static_cast<int64_t>(a.nt) * 64;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int rank = kk + 8 * h32 + e;
-        float u = 0.f;
-        if (rank < a.r) {
-          const float* up = a.up + static_cast<int64_t>(row_l) * a.R + a.off[t] + rank;
+    for (int v = 0; v < 16; ++v) {
+      const int rsub = (v >> 2) * 8 + h32 * 4 + (v & 3);
+      const int64_t row = rg * kRows + rt * 32 + rsub;
+      const float f = a.scale * __shfl(inv_l, rsub);
 #pragma unroll
-          for (int ks = 0; ks < kSlices; ++ks) u += up[static_cast<int64_t>(ks) * a.Tp * a.R];
-        }
-        uf[e] = static_cast<__bf16>(u * su);
-      }
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const uint16_t* brow = a.b[t] + static_cast<int64_t>(col0 + ct * half + l32 - lo_t) * a.r;
-        bf16x8 bf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int rank = kk + 8 * h32 + e;
-          bf[e] = __builtin_bit_cast(__bf16, rank < a.r ? brow[rank] : uint16_t{0});
-        }
-        lo[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(uf, bf, lo[ct], 0, 0, 0);
-      }
+      for (int ct = 0; ct < 2; ++ct) ub[row * ldu + ct * 32 + l32] = f32_to_bf16_bits(f * y[ct][v]);
     }
+    return;
   }
 
+  const int t = col0 < a.col_k ? 0 : (col0 < a.col_v ? 1 : 2);
+  const bool adapted = (a.targets >> t) & 1u;
   const int c0 = col0 + l32, c1 = col0 + half + l32;
   const float b0 = a.bias ? bf16_bits_to_f32(a.bias[c0]) : 0.f;
   const float b1 = a.bias ? bf16_bits_to_f32(a.bias[c1]) : 0.f;
   const bool rot = col0 < a.rot_end;
   const int i_pair = sub * 32 + l32;  // frequency index within the head
   const double om = exp2(-(2.0 * i_pair / a.D) * a.log2_theta) * 0.15915494309189533577;  // turns
+  const int64_t myrow = rg * kRows + rt * 32 + l32;
+  const int pos_l = myrow < a.T ? a.pos[myrow] : 0;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int rsub = (v >> 2) * 8 + h32 * 4 + (v & 3);
     const int64_t row = rg * kRows + rt * 32 + rsub;
     const float inv = __shfl(inv_l, rsub);
     const int pos = __shfl(pos_l, rsub);
-    float y0 = fmaf(y[0][v], inv, lo[0][v] + b0);
-    float y1 = fmaf(y[1][v], inv, lo[1][v] + b1);
+    float y0 = fmaf(y[0][v], inv, b0);
+    float y1 = fmaf(y[1][v], inv, b1);
     if (rot) {
       const double tt = static_cast<double>(pos) * om;
       const float f = static_cast<float>(tt - rint(tt));
@@ -321,9 +281,112 @@ __global__ __launch_bounds__(256, 1) void decode_main_kernel(MainArgs a) {
       y1 = r1;
     }
     if (row < a.T) {
+      if (adapted) {
+        float* o = a.y + row * a.N;
+        o[c0] = y0;
+        o[c1] = y1;
+      } else {
+        uint16_t* o = a.out + row * a.N;
+        o[c0] = f32_to_bf16_bits(y0);
+        o[c1] = f32_to_bf16_bits(y1);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- finish
+struct FinishArgs {
+  const float* y;
+  const uint16_t* u;
+  const uint16_t* b[3];
+  const int32_t* pos;
+  uint16_t* out;
+  int64_t T;
+  int N, D, r, nt;
+  int col_k, col_v, rot_end;
+  int ublock[3];  // A block of target t, or -1
+  double log2_theta;
+};
+
+// Two waves, one per 32-row token tile; each holds both members of its 32 rotate-half pairs.
+// VEC: r is a multiple of 8, so a lane's 8 ranks of a B row are one aligned 16-byte load.
+template <bool VEC>
+__global__ __launch_bounds__(128) void decode_finish_kernel(FinishArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, h32 = lane >> 5;
+  const int nb = blockIdx.x, rg = blockIdx.y;
+  const int half = a.D / 2;
+  const int per_head = a.D / 64;
+  const int head = nb / per_head, sub = nb % per_head;
+  const int col0 = head * a.D + sub * 32;
+  const int t = col0 < a.col_k ? 0 : (col0 < a.col_v ? 1 : 2);
+  const int ublk = t == 0 ? a.ublock[0] : (t == 1 ? a.ublock[1] : a.ublock[2]);
+  if (ublk < 0) return;  // no adapter: main stored these columns
+  const uint16_t* bt = t == 0 ? a.b[0] : (t == 1 ? a.b[1] : a.b[2]);
+  const int rt = wave;
+  const int lo_t = t == 0 ? 0 : (t == 1 ? a.col_k : a.col_v);
+  const int64_t ldu = static_cast<int64_t>(a.nt) * 64;
+  const int64_t myrow = rg * kRows + rt * 32 + l32;
+  const uint16_t* urow = a.u + myrow * ldu + ublk * 64;
+
+  // every load is issued before any result is needed: y, U and B fragments, positions
+  const int c0 = col0 + l32, c1 = col0 + half + l32;
+  float yv[16][2];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int64_t row = min(rg * kRows + rt * 32 + (v >> 2) * 8 + h32 * 4 + (v & 3), a.T - 1);
+    yv[v][0] = a.y[row * a.N + c0];
+    yv[v][1] = a.y[row * a.N + c1];
+  }
+  const int pos_l = myrow < a.T ? a.pos[myrow] : 0;
+  // ranks past r: B is zero there (vector loads skip them; element loads are clamped into
+  // the row and zeroed), so the four rank steps run unconditionally (U holds finite padding)
+  bf16x8 uf[4], bf[4][2];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int rank0 = kk * 16 + 8 * h32;
+    uf[kk] = *reinterpret_cast<const bf16x8*>(urow + rank0);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const uint16_t* brow = bt + static_cast<int64_t>(col0 + ct * half + l32 - lo_t) * a.r;
+      if constexpr (VEC) {
+        bf[kk][ct] = bf16x8{};
+        if (rank0 < a.r) bf[kk][ct] = *reinterpret_cast<const bf16x8*>(brow + rank0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t v = brow[min(rank0 + e, a.r - 1)];
+          bf[kk][ct][e] = __builtin_bit_cast(__bf16, rank0 + e < a.r ? v : uint16_t{0});
+        }
+      }
+    }
+  }
+  floatx16 lo[2] = {floatx16{}, floatx16{}};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) lo[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(uf[kk], bf[kk][ct], lo[ct], 0, 0, 0);
+
+  const bool rot = col0 < a.rot_end;
+  const double om = exp2(-(2.0 * (sub * 32 + l32) / a.D) * a.log2_theta) * 0.15915494309189533577;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int rsub = (v >> 2) * 8 + h32 * 4 + (v & 3);
+    const int64_t row = rg * kRows + rt * 32 + rsub;
+    const int pos = __shfl(pos_l, rsub);
+    float l0 = lo[0][v], l1 = lo[1][v];
+    if (rot) {
+      const double tt = static_cast<double>(pos) * om;
+      const float f = static_cast<float>(tt - rint(tt));
+      const float sn = __builtin_amdgcn_sinf(f), cs = __builtin_amdgcn_cosf(f);
+      const float r0 = l0 * cs - l1 * sn, r1 = l1 * cs + l0 * sn;
+      l0 = r0;
+      l1 = r1;
+    }
+    if (row < a.T) {
       uint16_t* o = a.out + row * a.N;
-      o[c0] = f32_to_bf16_bits(y0);
-      o[c1] = f32_to_bf16_bits(y1);
+      o[c0] = f32_to_bf16_bits(yv[v][0] + l0);
+      o[c1] = f32_to_bf16_bits(yv[v][1] + l1);
     }
   }
 }
@@ -331,7 +394,8 @@ __global__ __launch_bounds__(256, 1) void decode_main_kernel(MainArgs a) {
 }  // namespace
 
 bool decode_supports(const FwdParams& p) {
-  return p.D % 64 == 0 && p.d % 512 == 0 && p.d <= (1 << 20) && p.T <= kMaxTokens && p.r <= kMaxRank;
+  return p.D % 64 == 0 && p.d % 512 == 0 && p.d <= kMaxD && p.d / kBK >= kStages - 1 && p.T <= kMaxTokens &&
+         p.r <= 64;
 }
 
 size_t decode_workspace_bytes(const FwdParams& p) { return decode_layout(p).total; }
@@ -342,50 +406,56 @@ hipError_t launch_fwd_decode(const FwdParams& p, hipStream_t s) {
   unsigned char* ws = static_cast<unsigned char*>(p.ws);
   const int groups = L.Tp / kRows;
 
-  PrepArgs pa{};
-  pa.x = static_cast<const uint16_t*>(p.x);
-  pa.gamma = static_cast<const uint16_t*>(p.gamma);
-  for (int t = 0; t < 3; ++t) {
-    pa.a[t] = static_cast<const uint16_t*>(p.a[t]);
-    pa.off[t] = L.off[t];
-  }
-  pa.xg = reinterpret_cast<uint16_t*>(ws + L.xg);
-  pa.up = reinterpret_cast<float*>(ws + L.up);
-  pa.ss = reinterpret_cast<float*>(ws + L.ss);
-  pa.T = p.T;
-  pa.d = static_cast<int>(p.d);
-  pa.R = L.R;
-  pa.r = p.r;
-  pa.Tp = L.Tp;
-  const int rank_blocks = L.R > 0 ? (L.R + 31) / 32 : 1;
-  hipLaunchKernelGGL(decode_prep_kernel, dim3(kSlices, rank_blocks, groups), dim3(256), 0, s, pa);
-
   MainArgs ma{};
-  ma.xg = pa.xg;
+  ma.x = static_cast<const uint16_t*>(p.x);
+  ma.gamma = static_cast<const uint16_t*>(p.gamma);
   ma.w = static_cast<const uint16_t*>(p.w);
   ma.bias = p.has_bias ? static_cast<const uint16_t*>(p.bias) : nullptr;
-  for (int t = 0; t < 3; ++t) {
-    ma.b[t] = static_cast<const uint16_t*>(p.b[t]);
-    ma.off[t] = L.off[t];
-  }
-  ma.up = pa.up;
-  ma.ss = pa.ss;
+  for (int i = 0; i < 3; ++i) ma.a[i] = static_cast<const uint16_t*>(p.a[L.tgt[i]]);
   ma.pos = p.pos;
   ma.out = static_cast<uint16_t*>(p.out);
+  ma.y = reinterpret_cast<float*>(ws + L.y);
+  ma.u = reinterpret_cast<uint16_t*>(ws + L.u);
   ma.T = p.T;
   ma.d = static_cast<int>(p.d);
   ma.N = p.N;
   ma.D = p.D;
-  ma.Tp = L.Tp;
-  ma.R = L.R;
   ma.r = p.r;
+  ma.nt = L.nt;
+  ma.n_wblocks = p.N / 64;
   ma.col_k = p.col_k;
   ma.col_v = p.col_v;
   ma.rot_end = p.rot_end;
+  ma.targets = p.targets;
   ma.scale = p.scale;
   ma.eps = p.eps;
   ma.log2_theta = log2(p.theta);
-  hipLaunchKernelGGL(decode_main_kernel, dim3(p.N / 64, groups), dim3(256), 0, s, ma);
+  hipLaunchKernelGGL(decode_main_kernel, dim3(ma.n_wblocks + L.nt, groups), dim3(256), 0, s, ma);
+  if (L.nt == 0) return hipGetLastError();
+
+  FinishArgs fa{};
+  fa.y = ma.y;
+  fa.u = ma.u;
+  for (int t = 0; t < 3; ++t) {
+    fa.b[t] = static_cast<const uint16_t*>(p.b[t]);
+    fa.ublock[t] = -1;
+  }
+  for (int i = 0; i < L.nt; ++i) fa.ublock[L.tgt[i]] = i;
+  fa.pos = p.pos;
+  fa.out = ma.out;
+  fa.T = p.T;
+  fa.N = p.N;
+  fa.D = p.D;
+  fa.r = p.r;
+  fa.nt = L.nt;
+  fa.col_k = p.col_k;
+  fa.col_v = p.col_v;
+  fa.rot_end = p.rot_end;
+  fa.log2_theta = ma.log2_theta;
+  if (p.r % 8 == 0)
+    hipLaunchKernelGGL(decode_finish_kernel<true>, dim3(p.N / 64, groups), dim3(128), 0, s, fa);
+  else
+    hipLaunchKernelGGL(decode_finish_kernel<false>, dim3(p.N / 64, groups), dim3(128), 0, s, fa);
   return hipGetLastError();
 }
 
