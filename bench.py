@@ -10,15 +10,21 @@ two device synchronisations; one JSON line is printed.
 
 * ``value``: tokens per second of the whole job (one GPU).
 * ``roofline``: the dominant kernel's algorithmic FLOPs (or bytes, for the bandwidth-bound
-  decode workload) per launch over its average launch duration, timed with HIP events on
-  the stream it is launched on, against MI355X's published peak (bf16 dense MFMA
-  2500 TFLOP/s, HBM 8000 GB/s).  ``traffic`` comes from rocprofv3 FETCH_SIZE/WRITE_SIZE
-  counters recorded under profiles/ for the same kernel source (null if the source changed).
+  decode workload) per launch over its average launch duration, against MI355X's published
+  peak (bf16 dense MFMA 2500 TFLOP/s, HBM 8000 GB/s).  The duration comes from the
+  library's measurement hook (HIP events recorded on the launch stream around that one
+  kernel in every timed call); ``call_ms`` is the whole library call, timed the same way
+  from here.  ``traffic`` comes from rocprofv3 FETCH_SIZE/WRITE_SIZE counters recorded
+  under profiles/ for the same kernel source (null if the source changed).
 * ``cpu_baseline``: the CPU oracle (float64 numpy, untuned) timed on this host on a bounded
   sample of the same workload's rows.
 
 ``--copy-probe`` instead runs a plain device copy of known size (the calibration kernel for
-the FETCH_SIZE / WRITE_SIZE counters).
+the FETCH_SIZE / WRITE_SIZE counters).  ``--record-traffic`` turns the counter files of
+such runs into profiles/traffic.json (no GPU needed):
+
+    python bench.py --record-traffic WORKLOAD --family FAMILY --kernel NAME \
+        --fetch DIR --write DIR --calib-fetch DIR --calib-write DIR --calib-bytes N
 """
 from __future__ import annotations
 
@@ -60,10 +66,33 @@ def algorithmic_work(w, T=None):
     return f_fwd, f_bwd, bytes_fwd
 
 
+def dominant_kernel_work(w, family: str, backward: bool):
+    """Algorithmic work of one launch of a call's dominant kernel: (amount, unit kind).
+
+    Forward, tiled or generic: every matmul FLOP of the forward.  Forward, decode: the bytes
+    the streaming kernel must move (x, gamma, W, bias, the targets' A, positions, and the
+    outputs of columns without an adapter; the LoRA-up pass writes the rest).  Backward,
+    tiled: dh = G W + sum_t V'_t A_t, 2 T d (N + sum of ranks) FLOPs.  Backward, generic:
+    every matmul FLOP of the backward."""
+    f_fwd, f_bwd, _ = algorithmic_work(w)
+    T, d, N, r = w.n_tokens, w.d_model, w.n_out, w.lora_rank
+    cols = w.target_columns()
+    ranks = sum(r for t in cols if w.lora_targets & t)
+    if backward:
+        return (2.0 * T * d * (N + ranks), "flop") if family == "tiled" else (f_bwd, "flop")
+    if family == "decode":
+        eb = 2
+        unadapted = sum(hi - lo for t, (lo, hi) in cols.items() if not (w.lora_targets & t))
+        nbytes = eb * (T * d + d + N * d + (N if w.has_bias else 0) + ranks * d + T * unadapted) + 4 * T
+        return nbytes, "bytes"
+    return f_fwd, "flop"
+
+
 def kernel_source_digest(variant_name: str) -> str:
     """sha256 of the sources that define a kernel family (for matching stored counters)."""
-    files = {"tiled": ["fwd_tiled.hip"], "decode": ["fwd_decode.hip"], "generic": ["fwd_generic.hip"],
-             "bwd_tiled": ["bwd_tiled.hip"], "bwd_generic": ["bwd_generic.hip"]}[variant_name]
+    files = {"tiled": ["fwd_tiled.hip", "tile_common.h"], "decode": ["fwd_decode.hip", "tile_common.h"],
+             "generic": ["fwd_generic.hip"], "bwd_tiled": ["bwd_tiled.hip", "tile_common.h"],
+             "bwd_generic": ["bwd_generic.hip"]}[variant_name]
     h = hashlib.sha256()
     for f in files + ["lrq_internal.h"]:
         p = os.path.join(ROOT, "layer_rmsnorm_qkv_amd", "csrc", f)
@@ -81,6 +110,59 @@ def stored_traffic(workload: str, kernel: str):
     if not rec or rec.get("source_sha") != kernel_source_digest(kernel):
         return None
     return rec.get("bytes_per_launch")
+
+
+def _counter_means(directory: str, kernel_prefix: str):
+    """Mean counter value (KiB per dispatch) over the dispatches of one kernel in a
+    rocprofv3 --pmc csv directory, and the number of dispatches."""
+    import csv
+    import glob
+    vals = []
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            name = r["Kernel_Name"].replace("lrq::(anonymous namespace)::", "").replace("void ", "")
+            if name.startswith(kernel_prefix):
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no dispatch of {kernel_prefix} in {directory}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def record_traffic(args):
+    """HBM bytes per launch of one kernel from FETCH_SIZE / WRITE_SIZE passes, each scaled by
+    what the same counter reads for a device copy of known size; stored with the digest of
+    the kernel's source so that bench.py drops it once the kernel changes."""
+    fetch, nf = _counter_means(args.fetch, args.kernel)
+    write, nw = _counter_means(args.write, args.kernel)
+    cf, _ = _counter_means(args.calib_fetch, "__amd_rocclr_copyBuffer")
+    cw, _ = _counter_means(args.calib_write, "__amd_rocclr_copyBuffer")
+    # the copy probe's largest dispatch is the copy itself; smaller ones are fills
+    import csv
+    import glob
+
+    def largest(directory):
+        best = 0.0
+        for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if "copyBuffer" in r["Kernel_Name"]:
+                    best = max(best, float(r["Counter_Value"]))
+        return best
+    cf, cw = largest(args.calib_fetch), largest(args.calib_write)
+    ff = args.calib_bytes / (cf * 1024.0)
+    fw = args.calib_bytes / (cw * 1024.0)
+    rec = {"kernel": args.kernel, "source_sha": kernel_source_digest(args.family),
+           "fetch_size_kib": fetch, "write_size_kib": write, "fetch_factor": ff, "write_factor": fw,
+           "fetch_bytes": fetch * 1024.0 * ff, "write_bytes": write * 1024.0 * fw,
+           "bytes_per_launch": fetch * 1024.0 * ff + write * 1024.0 * fw, "dispatches": [nf, nw],
+           "calibration": f"{args.calib_bytes} B device copy (bench.py --copy-probe {args.calib_bytes}): "
+                          f"FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB per dispatch"}
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        data = {}
+    data[f"{args.record_traffic}:{args.family}"] = rec
+    json.dump(data, open(TRAFFIC_FILE, "w"), indent=1, sort_keys=True)
+    print(json.dumps(rec))
 
 
 def cpu_baseline(w, inp, budget_s: float, rows_cap: int, gpu_rows_fn=None):
@@ -144,7 +226,18 @@ def main():
     ap.add_argument("--w-copies", type=int, default=0,
                     help="rotate among this many W_qkv copies (defeats the 256 MB MALL; default 4 for decode)")
     ap.add_argument("--copy-probe", type=int, default=0, help="run a device copy of this many bytes and exit")
+    ap.add_argument("--record-traffic", default="", help="workload name: store counter traffic and exit")
+    ap.add_argument("--family", default="", help="kernel family key (tiled, decode, bwd_tiled, ...)")
+    ap.add_argument("--kernel", default="", help="kernel name prefix in the counter files")
+    ap.add_argument("--fetch", default="")
+    ap.add_argument("--write", default="")
+    ap.add_argument("--calib-fetch", default="")
+    ap.add_argument("--calib-write", default="")
+    ap.add_argument("--calib-bytes", type=int, default=1 << 30)
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this operator is measured on one GPU only; --gpus {args.gpus} is not supported "
@@ -188,6 +281,7 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
+    B.lrq_kernel_timing(True)
     t0 = time.perf_counter()
     for i in range(args.steps):
         e0, e1, e2 = ev[i]
@@ -202,6 +296,10 @@ def main():
     wall = time.perf_counter() - t0
     fwd_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
     bwd_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev])) if w.backward else 0.0
+    kfwd_ms, n_fwd = B.lrq_kernel_time_ms(False)
+    kbwd_ms, n_bwd = B.lrq_kernel_time_ms(True)
+    B.lrq_kernel_timing(False)
+    assert n_fwd == args.steps and n_bwd == (args.steps if w.backward else 0), (n_fwd, n_bwd)
 
     ms_per_step = wall * 1e3 / args.steps
     tokens = w.n_tokens
@@ -216,28 +314,36 @@ def main():
                    "kernel_family": vname, "parallelism": "none (1 GPU)",
                    "pass": "forward+backward" if w.backward else "forward"},
     }
-    # dominant kernel: the forward kernel (layer / decode workloads) or the larger of the two calls
+    # call-level rates (whole library calls)
     tflops_fwd = f_fwd / (fwd_ms * 1e-3) / 1e12
     result["tflops_forward"] = tflops_fwd
+    result["call_ms"] = {"forward": fwd_ms}
     if w.backward:
         result["tflops_backward"] = f_bwd / (bwd_ms * 1e-3) / 1e12
         result["tflops_step"] = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
+        result["call_ms"]["backward"] = bwd_ms
     if w.name == "decode":
-        gbs = bytes_fwd / (fwd_ms * 1e-3) / 1e9
-        traffic = stored_traffic(w.name, vname)
-        result["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                              "frac": gbs / PEAK_HBM_GBS, "traffic": traffic, "kernel": f"lrq forward ({vname})",
-                              "launch_ms": fwd_ms, "algorithmic_bytes": bytes_fwd}
+        result["gbs_forward_call"] = bytes_fwd / (fwd_ms * 1e-3) / 1e9
+    # dominant kernel: the longer of the forward and backward calls' dominant kernels
+    backward_dominant = w.backward and kbwd_ms > kfwd_ms
+    family = B.VARIANT_NAMES[prob.bwd_variant] if backward_dominant else vname
+    dom_ms = kbwd_ms if backward_dominant else kfwd_ms
+    work, kind = dominant_kernel_work(w, family, backward_dominant)
+    kname = {("tiled", False): "fwd_tiled_kernel", ("decode", False): "decode_main_kernel",
+             ("generic", False): "fwd_generic_kernel", ("tiled", True): "bwd_main_kernel",
+             ("generic", True): "bwd_generic_kernel"}[(family, backward_dominant)]
+    traffic = stored_traffic(w.name, ("bwd_" if backward_dominant else "") + family)
+    if kind == "bytes":
+        ach = work / (dom_ms * 1e-3) / 1e9
+        result["roofline"] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": ach / PEAK_HBM_GBS, "traffic": traffic, "kernel": kname,
+                              "launch_ms": dom_ms, "algorithmic_bytes": work}
     else:
-        dom_ms, dom_f, dom_name = fwd_ms, f_fwd, vname
-        if w.backward and bwd_ms > fwd_ms:
-            dom_ms, dom_f, dom_name = bwd_ms, f_bwd, "bwd_" + B.VARIANT_NAMES[prob.bwd_variant]
-        ach = dom_f / (dom_ms * 1e-3) / 1e12
         peak = PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+        ach = work / (dom_ms * 1e-3) / 1e12
         result["roofline"] = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
-                              "frac": ach / peak, "traffic": stored_traffic(w.name, dom_name),
-                              "kernel": f"lrq {'backward' if dom_name.startswith('bwd') else 'forward'} ({dom_name})",
-                              "launch_ms": dom_ms, "algorithmic_flop": dom_f}
+                              "frac": ach / peak, "traffic": traffic, "kernel": kname,
+                              "launch_ms": dom_ms, "algorithmic_flop": work}
     if not args.no_cpu_baseline:
         prob.w_qkv = w_list[0]
         got = prob.forward(stream=stream)

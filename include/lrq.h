@@ -155,6 +155,21 @@ const char* lrq_last_error(void);
 /* LRQ_ABI_VERSION of the loaded library. */
 int lrq_abi_version(void);
 
+/* Measurement hook (not part of the operator).  While enabled, every lrq_forward /
+ * lrq_backward call records a pair of HIP events on the caller's stream around the call's
+ * dominant kernel: the fused tile kernel of the tiled forward, the streaming kernel of the
+ * decode forward, the dh/dx product of the tiled backward, the single kernel of the
+ * generic family.  Enabling (or disabling) discards what was recorded.  Events are created
+ * on demand (at most 4096 pairs per direction) and kept until the process ends.  Not
+ * thread-safe: meant for one benchmarking thread.  Always LRQ_OK. */
+lrq_status lrq_kernel_timing(int enable);
+
+/* Mean duration in milliseconds of the dominant kernel over the forward (for_backward = 0)
+ * or backward (1) calls recorded since the hook was enabled, and their number; waits for
+ * the recorded events.  INVALID_ARG when mean_ms or count is NULL; LRQ_ERR_HIP if an event
+ * query fails.  count = 0 and mean 0 when nothing was recorded. */
+lrq_status lrq_kernel_time_ms(int for_backward, double* mean_ms, int* count);
+
 #ifdef __cplusplus
 }
 #endif

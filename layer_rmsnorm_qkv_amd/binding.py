@@ -22,7 +22,8 @@ VARIANT_NAMES = {LRQ_VARIANT_GENERIC: "generic", LRQ_VARIANT_TILED: "tiled", LRQ
 
 # every symbol include/lrq.h declares
 EXPORTED = ("lrq_forward", "lrq_backward", "lrq_workspace_size", "lrq_select_variant",
-            "lrq_status_string", "lrq_last_error", "lrq_abi_version")
+            "lrq_status_string", "lrq_last_error", "lrq_abi_version", "lrq_kernel_timing",
+            "lrq_kernel_time_ms")
 
 
 class LrqDesc(ctypes.Structure):
@@ -75,6 +76,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.lrq_last_error.restype = ctypes.c_char_p
         lib.lrq_abi_version.argtypes = []
         lib.lrq_abi_version.restype = ctypes.c_int
+        lib.lrq_kernel_timing.argtypes = [ctypes.c_int]
+        lib.lrq_kernel_timing.restype = ctypes.c_int
+        lib.lrq_kernel_time_ms.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                           ctypes.POINTER(ctypes.c_int)]
+        lib.lrq_kernel_time_ms.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -163,3 +169,14 @@ def lrq_last_error() -> str:
 
 def lrq_abi_version() -> int:
     return int(load().lrq_abi_version())
+
+
+def lrq_kernel_timing(enable: bool) -> None:
+    _check(load().lrq_kernel_timing(1 if enable else 0))
+
+
+def lrq_kernel_time_ms(for_backward: bool = False):
+    """(mean milliseconds, number of calls) of the dominant kernel since timing was enabled."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int(0)
+    _check(load().lrq_kernel_time_ms(1 if for_backward else 0, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

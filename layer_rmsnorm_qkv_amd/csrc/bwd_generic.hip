@@ -243,7 +243,9 @@ hipError_t launch(const BwdParams& bp, hipStream_t s) {
   }
   if (p.T > 0) {
     dim3 grid(static_cast<unsigned>((p.T + kRows - 1) / kRows));
+    timing_begin(s);
     hipLaunchKernelGGL((bwd_generic_kernel<TIn, kBf16>), grid, dim3(kThreads), 0, s, bp);
+    timing_end(s);
   }
   return hipGetLastError();
 }

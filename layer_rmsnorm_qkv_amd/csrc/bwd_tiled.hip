@@ -767,7 +767,9 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
     ma.items = n_mt * ma.n_nt;
     ma.remap = ma.items % 8 == 0;
     (void)cu_count_bwd;
+    timing_begin(s);
     hipLaunchKernelGGL(bwd_main_kernel, dim3(ma.items), dim3(kThreads), 0, s, ma);
+    timing_end(s);
 
     if (lora) {
       // ---- LoRA gradient partial sums

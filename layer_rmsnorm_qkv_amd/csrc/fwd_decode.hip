@@ -430,7 +430,9 @@ hipError_t launch_fwd_decode(const FwdParams& p, hipStream_t s) {
   ma.scale = p.scale;
   ma.eps = p.eps;
   ma.log2_theta = log2(p.theta);
+  timing_begin(s);
   hipLaunchKernelGGL(decode_main_kernel, dim3(ma.n_wblocks + L.nt, groups), dim3(256), 0, s, ma);
+  timing_end(s);
   if (L.nt == 0) return hipGetLastError();
 
   FinishArgs fa{};

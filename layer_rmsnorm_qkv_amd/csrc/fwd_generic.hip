@@ -205,7 +205,9 @@ template <typename TIn, bool kBf16>
 hipError_t launch(const FwdParams& p, hipStream_t s) {
   const int n_pairs = p.N / 2;
   dim3 grid(static_cast<unsigned>((p.T + kRows - 1) / kRows), (n_pairs + kPairs - 1) / kPairs);
+  timing_begin(s);
   hipLaunchKernelGGL((fwd_generic_kernel<TIn, kBf16>), grid, dim3(kThreads), 0, s, p);
+  timing_end(s);
   return hipGetLastError();
 }
 

@@ -389,11 +389,13 @@ hipError_t launch_fwd_tiled(const FwdParams& p, hipStream_t s) {
   a.remap = a.items % 8 == 0;
   const int rb = p.targets ? (p.r <= 32 ? 1 : 2) : 0;
   dim3 grid(a.items), block(kThreads);
+  timing_begin(s);
   switch (rb) {
     case 0: hipLaunchKernelGGL(fwd_tiled_kernel<0>, grid, block, 0, s, a); break;
     case 1: hipLaunchKernelGGL(fwd_tiled_kernel<1>, grid, block, 0, s, a); break;
     default: hipLaunchKernelGGL(fwd_tiled_kernel<2>, grid, block, 0, s, a); break;
   }
+  timing_end(s);
   return hipGetLastError();
 }
 

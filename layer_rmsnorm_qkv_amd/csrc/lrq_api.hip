@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <vector>
 
 #include "lrq.h"
 #include "lrq_internal.h"
@@ -19,6 +20,46 @@ size_t bwd_tiled_workspace_bytes(const FwdParams& p);
 hipError_t launch_fwd_tiled(const FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_decode(const FwdParams& p, hipStream_t s);
 hipError_t launch_bwd_tiled(const BwdParams& p, hipStream_t s);
+}  // namespace lrq
+
+namespace {
+
+// Measurement hook state (process-wide; the hook is meant for a single benchmarking thread).
+struct Timing {
+  bool on = false;
+  int kind = 0;                   // 0: the current call is a forward, 1: a backward
+  std::vector<hipEvent_t> ev[2];  // start, stop pairs; created on demand, kept until exit
+  size_t used[2] = {0, 0};        // pairs recorded since the hook was (re)enabled
+  bool open = false;              // a start was recorded and its stop is due
+};
+Timing g_timing;
+constexpr size_t kMaxTimedCalls = 4096;
+
+}  // namespace
+
+namespace lrq {
+
+void timing_begin(hipStream_t s) {
+  Timing& t = g_timing;
+  if (!t.on || t.used[t.kind] >= kMaxTimedCalls) return;
+  std::vector<hipEvent_t>& v = t.ev[t.kind];
+  const size_t u = t.used[t.kind];
+  while (v.size() < 2 * (u + 1)) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return;
+    v.push_back(e);
+  }
+  t.open = hipEventRecord(v[2 * u], s) == hipSuccess;
+}
+
+void timing_end(hipStream_t s) {
+  Timing& t = g_timing;
+  if (!t.on || !t.open) return;
+  t.open = false;
+  const size_t u = t.used[t.kind];
+  if (hipEventRecord(t.ev[t.kind][2 * u + 1], s) == hipSuccess) ++t.used[t.kind];
+}
+
 }  // namespace lrq
 
 namespace {
@@ -216,6 +257,7 @@ lrq_status lrq_forward(const lrq_desc* desc, const void* x, const void* gamma, c
   p.ws_bytes = workspace_bytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
+  g_timing.kind = 0;
   switch (v) {
     case LRQ_VARIANT_TILED: e = lrq::launch_fwd_tiled(p, s); break;
     case LRQ_VARIANT_DECODE: e = lrq::launch_fwd_decode(p, s); break;
@@ -261,11 +303,37 @@ lrq_status lrq_backward(const lrq_desc* desc, const void* x, const void* gamma, 
   bp.f.ws_bytes = workspace_bytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
+  g_timing.kind = 1;
   if (v == LRQ_VARIANT_TILED)
     e = lrq::launch_bwd_tiled(bp, s);
   else
     e = desc->dtype == LRQ_F32 ? lrq::launch_bwd_generic_f32(bp, s) : lrq::launch_bwd_generic_bf16(bp, s);
   return hip_status(e, "backward launch");
+}
+
+lrq_status lrq_kernel_timing(int enable) {
+  g_timing.on = enable != 0;
+  g_timing.used[0] = g_timing.used[1] = 0;
+  g_timing.open = false;
+  return ok();
+}
+
+lrq_status lrq_kernel_time_ms(int for_backward, double* mean_ms, int* count) {
+  if (!mean_ms || !count) return fail(LRQ_ERR_INVALID_ARG, "mean_ms and count are required");
+  const int k = for_backward ? 1 : 0;
+  const size_t n = g_timing.used[k];
+  double sum = 0.0;
+  for (size_t i = 0; i < n; ++i) {
+    hipEvent_t a = g_timing.ev[k][2 * i], b = g_timing.ev[k][2 * i + 1];
+    hipError_t e = hipEventSynchronize(b);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+    if (e != hipSuccess) return hip_status(e, "kernel timing");
+    sum += ms;
+  }
+  *mean_ms = n ? sum / static_cast<double>(n) : 0.0;
+  *count = static_cast<int>(n);
+  return ok();
 }
 
 }  // extern "C"

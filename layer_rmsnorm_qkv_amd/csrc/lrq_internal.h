@@ -51,6 +51,10 @@ __host__ __device__ inline void target_cols(const FwdParams& p, int t, int& lo, 
   hi = t == 0 ? p.col_k : (t == 1 ? p.col_v : p.N);
 }
 
+// ---- measurement hook: events around the dominant kernel of a call (lrq_api.hip) ----
+void timing_begin(hipStream_t s);
+void timing_end(hipStream_t s);
+
 // ---- launchers (defined in the kernel translation units) ----
 hipError_t launch_fwd_generic_f32(const FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_generic_bf16(const FwdParams& p, hipStream_t s);
