@@ -130,31 +130,41 @@ struct PrepArgs {
 };
 
 __global__ __launch_bounds__(256) void prep_weights_kernel(PrepArgs a) {
-  __shared__ uint16_t tile_s[64][65];
+  __shared__ uint16_t tile_s[64][72];  // 144-byte rows: 16-byte aligned, banks spread
   const int tid = threadIdx.x;
   if (static_cast<int>(blockIdx.x) < a.wt_blocks) {
-    // transpose a 64 x 64 block: source rows q (LoRA-extended K index) x columns j
+    // transpose a 64 x 64 block: source rows q (LoRA-extended K index) x columns j, moved as
+    // 16-byte vectors (8 columns of a source row in, 8 rows of a destination row out)
     const int jb = a.d / 64;
     const int kb = static_cast<int>(blockIdx.x) / jb, cb = static_cast<int>(blockIdx.x) % jb;
     const int q0 = kb * 64, j0 = cb * 64;
-    for (int e = tid; e < 64 * 64; e += 256) {
-      const int qi = e / 64, ji = e % 64;
-      const int q = q0 + qi, j = j0 + ji;
-      uint16_t v = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = tid + 256 * h;
+      const int qi = c >> 3, jc = (c & 7) * 8;
+      const int q = q0 + qi;
+      const uint16_t* src = nullptr;
       if (q < a.N) {
-        v = a.w[static_cast<int64_t>(q) * a.d + j];
+        src = a.w + static_cast<int64_t>(q) * a.d;
       } else if (q - a.N < a.R) {
-        const int c = q - a.N;
+        const int cq = q - a.N;
         for (int t = 0; t < 3; ++t)
-          if (((a.targets >> t) & 1u) && c >= a.off[t] && c < a.off[t] + a.r)
-            v = a.a[t][static_cast<int64_t>(c - a.off[t]) * a.d + j];
+          if (((a.targets >> t) & 1u) && cq >= a.off[t] && cq < a.off[t] + a.r)
+            src = a.a[t] + static_cast<int64_t>(cq - a.off[t]) * a.d;
       }
-      tile_s[qi][ji] = v;
+      const uint4 v = src ? *reinterpret_cast<const uint4*>(src + j0 + jc) : uint4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<uint4*>(&tile_s[qi][jc]) = v;
     }
     __syncthreads();
-    for (int e = tid; e < 64 * 64; e += 256) {
-      const int ji = e / 64, qi = e % 64;
-      a.wt[static_cast<int64_t>(j0 + ji) * a.K + q0 + qi] = tile_s[qi][ji];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = tid + 256 * h;
+      const int ji = c >> 3, qc = (c & 7) * 8;
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = static_cast<uint32_t>(tile_s[qc + 2 * e][ji]) | (static_cast<uint32_t>(tile_s[qc + 2 * e + 1][ji]) << 16);
+      *reinterpret_cast<uint4*>(a.wt + static_cast<int64_t>(j0 + ji) * a.K + q0 + qc) = uint4{w[0], w[1], w[2], w[3]};
     }
     return;
   }
