@@ -46,7 +46,7 @@ struct BwdLayout {
   int groups[4];  // work groups per LoRA-gradient job (dA, then each target's dB)
   int chunk;    // tokens per partial sum (multiple of 16)
   int chunks;   // token chunks of the LoRA-gradient partial sums
-  size_t wt, bt[3], ap[3], gcat, u, inv, m, pda, pdb[3], total;
+  size_t wt, bt[3], ap_all, ap[3], gcat, u, inv, m, pda, pdb[3], total;
 };
 
 size_t al256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
@@ -89,8 +89,10 @@ BwdLayout bwd_layout(const FwdParams& p) {
     target_cols(p, t, lo, hi);
     const bool on = p.targets & (1u << t);
     L.bt[t] = take(on ? static_cast<size_t>(p.r) * (hi - lo) * 2 : 0);
-    L.ap[t] = take(on ? static_cast<size_t>(p.r) * p.d * 2 : 0);
   }
+  // A'_t of all targets as one [R][d] block (target t at row off_t)
+  L.ap_all = take(static_cast<size_t>(R) * p.d * 2);
+  for (int t = 0; t < 3; ++t) L.ap[t] = L.ap_all + static_cast<size_t>(L.off[t]) * p.d * 2;
   L.gcat = take(static_cast<size_t>(p.T) * L.K * 2);
   L.u = take(static_cast<size_t>(p.T) * std::max(R, 1) * 2);
   L.inv = take(static_cast<size_t>(p.T) * 4);
@@ -278,6 +280,7 @@ struct RankJob {
   int64_t lda;
   const uint16_t* bs;  // small operand rows [r][nk * 64]
   int64_t ldb;
+  int r;               // rows of bs (at most 32 RB)
   int nk;              // K steps of 64
   uint16_t* out;
   int64_t ldo;
@@ -288,9 +291,8 @@ struct RankJob {
 };
 
 struct RankArgs {
-  RankJob job[6];
+  RankJob job[6];  // up to 3 V jobs and 3 U jobs
   int64_t T;
-  int r;
 };
 
 template <int RB>
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(kThreads, 1) void rank_kernel(RankArgs a) {
   const RankJob& j = a.job[blockIdx.y];
   const Src src = make_src(j.a, j.lda, row0, a.T, j.bs, j.ldb, wave, lane);
   floatx16 u[RB == 2 ? 4 : 2];
-  rankpass<RB>(smem, src, make_rank_src(j.bs, j.ldb, a.r, RB, wave, lane), j.nk, wave, lane, u);
+  rankpass<RB>(smem, src, make_rank_src(j.bs, j.ldb, j.r, RB, wave, lane), j.nk, wave, lane, u);
   const int k = rank_col<RB>(wn, l32);
 #pragma unroll
   for (int i = 0; i < (RB == 2 ? 4 : 2); ++i) {
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(kThreads, 1) void rank_kernel(RankArgs a) {
       const int64_t row = row0 + rank_row<RB>(i, v, wm, wn, h32);
       if (row >= a.T) continue;
       uint16_t* o = j.out + row * j.ldo + j.col0;
-      if (k < a.r) {
+      if (k < j.r) {
         const float f = j.inv ? j.inv[row] * j.scale : j.scale;
         o[k] = f32_to_bf16_bits(f * u[i][v]);
       } else if (j.col0 + k < j.pad_to) {
@@ -347,12 +349,12 @@ struct MainArgs {
   int remap;
 };
 
-__global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(MainArgs a) {
+__global__ __launch_bounds__(kThreads8, 1) void bwd_main_kernel(MainArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kRingBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave & 3, wn = wave >> 2;
   const int l32 = lane & 31, h32 = lane >> 5;
   int item = blockIdx.x;
   if (a.remap) item = (blockIdx.x & 7) * (a.items >> 3) + (blockIdx.x >> 3);
@@ -361,24 +363,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_main_kernel(MainArgs a) {
   const int64_t row0 = static_cast<int64_t>(mt) * BM;
   const int64_t col0 = static_cast<int64_t>(nt) * BN;
 
-  Acc ta;
+  Acc8 ta;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) ta.acc[i][j] = floatx16{};
-  const Src src = make_src(a.gcat, a.K, row0, a.T, a.wt, a.K, wave, lane);
-  kloop<false>(smem, ta, src, col0, static_cast<int>(a.K / BK), wave, lane);
+  const Src8 src = make_src8(a.gcat, a.K, row0, a.T, a.wt, a.K, wave, lane);
+  kloop8(smem, ta, src, col0, static_cast<int>(a.K / BK), wave, lane);
 
   // epilogue: dx = inv * gamma * dh - m * x for the lane's rows and columns
-  // (lane rows: 128 wm + 32 i + 8 (v / 4) + 4 h32 + v % 4; columns 128 wn + 32 j + l32)
+  // (lane rows: 64 wm + 32 i + 8 (v / 4) + 4 h32 + v % 4; columns 128 wn + 32 j + l32)
   float gam[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) gam[j] = bf16_bits_to_f32(a.gamma[col0 + wn * 128 + j * 32 + l32]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int64_t row = row0 + wm * 128 + i * 32 + (v >> 2) * 8 + h32 * 4 + (v & 3);
+      const int64_t row = row0 + wm * 64 + i * 32 + (v >> 2) * 8 + h32 * 4 + (v & 3);
       if (row >= a.T) continue;
       const float inv = a.inv[row], mm = a.m[row];
       const uint16_t* xr = a.x + row * a.d + col0 + wn * 128 + l32;
@@ -719,10 +721,11 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
     hipLaunchKernelGGL(rows_kernel, dim3(static_cast<unsigned>((p.T + 3) / 4)), dim3(256), 0, s, ra);
 
     if (lora) {
-      // ---- V' = bf16(s G_t B_t) into Gcat's LoRA columns; U_t = bf16(inv x A'_t^T)
+      // ---- V' = bf16(s G_t B_t) into Gcat's LoRA columns; U = bf16(inv x A'^T) for the R
+      // rows of all targets' A' at once (x is read once per 32 RB of them)
       RankArgs ra2{};
       ra2.T = p.T;
-      ra2.r = p.r;
+      const int rb = p.r <= 32 ? 1 : 2;
       int nj = 0, last_t = -1;
       for (int t = 0; t < 3; ++t)
         if (p.targets & (1u << t)) last_t = t;
@@ -733,6 +736,7 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
         vj.lda = L.K;
         vj.bs = at<uint16_t>(ws, L.bt[t]);
         vj.ldb = nt[t];
+        vj.r = p.r;
         vj.nk = nt[t] / BK;
         vj.out = at<uint16_t>(ws, L.gcat);
         vj.ldo = L.K;
@@ -740,21 +744,24 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
         vj.pad_to = t == last_t ? static_cast<int>(L.K) : vj.col0 + p.r;
         vj.scale = p.scale;
         vj.inv = nullptr;
+      }
+      for (int c0 = 0; c0 < L.R; c0 += 32 * rb) {
         RankJob& uj = ra2.job[nj++];
         uj.a = static_cast<const uint16_t*>(p.x);
         uj.lda = p.d;
-        uj.bs = at<uint16_t>(ws, L.ap[t]);
+        uj.bs = at<uint16_t>(ws, L.ap_all) + static_cast<int64_t>(c0) * p.d;
         uj.ldb = p.d;
+        uj.r = std::min(32 * rb, L.R - c0);
         uj.nk = static_cast<int>(p.d / BK);
         uj.out = at<uint16_t>(ws, L.u);
         uj.ldo = L.R;
-        uj.col0 = L.off[t];
-        uj.pad_to = uj.col0 + p.r;
+        uj.col0 = c0;
+        uj.pad_to = c0 + uj.r;
         uj.scale = 1.0f;
         uj.inv = at<float>(ws, L.inv);
       }
       const dim3 grid(static_cast<unsigned>((p.T + BM - 1) / BM), nj);
-      if (p.r <= 32)
+      if (rb == 1)
         hipLaunchKernelGGL(rank_kernel<1>, grid, dim3(kThreads), 0, s, ra2);
       else
         hipLaunchKernelGGL(rank_kernel<2>, grid, dim3(kThreads), 0, s, ra2);
@@ -778,7 +785,7 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
     ma.remap = ma.items % 8 == 0;
     (void)cu_count_bwd;
     timing_begin(s);
-    hipLaunchKernelGGL(bwd_main_kernel, dim3(ma.items), dim3(kThreads), 0, s, ma);
+    hipLaunchKernelGGL(bwd_main_kernel, dim3(ma.items), dim3(kThreads8), 0, s, ma);
     timing_end(s);
 
     if (lora) {

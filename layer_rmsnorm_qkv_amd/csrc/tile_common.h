@@ -10,6 +10,12 @@
 //     whole 128-byte line.  Each lane picks its global source so that the 16-byte chunks
 //     land XOR-swizzled by row (conflict-free ds_read_b128).
 //   * Stage map: A half at [0, 64 KB), B half at [64 KB, 128 KB).
+//   * kloop8 / Acc8: the same product with 512 threads = 8 wavefronts, two per SIMD.
+//     Wavefront w owns rows 64 (w % 4) .. +64 and columns 128 (w / 4) .. +128 of the tile:
+//     2 x 4 accumulators (128 fp32 per lane).  The two groups of four wavefronts (w / 4 =
+//     0, 1) take turns: while one group issues the MFMAs of a step, the other reads its
+//     fragments of the next step from LDS and issues the ring's DMA, and the two swap at a
+//     workgroup barrier; the MFMA phase runs at raised wave priority.
 #pragma once
 
 #include "lrq_internal.h"
@@ -287,6 +293,131 @@ __device__ __forceinline__ void kloop(unsigned char* smem, Acc& ta, const Src& s
   for (int i = 0; i < 4; ++i) mfma_row(ta, fb, i);
   if (STATS) slice_stats(ta, fb);
   sched_fence();
+  barrier_all();  // every wave is done with the stage ring
+}
+
+// ------------------------------------------------------------------ 8-wavefront products
+constexpr int kThreads8 = 512;
+
+// Per-wave accumulators of one tile: rows 64 wm + 32 i + (lane layout), columns
+// 128 wn + 32 j + l32.
+struct Acc8 {
+  floatx16 acc[2][4];
+};
+
+// Per-lane DMA sources of the 8-wavefront pipeline.  Instruction c (0..3) of wave w fills
+// rows R = 32 w + 8 c + lane / 8 of the A and the B half of a stage (logical chunk
+// (lane % 8) ^ chunk_xor(R) lands in physical chunk lane % 8).
+struct Src8 {
+  const uint16_t* a[4];  // A rows; rows past the panel's end re-read its last row
+  const uint16_t* b[4];  // B rows of column tile 0
+  int64_t ldb;
+};
+
+__device__ __forceinline__ Src8 make_src8(const uint16_t* A, int64_t lda, int64_t row0, int64_t rows_valid,
+                                          const uint16_t* B, int64_t ldb, int wave, int lane) {
+  Src8 s;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int R = 32 * wave + 8 * c + (lane >> 3);
+    const int lc = (lane & 7) ^ chunk_xor(R);
+    s.a[c] = A + min(row0 + R, rows_valid - 1) * lda + lc * 8;
+    s.b[c] = B + static_cast<int64_t>(R) * ldb + lc * 8;
+  }
+  s.ldb = ldb;
+  return s;
+}
+
+// workgroup barrier that the compiler's scheduler does not move instructions across
+__device__ __forceinline__ void fenced_barrier() {
+  sched_fence();
+  __builtin_amdgcn_s_barrier();
+  sched_fence();
+}
+
+// kloop with 8 wavefronts: acc = A_panel B_tile^T, B_tile = B rows [col0, col0 + 256).
+// Called by all 8 wavefronts; leaves the stage ring free.
+//
+// Step ks is two intervals between workgroup barriers.  Group 0 reads the fragments of
+// stage ks (all four 16-wide slices) in interval 2 ks and multiplies in 2 ks + 1; group 1
+// is one interval behind.  The DMA of stage ks + 1 goes out in interval 2 ks (group 0 at
+// the start of its read phase, group 1 at the start of its MFMA phase for step ks - 1),
+// into the buffer of stage ks - 1, which both groups finished reading in interval 2 ks - 1;
+// every wave waits for its own part of stage ks + 1 at the end of interval 2 ks + 1, so
+// the stage is complete when group 0 reads it in interval 2 ks + 2.
+__device__ __forceinline__ void kloop8(unsigned char* smem, Acc8& ta, const Src8& src, int64_t col0, int nk, int wave,
+                                      int lane) {
+  const int g = wave >> 2;
+  const int wm = wave & 3, wn = g;
+  const int l32 = lane & 31, h32 = lane >> 5;
+  const uint32_t sbase = lds_addr(smem);
+  const int64_t boff = col0 * src.ldb;
+
+  auto issue = [&](int ks) {
+    const uint32_t xa = sbase + kStageA + (ks & 1) * kTileBytes + wave * 4096;
+    const uint32_t xb = sbase + kStageB + (ks & 1) * kTileBytes + wave * 4096;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      dma16(src.a[c] + ks * BK, xa + c * 1024);
+      dma16(src.b[c] + boff + ks * BK, xb + c * 1024);
+    }
+  };
+  bf16x8 fa[kSlices][2], fb[kSlices][4];
+  auto read = [&](int ks) {
+    const unsigned char* xs = smem + kStageA + (ks & 1) * kTileBytes;
+    const unsigned char* ws = smem + kStageB + (ks & 1) * kTileBytes;
+#pragma unroll
+    for (int s = 0; s < kSlices; ++s) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        fa[s][i] = *reinterpret_cast<const bf16x8*>(xs + swz(wm * 64 + i * 32 + l32, s * 2 + h32));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        fb[s][j] = *reinterpret_cast<const bf16x8*>(ws + swz(wn * 128 + j * 32 + l32, s * 2 + h32));
+    }
+  };
+  auto multiply = [&]() {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int s = 0; s < kSlices; ++s) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          ta.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], ta.acc[i][j], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // s_waitcnt encodings: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8
+  constexpr int kLgkm0 = 15 | (3 << 14) | (7 << 4) | (0 << 8);
+  constexpr int kVm0Lgkm0 = 0 | (0 << 14) | (7 << 4) | (0 << 8);
+  constexpr int kVm0 = 0 | (0 << 14) | (7 << 4) | (15 << 8);
+
+  issue(0);
+  wait_barrier<0>();
+  if (g == 1) {
+    if (nk > 1) issue(1);
+    fenced_barrier();
+  }
+  for (int ks = 0; ks < nk; ++ks) {
+    sched_fence();
+    if (g == 0 && ks + 1 < nk) issue(ks + 1);
+    sched_fence();
+    read(ks);
+    sched_fence();
+    if (g == 1)
+      __builtin_amdgcn_s_waitcnt(kVm0Lgkm0);
+    else
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+    fenced_barrier();
+    if (g == 1 && ks + 2 < nk) issue(ks + 2);
+    sched_fence();
+    multiply();
+    sched_fence();
+    if (g == 0) __builtin_amdgcn_s_waitcnt(kVm0);
+    fenced_barrier();
+  }
+  if (g == 0) fenced_barrier();
   barrier_all();  // every wave is done with the stage ring
 }
 
