@@ -147,3 +147,18 @@ def test_backward_checks():
 def test_workspace_queries():
     assert B.lrq_workspace_size(good_desc()) == 0  # the generic family needs none
     assert B.lrq_workspace_size(good_desc(), True) == 0
+
+
+def test_timing_hook_without_calls():
+    """The measurement hook: enabling it clears the record, nothing recorded reads as 0 calls,
+    and NULL outputs are rejected."""
+    B.lrq_kernel_timing(True)
+    assert B.lrq_kernel_time_ms(False) == (0.0, 0)
+    assert B.lrq_kernel_time_ms(True) == (0.0, 0)
+    lib = B.load()
+    n = ctypes.c_int(-1)
+    assert lib.lrq_kernel_time_ms(0, None, ctypes.byref(n)) == B.LRQ_ERR_INVALID_ARG
+    ms = ctypes.c_double(-1.0)
+    assert lib.lrq_kernel_time_ms(1, ctypes.byref(ms), None) == B.LRQ_ERR_INVALID_ARG
+    B.lrq_kernel_timing(False)
+    assert B.lrq_kernel_time_ms(False) == (0.0, 0)

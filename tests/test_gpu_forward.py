@@ -157,3 +157,31 @@ def test_zero_tokens_launches_nothing():
     B.lrq_forward(d0, prob.x, prob.gamma, prob.w_qkv, prob.bias, prob.a, prob.b, prob.positions, empty,
                   prob.workspace)
     torch.cuda.synchronize()
+
+
+def test_timing_hook_counts_calls():
+    """The measurement hook records one interval per call while enabled (forward and
+    backward separately), none while disabled, and its mean lies within the whole call's."""
+    import torch
+    w = SMALL_BF16["l3_t70"]
+    inp = wl.make_inputs(w, with_dy=True)
+    prob = DeviceProblem(w, inp, variant=B.LRQ_VARIANT_TILED, backward=True)
+    log("[gpu] timing hook")
+    prob.forward()
+    torch.cuda.synchronize()
+    B.lrq_kernel_timing(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        prob.forward()
+    e1.record()
+    prob.backward()
+    torch.cuda.synchronize()
+    ms_f, n_f = B.lrq_kernel_time_ms(False)
+    ms_b, n_b = B.lrq_kernel_time_ms(True)
+    assert (n_f, n_b) == (3, 1)
+    assert 0.0 < ms_f <= e0.elapsed_time(e1) / 3 * 1.5 and ms_b > 0.0
+    B.lrq_kernel_timing(False)
+    prob.forward()
+    torch.cuda.synchronize()
+    assert B.lrq_kernel_time_ms(False) == (0.0, 0)
