@@ -69,9 +69,7 @@ def algorithmic_work(w, T=None):
 def dominant_kernel_work(w, family: str, backward: bool):
     """Algorithmic work of one launch of a call's dominant kernel: (amount, unit kind).
 
-    Forward, tiled: every matmul FLOP of the forward, less the LoRA down projection when a
-    kernel of its own computes it before the tile kernel (ranks up to 32).  Forward, generic:
-    every matmul FLOP of the forward.  Forward, decode: the bytes
+    Forward, tiled or generic: every matmul FLOP of the forward.  Forward, decode: the bytes
     the streaming kernel must move (x, gamma, W, bias, the targets' A, positions, and the
     outputs of columns without an adapter; the LoRA-up pass writes the rest).  Backward,
     tiled: dh = G W + sum_t V'_t A_t, 2 T d (N + sum of ranks) FLOPs.  Backward, generic:
@@ -87,8 +85,6 @@ def dominant_kernel_work(w, family: str, backward: bool):
         unadapted = sum(hi - lo for t, (lo, hi) in cols.items() if not (w.lora_targets & t))
         nbytes = eb * (T * d + d + N * d + (N if w.has_bias else 0) + ranks * d + T * unadapted) + 4 * T
         return nbytes, "bytes"
-    if family == "tiled" and 0 < r <= 32:
-        return f_fwd - 2.0 * T * d * ranks, "flop"
     return f_fwd, "flop"
 
 

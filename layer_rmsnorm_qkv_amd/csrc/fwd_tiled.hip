@@ -7,9 +7,7 @@
 // (one bandwidth-bound pass per call, W' = bf16(W * gamma) into the workspace), and the row
 // scale inv commutes with both products, so it is applied to the fp32 accumulators in the
 // epilogue.  x enters the MFMAs exactly as given; sum(x^2) of the rows is gathered from the
-// same LDS tiles, so h is never formed.  For ranks up to 32 the LoRA down projection
-// bf16(s U) = bf16(s x A'^T) of all tokens and targets is one small product before the tile
-// kernel (T x R values in the workspace); above that it is a K pass inside the tile kernel.
+// same LDS tiles.  Neither h nor U = A h is written to memory.
 //
 // Work decomposition (gfx950: 64-wide wavefronts, 160 KB LDS, one workgroup per CU)
 //   * Output tile 256 tokens x 256 columns (two heads), 256 threads = 4 wavefronts, one
@@ -20,11 +18,10 @@
 //   * K-loop: the shared tile pipeline (tile_common.h) with A = x and B = W': 64-wide steps
 //     over d through a two-stage direct-to-LDS ring, one barrier per step.
 //   * One workgroup processes one token tile against a run of consecutive column tiles.
-//     Before the first tile of the run that needs target t's adapter, the tile's rows of
-//     bf16(s U_t) are copied into LDS (or, for ranks above 32, computed by a K pass over the
-//     x tile and A'_t's rows) and kept for the rest of the run; the rank-r up projection is
-//     an extra K segment of MFMAs (K = r rounded up to 16) before the epilogue of every tile
-//     of that target.
+//     Before the first tile of the run that needs target t's adapter, a short K pass over
+//     the x tile and the rows of A'_t computes U_t = x A'_t^T and keeps bf16(s U_t) in LDS
+//     for the rest of the run; the rank-r up projection is an extra K segment of MFMAs
+//     (K = r rounded up to 16) before the epilogue of every tile of that target.
 //   * Workgroup ids are remapped so that the runs of one token tile share an XCD (and its
 //     L2) when the grid is a multiple of the XCD count.
 //   * Epilogue: row sums of squares -> inv, bias, RoPE on q and k heads (angle pos * omega_i
@@ -55,10 +52,7 @@ struct Lay {
 struct TiledArgs {
   const uint16_t* x;
   const uint16_t* wg;     // W' = bf16(W * gamma) [N][d] (workspace)
-  const uint16_t* ag[3];  // A'_t = bf16(A_t * gamma) [r][d] (workspace; ranks above 32)
-  const uint16_t* us;     // bf16(s U) [T][R] of all targets (workspace, lora_down_kernel)
-  int R;                  // columns of us
-  int uoff[3];            // first column of target t in us
+  const uint16_t* ag[3];  // A'_t = bf16(A_t * gamma) [r][d] (workspace)
   const uint16_t* bias;  // nullptr without bias
   const uint16_t* b[3];
   const int32_t* pos;
@@ -165,24 +159,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiled_kernel(TiledArgs p) {
     const bool need_u = lora && u_target != t;
     const int64_t col0 = static_cast<int64_t>(nt) * BN;
 
-    if (RB == 1 && need_u) {
-      // bf16(s U_t) of the token tile's rows from the down-projection kernel into LDS (ranks
-      // >= r and rows >= T as 0); the barrier first lets the previous tile's up projection
-      // finish reading s_u
-      barrier_all();
-      const uint16_t* ut = p.us + p.uoff[t];
-      for (int e = tid; e < BM * L::kUStride; e += kThreads) {
-        const int row = e / L::kUStride, k = e - row * L::kUStride;
-        const int64_t gr = row0 + row;
-        s_u[e] = (k < p.r && gr < T) ? ut[gr * p.R + k] : uint16_t{0};
-      }
-      barrier_all();
-      u_target = t;
-    }
-    if (RB == 2 && need_u) {
-      // ranks above 32: U_t = x A'_t^T for the token tile as a K pass here (the
-      // down-projection kernel's A' reads per workgroup grow with the rank); bf16(s U) is
-      // kept for the rest of the run (ranks >= r re-read A'_t row r - 1 and are stored as 0)
+    if (RB > 0 && need_u) {
+      // U_t = x A'_t^T for the token tile; bf16(s U) kept for the rest of the run (ranks >= r
+      // re-read A'_t row r - 1 and are stored as 0)
       floatx16 u[RB == 2 ? 4 : 2];
       rankpass<RB>(smem, src, make_rank_src(p.ag[t], d, p.r, RB, wave, lane), nk, wave, lane, u);
 #pragma unroll
@@ -196,7 +175,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiled_kernel(TiledArgs p) {
       barrier_all();
       u_target = t;
     }
-
 
     Acc ta;
 #pragma unroll
@@ -285,76 +263,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiled_kernel(TiledArgs p) {
   }
 }
 
-// LoRA down projection for the whole call, before the tile kernel (ranks up to 32):
-//   us[t][c] = bf16(s * sum_j x[t][j] A'[c][j])
-// for the R stacked rows c of the targets' A' (in the workspace right after W').  One
-// workgroup per 32 tokens; each wavefront takes a quarter of the 64-wide K steps of d and
-// multiplies the tokens' rows by every rank block of 32 (fragments straight from global
-// memory, MFMA 32x32x16), and the four fp32 partial products are added in wave order.
-// x is read once per call here instead of once per tile run inside the tile kernel.
-struct DownArgs {
-  const uint16_t* x;
-  const uint16_t* ag;  // [R][d]
-  uint16_t* us;        // [T][R]
-  int64_t T;
-  int d, R;
-  float scale;
-};
-
-template <int NB>
-__global__ __launch_bounds__(256) void lora_down_kernel(DownArgs a) {
-  __shared__ float red[3][NB][16][64];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int l32 = lane & 31, h32 = lane >> 5;
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * 32;
-  const int64_t d = a.d;
-  // lane l feeds row l % 32 of the token block and of each rank block; in K step ks, slice j
-  // (16 wide) is the lane's 8 values at ks * 64 + 16 j + 8 h32
-  const uint16_t* xr = a.x + min(row0 + l32, a.T - 1) * d + 8 * h32;
-  const uint16_t* ar[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) ar[b] = a.ag + static_cast<int64_t>(min(32 * b + l32, a.R - 1)) * d + 8 * h32;
-  floatx16 acc[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = floatx16{};
-  const int nk = a.d / 64;
-  const int per = (nk + 3) / 4;
-  const int k0 = wave * per, k1 = min(nk, k0 + per);
-  for (int ks = k0; ks < k1; ++ks) {
-    bf16x8 xf[4], af[NB][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) xf[j] = *reinterpret_cast<const bf16x8*>(xr + ks * 64 + 16 * j);
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) af[b][j] = *reinterpret_cast<const bf16x8*>(ar[b] + ks * 64 + 16 * j);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int b = 0; b < NB; ++b) acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[j], af[b][j], acc[b], 0, 0, 0);
-  }
-  if (wave > 0) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) red[wave - 1][b][v][lane] = acc[b][v];
-  }
-  __syncthreads();
-  if (wave > 0) return;
-  // lane holds rank 32 b + l32 of token rows (v / 4) * 8 + 4 h32 + v % 4
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int c = 32 * b + l32;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float sum = ((acc[b][v] + red[0][b][v][lane]) + red[1][b][v][lane]) + red[2][b][v][lane];
-      const int64_t row = row0 + (v >> 2) * 8 + 4 * h32 + (v & 3);
-      if (row < a.T && c < a.R) a.us[row * a.R + c] = f32_to_bf16_bits(a.scale * sum);
-    }
-  }
-}
-
 // W' = bf16(W * gamma) and A'_t = bf16(A_t * gamma): rows [0, N) of the destination
 // come from W, then r rows per target from A_q, A_k, A_v (targets only).  Each thread
 // scales 8 consecutive elements of one row (d % 8 == 0).
@@ -421,11 +329,9 @@ int n_targets(const FwdParams& p) { return (p.targets & 1u) + ((p.targets >> 1) 
 size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 }  // namespace
 
-// W' then A'_t for every target, bf16, d elements per row; then bf16(s U) [T][R] (filled for
-// ranks up to 32).
+// W' then A'_t for every target, bf16, d elements per row.
 size_t tiled_workspace_bytes(const FwdParams& p) {
-  const size_t R = static_cast<size_t>(n_targets(p)) * p.r;
-  return align256((p.N + R) * static_cast<size_t>(p.d) * 2) + align256(static_cast<size_t>(p.T) * R * 2);
+  return align256(static_cast<size_t>(p.N + n_targets(p) * p.r) * static_cast<size_t>(p.d) * 2);
 }
 
 hipError_t launch_fwd_tiled(const FwdParams& p, hipStream_t s) {
@@ -442,11 +348,9 @@ hipError_t launch_fwd_tiled(const FwdParams& p, hipStream_t s) {
   for (int t = 0; t < 3; ++t) {
     f.a[t] = static_cast<const uint16_t*>(p.a[t]);
     f.slot_t[t] = 0;
-    a.uoff[t] = 0;
     a.ag[t] = nullptr;
     a.b[t] = static_cast<const uint16_t*>(p.b[t]);
     if (p.targets & (1u << t)) {
-      a.uoff[t] = slots * p.r;
       a.ag[t] = ws + (static_cast<int64_t>(p.N) + static_cast<int64_t>(slots) * p.r) * p.d;
       f.slot_t[slots++] = t;
     }
@@ -455,26 +359,6 @@ hipError_t launch_fwd_tiled(const FwdParams& p, hipStream_t s) {
   const int64_t chunks = f.rows * (p.d / 8);
   const int fold_blocks = static_cast<int>(std::min<int64_t>((chunks + 255) / 256, 8 * 1024));
   hipLaunchKernelGGL(fold_gamma_kernel, dim3(fold_blocks), dim3(256), 0, s, f);
-
-  a.R = slots * p.r;
-  a.us = ws + align256(static_cast<size_t>(f.rows) * static_cast<size_t>(p.d) * 2) / 2;
-  const int rb = p.targets ? (p.r <= 32 ? 1 : 2) : 0;
-  if (rb == 1) {
-    DownArgs da;
-    da.x = static_cast<const uint16_t*>(p.x);
-    da.ag = ws + static_cast<int64_t>(p.N) * p.d;
-    da.us = const_cast<uint16_t*>(a.us);
-    da.T = p.T;
-    da.d = static_cast<int>(p.d);
-    da.R = a.R;
-    da.scale = p.scale;
-    const dim3 dgrid(static_cast<unsigned>((p.T + 31) / 32));
-    switch ((a.R + 31) / 32) {  // R <= 3 * 32
-      case 1: hipLaunchKernelGGL(lora_down_kernel<1>, dgrid, dim3(256), 0, s, da); break;
-      case 2: hipLaunchKernelGGL(lora_down_kernel<2>, dgrid, dim3(256), 0, s, da); break;
-      default: hipLaunchKernelGGL(lora_down_kernel<3>, dgrid, dim3(256), 0, s, da); break;
-    }
-  }
 
   a.x = static_cast<const uint16_t*>(p.x);
   a.wg = ws;
@@ -503,6 +387,7 @@ hipError_t launch_fwd_tiled(const FwdParams& p, hipStream_t s) {
   a.runs_per_m = (a.n_nt + run - 1) / run;
   a.items = n_mt * a.runs_per_m;
   a.remap = a.items % 8 == 0;
+  const int rb = p.targets ? (p.r <= 32 ? 1 : 2) : 0;
   dim3 grid(a.items), block(kThreads);
   timing_begin(s);
   switch (rb) {
