@@ -91,3 +91,21 @@ def test_backward_zero_tokens_zeroes_lora_grads():
     for t in prob.da + prob.db:
         if t is not None:
             assert torch.count_nonzero(t).item() == 0
+
+
+LIMITS = {
+    # the largest rank on every target with d = 8192 (a 130-step main product) and a ragged tile
+    "bf16_d8192_r64_allt": TRAIN.replace(n_tokens=300, d_model=8192, n_q_heads=4, n_kv_heads=2, lora_rank=64,
+                                         lora_targets=TQ | TK | TV),
+    # the generic family's largest head (256), float32
+    "f32_head256_r64": TINY.replace(n_tokens=12, d_model=64, head_dim=256, n_q_heads=2, n_kv_heads=1,
+                                    lora_rank=64, lora_targets=TQ | TK | TV),
+}
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("name", list(LIMITS))
+def test_backward_at_size_limits(name, variant):
+    w = LIMITS[name]
+    errs = run_backward(w, VARIANTS[variant])
+    assert max(errs.values()) <= TOL[w.dtype], errs

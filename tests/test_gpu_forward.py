@@ -185,3 +185,32 @@ def test_timing_hook_counts_calls():
     prob.forward()
     torch.cuda.synchronize()
     assert B.lrq_kernel_time_ms(False) == (0.0, 0)
+
+
+LIMITS = {
+    # the decode family's largest shape (d = 8192, 256 rows) at the largest rank on every target
+    "dec_max_d_rows_rank": DEC.replace(n_tokens=256, d_model=8192, n_q_heads=8, n_kv_heads=8, lora_rank=64,
+                                       lora_targets=TQ | TK | TV),
+    # a long K loop (128 steps of 64) with a ragged token tile in the tiled family
+    "l3_d8192_t300": L3.replace(n_tokens=300, d_model=8192, n_q_heads=4, n_kv_heads=2, lora_rank=32),
+}
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("name", list(LIMITS))
+def test_forward_at_size_limits(name, variant):
+    w = LIMITS[name]
+    got, ref, _ = run_case(w, VARIANTS[variant])
+    errs = forward_errors(w, got, ref)
+    log(f"  errors {errs}")
+    assert max(errs.values()) <= TOL["bf16"], errs
+
+
+def test_forward_f32_largest_head():
+    """The generic family's largest head (256) at the largest rank, float32."""
+    w = TINY.replace(n_tokens=20, d_model=64, head_dim=256, n_q_heads=2, n_kv_heads=1, lora_rank=64,
+                     lora_targets=TQ | TK | TV)
+    got, ref, _ = run_case(w, B.LRQ_VARIANT_GENERIC)
+    errs = forward_errors(w, got, ref)
+    log(f"  errors {errs}")
+    assert max(errs.values()) <= TOL["f32"], errs
