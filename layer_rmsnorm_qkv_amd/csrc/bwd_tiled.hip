@@ -647,13 +647,6 @@ __global__ __launch_bounds__(256) void lora_reduce_kernel(ReduceArgs a) {
   }
 }
 
-int cu_count_bwd() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
-  return n;
-}
-
 }  // namespace
 
 bool bwd_tiled_supports(const FwdParams& p) {
@@ -783,7 +776,6 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
     const int n_mt = static_cast<int>((p.T + BM - 1) / BM);
     ma.items = n_mt * ma.n_nt;
     ma.remap = ma.items % 8 == 0;
-    (void)cu_count_bwd;
     timing_begin(s);
     hipLaunchKernelGGL(bwd_main_kernel, dim3(ma.items), dim3(kThreads8), 0, s, ma);
     timing_end(s);

@@ -109,3 +109,41 @@ def test_backward_at_size_limits(name, variant):
     w = LIMITS[name]
     errs = run_backward(w, VARIANTS[variant])
     assert max(errs.values()) <= TOL[w.dtype], errs
+
+
+def test_forward_and_backward_replay_in_a_hip_graph():
+    """A forward and a backward call captured in one HIP graph (the calls allocate nothing,
+    clear nothing with memset and never synchronise) replay to the eager results, with eager
+    calls and synchronisations between the replays."""
+    import torch
+    w = CASES["bf16_gqa_t513_r24"]
+    inp = wl.make_inputs(w, with_dy=True)
+    if B.lrq_select_variant(desc_for(w, variant=B.LRQ_VARIANT_TILED), True) < 0:
+        pytest.skip("tiled family does not cover this shape")
+    log("[gpu] graph capture and replay (tiled forward + backward)")
+    prob = DeviceProblem(w, inp, variant=B.LRQ_VARIANT_TILED, backward=True)
+    y = prob.forward().clone()
+    dx, da, db = prob.backward(y=y)
+    ref = [dx.clone()] + [t.clone() for t in da + db if t is not None]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        prob.forward()
+        prob.backward(y=y)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        prob.forward()
+        prob.backward(y=y)
+    for _ in range(3):
+        prob.out.zero_()
+        prob.dx.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [prob.dx] + [t for t in prob.da + prob.db if t is not None]
+        assert torch.equal(prob.out, y)
+        assert all(torch.equal(g, r) for g, r in zip(got, ref))
+        prob.forward()
+        torch.cuda.synchronize()

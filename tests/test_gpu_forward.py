@@ -214,3 +214,33 @@ def test_forward_f32_largest_head():
     errs = forward_errors(w, got, ref)
     log(f"  errors {errs}")
     assert max(errs.values()) <= TOL["f32"], errs
+
+
+@pytest.mark.parametrize("variant", ["tiled", "decode"])
+def test_forward_replays_in_a_hip_graph(variant):
+    """Forward calls captured in a HIP graph replay to the eager result, with eager calls and
+    synchronisations between the replays (a decode step is the launch-bound case)."""
+    import torch
+    w = SMALL_BF16["dec_t200_gqa_r24"]
+    if B.lrq_select_variant(desc_for(w, variant=VARIANTS[variant])) < 0:
+        pytest.skip("variant does not cover this shape")
+    log(f"[gpu] graph capture and replay variant={variant}")
+    prob = DeviceProblem(w, wl.make_inputs(w), variant=VARIANTS[variant])
+    eager = prob.forward().clone()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        prob.forward()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        prob.forward()
+    for _ in range(3):
+        prob.out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(prob.out, eager)
+        prob.forward()
+        torch.cuda.synchronize()
