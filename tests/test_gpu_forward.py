@@ -244,3 +244,21 @@ def test_forward_replays_in_a_hip_graph(variant):
         assert torch.equal(prob.out, eager)
         prob.forward()
         torch.cuda.synchronize()
+
+
+def test_forward_output_past_2_31_elements():
+    """T x N above 2^31 output elements (360448 tokens x 6144 columns, d = 512): every row and
+    column offset must be formed in 64 bits.  Checked on sampled rows, including the last."""
+    import torch
+    w = L3.replace(n_tokens=360448, d_model=512, lora_rank=16)
+    assert w.n_tokens * w.n_out > 2 ** 31
+    log(f"[gpu] forward T={w.n_tokens} N={w.n_out} (T*N = {w.n_tokens * w.n_out}); generating inputs")
+    inp = wl.make_inputs(w)
+    prob = DeviceProblem(w, inp, variant=B.LRQ_VARIANT_TILED)
+    rows = sample_rows(w.n_tokens, 128, seed=11)
+    out = prob.forward()
+    got = to_np(out[torch.as_tensor(rows, device=out.device)])
+    torch.cuda.synchronize()
+    errs = forward_errors(w, got, oracle_forward(w, inp, rows))
+    log(f"  errors {errs}")
+    assert max(errs.values()) <= TOL["bf16"], errs
