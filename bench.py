@@ -217,8 +217,8 @@ def copy_probe(nbytes: int, reps: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30, help="untimed steps first (the clocks settle within about 20 steps of sustained MFMA load)")
     ap.add_argument("--workload", default="llama3", choices=["tiny", "llama3", "llama2", "decode", "train"])
     ap.add_argument("--variant", default="auto", choices=["auto", "generic", "tiled", "decode"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
