@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define LRQ_ABI_VERSION 1
+#define LRQ_ABI_VERSION 2
 #define LRQ_MAX_LORA_RANK 64
 
 typedef enum lrq_status {
@@ -124,6 +124,39 @@ lrq_status lrq_forward(const lrq_desc* desc, const void* x, const void* gamma, c
                        const void* bias, const void* const* lora_a, const void* const* lora_b,
                        const int32_t* positions, void* out, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* Destination of a forward call's keys and values in a key/value cache.  The rotated k and
+ * the (unrotated) v that the projection produces are what the attention step after it reads:
+ * "Liger-Kernel底层优化：新一代内核级推理加速引擎深度解析" shows the decoder layer's op
+ * sequence (normalise, project to q, k, v, rotate, attention), lists a fused attention
+ * kernel with KV-cache handling next to the fused norm/QKV/RoPE kernel, and mentions paged
+ * KV-cache management in serving engines.  The pages define no cache layout, so this one is
+ * the library's: one row per cached token, which covers a contiguous cache (slot = position)
+ * and a paged one flattened to [num_blocks * block_size] rows (slot = the caller's mapping
+ * of the token's page and offset).
+ *   k_cache, v_cache  [num_slots, Hkv * D]  dtype of the call, 16-byte aligned
+ *   slots             [T] int32             cache row of token t
+ * Tokens with slots[t] < 0 or >= num_slots are not written (padding).  Two tokens with the
+ * same valid slot: which one's row lands is unspecified.  Rows that no token names are left
+ * as they were.  The caches are owned by the caller, like every other buffer. */
+typedef struct {
+  void* k_cache;
+  void* v_cache;
+  const int32_t* slots;
+  int64_t num_slots;  /* >= 0; 0 writes nothing */
+} lrq_kv_cache;
+
+/* lrq_forward, and in the same call k_cache[slots[t]] = out[t, Hq*D : (Hq+Hkv)*D] and
+ * v_cache[slots[t]] = out[t, (Hq+Hkv)*D : N], bit for bit the values written to out.  The
+ * decode family stores the cache rows from the same epilogues that store out; the other
+ * families copy them from out in one more pass on the stream.  kv == NULL behaves as
+ * lrq_forward.  Same INVALID_ARG rules as lrq_forward, plus num_slots < 0, or k_cache,
+ * v_cache or slots NULL (T > 0); UNSUPPORTED for a cache or slots pointer that is not
+ * 16-byte aligned. */
+lrq_status lrq_forward_kv(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,
+                          const void* bias, const void* const* lora_a, const void* const* lora_b,
+                          const int32_t* positions, void* out, const lrq_kv_cache* kv, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /* Backward of the forward above with W, gamma and bias frozen.  Given dy = dL/d(out),
  * writes dx = dL/dx (dtype) and, for every target t, d_lora_a[t] = dL/dA_t and

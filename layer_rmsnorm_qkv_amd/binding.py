@@ -21,7 +21,7 @@ LRQ_VARIANT_AUTO, LRQ_VARIANT_GENERIC, LRQ_VARIANT_TILED, LRQ_VARIANT_DECODE = 0
 VARIANT_NAMES = {LRQ_VARIANT_GENERIC: "generic", LRQ_VARIANT_TILED: "tiled", LRQ_VARIANT_DECODE: "decode"}
 
 # every symbol include/lrq.h declares
-EXPORTED = ("lrq_forward", "lrq_backward", "lrq_workspace_size", "lrq_select_variant",
+EXPORTED = ("lrq_forward", "lrq_forward_kv", "lrq_backward", "lrq_workspace_size", "lrq_select_variant",
             "lrq_status_string", "lrq_last_error", "lrq_abi_version", "lrq_kernel_timing",
             "lrq_kernel_time_ms")
 
@@ -34,6 +34,11 @@ class LrqDesc(ctypes.Structure):
                 ("lora_rank", ctypes.c_int32), ("lora_alpha", ctypes.c_float),
                 ("lora_targets", ctypes.c_uint32), ("has_bias", ctypes.c_int32),
                 ("variant", ctypes.c_int32)]
+
+
+class LrqKvCache(ctypes.Structure):
+    _fields_ = [("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("slots", ctypes.c_void_p),
+                ("num_slots", ctypes.c_int64)]
 
 
 class LrqError(RuntimeError):
@@ -64,6 +69,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         PP = ctypes.POINTER(ctypes.c_void_p)
         lib.lrq_forward.argtypes = [ctypes.POINTER(LrqDesc), P, P, P, P, PP, PP, P, P, P, S, P]
         lib.lrq_forward.restype = ctypes.c_int
+        lib.lrq_forward_kv.argtypes = [ctypes.POINTER(LrqDesc), P, P, P, P, PP, PP, P, P,
+                                       ctypes.POINTER(LrqKvCache), P, S, P]
+        lib.lrq_forward_kv.restype = ctypes.c_int
         lib.lrq_backward.argtypes = [ctypes.POINTER(LrqDesc), P, P, P, P, PP, PP, P, P, P, P, PP, PP, P, S, P]
         lib.lrq_backward.restype = ctypes.c_int
         lib.lrq_workspace_size.argtypes = [ctypes.POINTER(LrqDesc), ctypes.c_int]
@@ -137,6 +145,19 @@ def lrq_forward(desc: LrqDesc, x, gamma, w_qkv, bias, lora_a, lora_b, positions,
     st = lib.lrq_forward(ctypes.byref(desc), _ptr(x), _ptr(gamma), _ptr(w_qkv), _ptr(bias),
                          _ptr3(lora_a), _ptr3(lora_b), _ptr(positions), _ptr(out), _ptr(workspace),
                          int(workspace_bytes), _stream(stream, (x, out)))
+    _check(st)
+
+
+def lrq_forward_kv(desc: LrqDesc, x, gamma, w_qkv, bias, lora_a, lora_b, positions, out,
+                   k_cache, v_cache, slots, num_slots: int, workspace=None,
+                   workspace_bytes: Optional[int] = None, stream=None) -> None:
+    """lrq_forward plus the k and v rows written to k_cache / v_cache at rows ``slots``."""
+    lib = load()
+    workspace_bytes = _ws_bytes(workspace, workspace_bytes)
+    kv = LrqKvCache(_ptr(k_cache), _ptr(v_cache), _ptr(slots), int(num_slots))
+    st = lib.lrq_forward_kv(ctypes.byref(desc), _ptr(x), _ptr(gamma), _ptr(w_qkv), _ptr(bias),
+                            _ptr3(lora_a), _ptr3(lora_b), _ptr(positions), _ptr(out), ctypes.byref(kv),
+                            _ptr(workspace), int(workspace_bytes), _stream(stream, (x, out)))
     _check(st)
 
 

@@ -13,6 +13,8 @@
 //             A block:  U_t = bf16(s * inv * acc) into the workspace
 //   finish  one block per 64 adapted columns and 64 rows:  out = bf16(y + RoPE(B_t U_t)),
 //           where RoPE is applied to the LoRA term on its own (the rotation is linear).
+// With a key/value cache, the stores of the k and v columns into out (main for columns
+// without an adapter, finish for the others) also go to the token's cache row.
 //
 // The operator is RoPE(W h + b + s B (A h)) with h = x * inv * gamma; inv, a per-row scalar,
 // is applied after the products and gamma before them.  Every sum runs in a fixed order, so
@@ -61,6 +63,15 @@ DecodeLayout decode_layout(const FwdParams& p) {
   return L;
 }
 
+// Cache row of a token (or nullptr): the k or v cache row of the token when the call has a
+// cache, `col0` is a k or v column and the slot lies in the cache.  Column c of that block
+// lands at row[c - first column of the block].
+__device__ __forceinline__ uint16_t* cache_row(uint16_t* kv_k, uint16_t* kv_v, int64_t num_slots, int slot,
+                                               int col0, int col_k, int col_v) {
+  if (!kv_k || col0 < col_k || slot < 0 || slot >= num_slots) return nullptr;
+  return (col0 < col_v ? kv_k : kv_v) + static_cast<int64_t>(slot) * (col_v - col_k);
+}
+
 // ---------------------------------------------------------------- main
 struct MainArgs {
   const uint16_t* x;
@@ -72,6 +83,10 @@ struct MainArgs {
   uint16_t* out;
   float* y;
   uint16_t* u;
+  uint16_t* kv_k;           // key/value cache rows (nullptr: none)
+  uint16_t* kv_v;
+  const int32_t* kv_slots;
+  int64_t kv_num_slots;
   int64_t T;
   int d, N, D, r, nt, n_wblocks;
   int col_k, col_v, rot_end;
@@ -264,12 +279,14 @@ __global__ __launch_bounds__(256, 1) void decode_main_kernel(MainArgs a) {
   const double om = exp2(-(2.0 * i_pair / a.D) * a.log2_theta) * 0.15915494309189533577;  // turns
   const int64_t myrow = rg * kRows + rt * 32 + l32;
   const int pos_l = myrow < a.T ? a.pos[myrow] : 0;
+  const int slot_l = a.kv_slots && myrow < a.T ? a.kv_slots[myrow] : -1;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int rsub = (v >> 2) * 8 + h32 * 4 + (v & 3);
     const int64_t row = rg * kRows + rt * 32 + rsub;
     const float inv = __shfl(inv_l, rsub);
     const int pos = __shfl(pos_l, rsub);
+    const int slot = __shfl(slot_l, rsub);
     float y0 = fmaf(y[0][v], inv, b0);
     float y1 = fmaf(y[1][v], inv, b1);
     if (rot) {
@@ -287,8 +304,15 @@ __global__ __launch_bounds__(256, 1) void decode_main_kernel(MainArgs a) {
         o[c1] = y1;
       } else {
         uint16_t* o = a.out + row * a.N;
-        o[c0] = f32_to_bf16_bits(y0);
-        o[c1] = f32_to_bf16_bits(y1);
+        const uint16_t o0 = f32_to_bf16_bits(y0), o1 = f32_to_bf16_bits(y1);
+        o[c0] = o0;
+        o[c1] = o1;
+        uint16_t* kvr = cache_row(a.kv_k, a.kv_v, a.kv_num_slots, slot, col0, a.col_k, a.col_v);
+        if (kvr) {
+          const int cb = col0 < a.col_v ? a.col_k : a.col_v;
+          kvr[c0 - cb] = o0;
+          kvr[c1 - cb] = o1;
+        }
       }
     }
   }
@@ -301,6 +325,10 @@ struct FinishArgs {
   const uint16_t* b[3];
   const int32_t* pos;
   uint16_t* out;
+  uint16_t* kv_k;
+  uint16_t* kv_v;
+  const int32_t* kv_slots;
+  int64_t kv_num_slots;
   int64_t T;
   int N, D, r, nt;
   int col_k, col_v, rot_end;
@@ -339,6 +367,7 @@ __global__ __launch_bounds__(128) void decode_finish_kernel(FinishArgs a) {
     yv[v][1] = a.y[row * a.N + c1];
   }
   const int pos_l = myrow < a.T ? a.pos[myrow] : 0;
+  const int slot_l = a.kv_slots && myrow < a.T ? a.kv_slots[myrow] : -1;
   // ranks past r: B is zero there (vector loads skip them; element loads are clamped into
   // the row and zeroed), so the four rank steps run unconditionally (U holds finite padding)
   bf16x8 uf[4], bf[4][2];
@@ -374,6 +403,7 @@ __global__ __launch_bounds__(128) void decode_finish_kernel(FinishArgs a) {
     const int rsub = (v >> 2) * 8 + h32 * 4 + (v & 3);
     const int64_t row = rg * kRows + rt * 32 + rsub;
     const int pos = __shfl(pos_l, rsub);
+    const int slot = __shfl(slot_l, rsub);
     float l0 = lo[0][v], l1 = lo[1][v];
     if (rot) {
       const double tt = static_cast<double>(pos) * om;
@@ -385,8 +415,15 @@ __global__ __launch_bounds__(128) void decode_finish_kernel(FinishArgs a) {
     }
     if (row < a.T) {
       uint16_t* o = a.out + row * a.N;
-      o[c0] = f32_to_bf16_bits(yv[v][0] + l0);
-      o[c1] = f32_to_bf16_bits(yv[v][1] + l1);
+      const uint16_t o0 = f32_to_bf16_bits(yv[v][0] + l0), o1 = f32_to_bf16_bits(yv[v][1] + l1);
+      o[c0] = o0;
+      o[c1] = o1;
+      uint16_t* kvr = cache_row(a.kv_k, a.kv_v, a.kv_num_slots, slot, col0, a.col_k, a.col_v);
+      if (kvr) {
+        const int cb = col0 < a.col_v ? a.col_k : a.col_v;
+        kvr[c0 - cb] = o0;
+        kvr[c1 - cb] = o1;
+      }
     }
   }
 }
@@ -414,6 +451,10 @@ hipError_t launch_fwd_decode(const FwdParams& p, hipStream_t s) {
   for (int i = 0; i < 3; ++i) ma.a[i] = static_cast<const uint16_t*>(p.a[L.tgt[i]]);
   ma.pos = p.pos;
   ma.out = static_cast<uint16_t*>(p.out);
+  ma.kv_k = static_cast<uint16_t*>(p.kv_k);
+  ma.kv_v = static_cast<uint16_t*>(p.kv_v);
+  ma.kv_slots = p.kv_slots;
+  ma.kv_num_slots = p.kv_num_slots;
   ma.y = reinterpret_cast<float*>(ws + L.y);
   ma.u = reinterpret_cast<uint16_t*>(ws + L.u);
   ma.T = p.T;
@@ -445,6 +486,10 @@ hipError_t launch_fwd_decode(const FwdParams& p, hipStream_t s) {
   for (int i = 0; i < L.nt; ++i) fa.ublock[L.tgt[i]] = i;
   fa.pos = p.pos;
   fa.out = ma.out;
+  fa.kv_k = ma.kv_k;
+  fa.kv_v = ma.kv_v;
+  fa.kv_slots = ma.kv_slots;
+  fa.kv_num_slots = ma.kv_num_slots;
   fa.T = p.T;
   fa.N = p.N;
   fa.D = p.D;

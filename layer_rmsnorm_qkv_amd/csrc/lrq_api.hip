@@ -126,6 +126,7 @@ lrq_status check_desc(const lrq_desc* d, lrq::FwdParams& p) {
   p.r = d->lora_targets ? d->lora_rank : 0;
   p.scale = d->lora_targets ? d->lora_alpha / static_cast<float>(d->lora_rank) : 0.f;
   p.has_bias = d->has_bias;
+  p.esize = d->dtype == LRQ_F32 ? 4 : 2;
   return LRQ_OK;
 }
 
@@ -235,10 +236,10 @@ size_t lrq_workspace_size(const lrq_desc* desc, int for_backward) {
   return workspace_for(v, p, for_backward != 0);
 }
 
-lrq_status lrq_forward(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,
-                       const void* bias, const void* const* lora_a, const void* const* lora_b,
-                       const int32_t* positions, void* out, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+lrq_status lrq_forward_kv(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,
+                          const void* bias, const void* const* lora_a, const void* const* lora_b,
+                          const int32_t* positions, void* out, const lrq_kv_cache* kv, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   lrq::FwdParams p;
   lrq_status st = check_desc(desc, p);
   if (st != LRQ_OK) return st;
@@ -246,6 +247,14 @@ lrq_status lrq_forward(const lrq_desc* desc, const void* x, const void* gamma, c
   if (st != LRQ_OK) return st;
   if (p.T > 0 && !out) return fail(LRQ_ERR_INVALID_ARG, "out is NULL");
   if (out && !aligned16(out)) return fail(LRQ_ERR_UNSUPPORTED, "out must be 16-byte aligned");
+  if (kv) {
+    if (kv->num_slots < 0) return fail(LRQ_ERR_INVALID_ARG, "kv->num_slots < 0");
+    if (p.T > 0 && (!kv->k_cache || !kv->v_cache || !kv->slots))
+      return fail(LRQ_ERR_INVALID_ARG, "kv->k_cache, kv->v_cache and kv->slots are required");
+    for (const void* q : {static_cast<const void*>(kv->k_cache), static_cast<const void*>(kv->v_cache),
+                          static_cast<const void*>(kv->slots)})
+      if (q && !aligned16(q)) return fail(LRQ_ERR_UNSUPPORTED, "kv cache pointers must be 16-byte aligned");
+  }
   const int v = select(desc, p, false);
   if (v < 0) return LRQ_ERR_UNSUPPORTED;
   const size_t need = workspace_for(v, p, false);
@@ -255,6 +264,12 @@ lrq_status lrq_forward(const lrq_desc* desc, const void* x, const void* gamma, c
   p.out = out;
   p.ws = workspace;
   p.ws_bytes = workspace_bytes;
+  if (kv && kv->num_slots > 0) {
+    p.kv_k = kv->k_cache;
+    p.kv_v = kv->v_cache;
+    p.kv_slots = kv->slots;
+    p.kv_num_slots = kv->num_slots;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   g_timing.kind = 0;
@@ -264,7 +279,17 @@ lrq_status lrq_forward(const lrq_desc* desc, const void* x, const void* gamma, c
     default:
       e = desc->dtype == LRQ_F32 ? lrq::launch_fwd_generic_f32(p, s) : lrq::launch_fwd_generic_bf16(p, s);
   }
+  // the decode family stores the cache rows from its own epilogues
+  if (e == hipSuccess && v != LRQ_VARIANT_DECODE) e = lrq::launch_kv_scatter(p, s);
   return hip_status(e, "forward launch");
+}
+
+lrq_status lrq_forward(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,
+                       const void* bias, const void* const* lora_a, const void* const* lora_b,
+                       const int32_t* positions, void* out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return lrq_forward_kv(desc, x, gamma, w_qkv, bias, lora_a, lora_b, positions, out, nullptr, workspace,
+                        workspace_bytes, stream);
 }
 
 lrq_status lrq_backward(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,

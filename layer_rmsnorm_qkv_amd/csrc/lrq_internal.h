@@ -34,6 +34,12 @@ struct FwdParams {
   void* out;
   void* ws;
   size_t ws_bytes;
+  int esize;                // bytes per element of the call's dtype
+  // optional key/value cache destination (kv_slots == nullptr: none)
+  void* kv_k;               // [kv_num_slots][Hkv * D]
+  void* kv_v;
+  const int32_t* kv_slots;  // [T]; slots outside [0, kv_num_slots) are skipped
+  int64_t kv_num_slots;
 };
 
 struct BwdParams {
@@ -56,6 +62,7 @@ void timing_begin(hipStream_t s);
 void timing_end(hipStream_t s);
 
 // ---- launchers (defined in the kernel translation units) ----
+hipError_t launch_kv_scatter(const FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_generic_f32(const FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_generic_bf16(const FwdParams& p, hipStream_t s);
 hipError_t launch_bwd_generic_f32(const BwdParams& p, hipStream_t s);

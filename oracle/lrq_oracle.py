@@ -220,6 +220,28 @@ def forward_chunked(spec: Spec, x, gamma, w, bias, a, b, positions, chunk: int =
     return out
 
 
+# --------------------------------------------------------------------------- key/value cache
+
+def kv_cache_write(spec: Spec, out, slots, k_cache, v_cache) -> Tuple[np.ndarray, np.ndarray]:
+    """The caches after a forward call writes its keys and values: a copy of each cache with
+    row slots[t] replaced by token t's k block (columns of the k heads) and v block of
+    ``out``, for every token whose slot lies in [0, num_slots); other rows are kept.  The
+    attention step that follows the projection reads the rotated k and the v (decoder-layer
+    op sequence on the inference-engine page; the same page lists a fused attention kernel
+    with KV-cache handling).  The row-per-token layout is a reading: the pages define none.
+    Slots must be distinct among the written tokens (several correct results otherwise)."""
+    out = _f64(out)
+    kc, vc = _f64(k_cache).copy(), _f64(v_cache).copy()
+    k_lo, k_hi = spec.columns(TARGET_K)
+    v_lo, v_hi = spec.columns(TARGET_V)
+    n = kc.shape[0]
+    for t, slot in enumerate(np.asarray(slots).tolist()):
+        if 0 <= slot < n:
+            kc[slot] = out[t, k_lo:k_hi]
+            vc[slot] = out[t, v_lo:v_hi]
+    return kc, vc
+
+
 # --------------------------------------------------------------------------- backward
 
 def unrotate_grad(spec: Spec, dy, positions) -> np.ndarray:

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol():
     assert set(syms) == set(B.EXPORTED), syms
     for s in syms:
         assert hasattr(lib, s), s
-    assert B.lrq_abi_version() == 1
+    assert B.lrq_abi_version() == 2
 
 
 def test_desc_layout_matches_header(tmp_path):
@@ -128,6 +128,30 @@ def test_zero_tokens_is_a_noop():
     B.lrq_forward(good_desc(n_tokens=0), None, None, None, None, [FAKE, None, FAKE], [FAKE, None, FAKE],
                   None, None)
     B.lrq_forward(good_desc(n_tokens=0, lora_targets=0), None, None, None, None, None, None, None, None)
+
+
+def fwd_kv(desc, kv_over=None, **over):
+    args = dict(x=FAKE, gamma=FAKE, w_qkv=FAKE, bias=None, lora_a=[FAKE, None, FAKE], lora_b=[FAKE, None, FAKE],
+                positions=FAKE, out=FAKE, k_cache=FAKE, v_cache=FAKE, slots=FAKE, num_slots=16, workspace=None,
+                stream=None)
+    args.update(over)
+    args.update(kv_over or {})
+    B.lrq_forward_kv(desc, **args)
+
+
+def test_forward_kv_checks():
+    # every call fails validation: the cache arguments are checked like the others
+    expect(B.LRQ_ERR_INVALID_ARG, fwd_kv, good_desc(), dict(num_slots=-1))
+    for missing in ("k_cache", "v_cache", "slots"):
+        expect(B.LRQ_ERR_INVALID_ARG, fwd_kv, good_desc(), {missing: None})
+    expect(B.LRQ_ERR_UNSUPPORTED, fwd_kv, good_desc(), dict(slots=FAKE + 4))
+    expect(B.LRQ_ERR_UNSUPPORTED, fwd_kv, good_desc(), dict(k_cache=FAKE + 2))
+    # the forward's own checks still apply
+    expect(B.LRQ_ERR_INVALID_ARG, fwd_kv, good_desc(n_q_heads=3))
+    expect(B.LRQ_ERR_INVALID_ARG, fwd_kv, good_desc(), out=None)
+    # T == 0: nothing to write, NULL caches allowed
+    B.lrq_forward_kv(good_desc(n_tokens=0, lora_targets=0), None, None, None, None, None, None, None, None,
+                     None, None, None, 0)
 
 
 def test_backward_checks():
