@@ -225,6 +225,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--w-copies", type=int, default=0,
                     help="rotate among this many W_qkv copies (defeats the 256 MB MALL; default 4 for decode)")
+    ap.add_argument("--kv-cache", action="store_true",
+                    help="forward through lrq_forward_kv: every token also writes its k and v rows to a "
+                         "cache of T rows (slot t for token t)")
     ap.add_argument("--copy-probe", type=int, default=0, help="run a device copy of this many bytes and exit")
     ap.add_argument("--record-traffic", default="", help="workload name: store counter traffic and exit")
     ap.add_argument("--family", default="", help="kernel family key (tiled, decode, bwd_tiled, ...)")
@@ -266,10 +269,23 @@ def main():
 
     n_copies = args.w_copies or (4 if w.name == "decode" else 1)
     w_list = [prob.w_qkv] + [prob.w_qkv.clone() for _ in range(n_copies - 1)]
+    kvw = w.n_kv_heads * w.head_dim
+    if args.kv_cache:
+        k_cache = torch.zeros((w.n_tokens, kvw), dtype=prob.out.dtype, device=prob.out.device)
+        v_cache = torch.zeros_like(k_cache)
+        slots = torch.arange(w.n_tokens, dtype=torch.int32, device=prob.out.device)
+
+    def forward():
+        if args.kv_cache:
+            B.lrq_forward_kv(prob.desc, prob.x, prob.gamma, prob.w_qkv, prob.bias, prob.a, prob.b, prob.positions,
+                             prob.out, k_cache, v_cache, slots, w.n_tokens, prob.workspace, stream=stream)
+        else:
+            prob.forward(stream=stream)
+        return prob.out
 
     def step(i):
         prob.w_qkv = w_list[i % n_copies]
-        prob.forward(stream=stream)
+        forward()
         if w.backward:
             prob.backward(stream=stream)
 
@@ -297,7 +313,7 @@ def main():
         e0, e1, e2 = ev[i]
         prob.w_qkv = w_list[i % n_copies]
         e0.record(stream)
-        prob.forward(stream=stream)
+        forward()
         e1.record(stream)
         if w.backward:
             prob.backward(stream=stream)
@@ -309,6 +325,8 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     tokens = w.n_tokens
     f_fwd, f_bwd, bytes_fwd = algorithmic_work(w)
+    if args.kv_cache:
+        bytes_fwd += 2 * w.n_tokens * kvw * (4 if w.dtype == "f32" else 2)  # the cache rows written
     result = {
         "metric": METRIC, "value": tokens / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
@@ -317,7 +335,8 @@ def main():
         "config": {"workload": w.name, "description": w.description, "tokens": tokens, "d_model": w.d_model,
                    "n_out": w.n_out, "lora_rank": w.lora_rank, "lora_targets": w.lora_targets,
                    "kernel_family": vname, "parallelism": "none (1 GPU)",
-                   "pass": "forward+backward" if w.backward else "forward"},
+                   "pass": "forward+backward" if w.backward else "forward",
+                   "kv_cache": bool(args.kv_cache)},
     }
     # call-level rates (whole library calls)
     tflops_fwd = f_fwd / (fwd_ms * 1e-3) / 1e12
@@ -351,7 +370,7 @@ def main():
                               "launch_ms": dom_ms, "algorithmic_flop": work}
     if not args.no_cpu_baseline:
         prob.w_qkv = w_list[0]
-        got = prob.forward(stream=stream)
+        got = forward()
         torch.cuda.synchronize()
         got = got.float().cpu().numpy().astype(np.float64)
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, rows_cap=w.n_tokens,
