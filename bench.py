@@ -6,7 +6,9 @@
 A step is one call of the whole operator on one batch of synthetic, seeded input that is
 already resident in HBM: the forward for the layer and decode workloads, forward then
 backward for the training workload.  W untimed warm-up steps, then K timed steps between
-two device synchronisations; one JSON line is printed.
+two device synchronisations; one JSON line is printed.  The K steps are launched as one
+replay of a HIP graph that holds them (``--graph off``: eager calls), so the host's launch
+cost neither bounds a decode step nor leaves gaps between the kernels of a layer step.
 
 * ``value``: tokens per second of the whole job (one GPU).
 * ``roofline``: the dominant kernel's algorithmic FLOPs (or bytes, for the bandwidth-bound
@@ -225,6 +227,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--w-copies", type=int, default=0,
                     help="rotate among this many W_qkv copies (defeats the 256 MB MALL; default 4 for decode)")
+    ap.add_argument("--graph", choices=["on", "off"], default="on",
+                    help="launch the K timed steps as one replay of a HIP graph that holds them (on), or as "
+                         "eager library calls (off)")
     ap.add_argument("--kv-cache", action="store_true",
                     help="forward through lrq_forward_kv: every token also writes its k and v rows to a "
                          "cache of T rows (slot t for token t)")
@@ -275,30 +280,53 @@ def main():
         v_cache = torch.zeros_like(k_cache)
         slots = torch.arange(w.n_tokens, dtype=torch.int32, device=prob.out.device)
 
-    def forward():
+    def forward(s=None):
+        s = stream if s is None else s
         if args.kv_cache:
             B.lrq_forward_kv(prob.desc, prob.x, prob.gamma, prob.w_qkv, prob.bias, prob.a, prob.b, prob.positions,
-                             prob.out, k_cache, v_cache, slots, w.n_tokens, prob.workspace, stream=stream)
+                             prob.out, k_cache, v_cache, slots, w.n_tokens, prob.workspace, stream=s)
         else:
-            prob.forward(stream=stream)
+            prob.forward(stream=s)
         return prob.out
 
-    def step(i):
+    def step(i, s=None):
         prob.w_qkv = w_list[i % n_copies]
-        forward()
+        forward(s)
         if w.backward:
-            prob.backward(stream=stream)
+            prob.backward(stream=stream if s is None else s)
 
     for i in range(args.warmup):
         step(i)
 
+    use_graph = args.graph == "on"
+    if use_graph:
+        # One graph holds the K steps, each with the library's timing events around its dominant
+        # kernel (the events are created by an eager pass first: nothing is created during
+        # capture).  One untimed replay, then the timed one.
+        B.lrq_kernel_timing(True)
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        B.lrq_kernel_timing(True)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream()
+            for i in range(args.steps):
+                step(i, cap)
+        graph.replay()
+        torch.cuda.synchronize()
+
     # timed region: exactly K steps, nothing else on the stream but the library's own timing
     # events around each call's dominant kernel (the roofline's per-launch duration)
     torch.cuda.synchronize()
-    B.lrq_kernel_timing(True)
+    if not use_graph:
+        B.lrq_kernel_timing(True)
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
+    if use_graph:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kfwd_ms, n_fwd = B.lrq_kernel_time_ms(False)
@@ -336,7 +364,8 @@ def main():
                    "n_out": w.n_out, "lora_rank": w.lora_rank, "lora_targets": w.lora_targets,
                    "kernel_family": vname, "parallelism": "none (1 GPU)",
                    "pass": "forward+backward" if w.backward else "forward",
-                   "kv_cache": bool(args.kv_cache)},
+                   "kv_cache": bool(args.kv_cache),
+                   "launch": "one HIP graph replay of the K steps" if use_graph else "eager calls"},
     }
     # call-level rates (whole library calls)
     tflops_fwd = f_fwd / (fwd_ms * 1e-3) / 1e12
