@@ -362,7 +362,7 @@ __global__ __launch_bounds__(128) void decode_finish_kernel(FinishArgs a) {
   float yv[16][2];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    const int64_t row = min(rg * kRows + rt * 32 + (v >> 2) * 8 + h32 * 4 + (v & 3), a.T - 1);
+    const int64_t row = min(static_cast<int64_t>(rg * kRows + rt * 32 + (v >> 2) * 8 + h32 * 4 + (v & 3)), a.T - 1);
     yv[v][0] = a.y[row * a.N + c0];
     yv[v][1] = a.y[row * a.N + c1];
   }
@@ -379,8 +379,9 @@ __global__ __launch_bounds__(128) void decode_finish_kernel(FinishArgs a) {
     for (int ct = 0; ct < 2; ++ct) {
       const uint16_t* brow = bt + static_cast<int64_t>(col0 + ct * half + l32 - lo_t) * a.r;
       if constexpr (VEC) {
-        bf[kk][ct] = bf16x8{};
-        if (rank0 < a.r) bf[kk][ct] = *reinterpret_cast<const bf16x8*>(brow + rank0);
+        // unconditional load (clamped into the row; zeroed below): a load under a lane-divergent
+        // branch makes the compiler wait for every earlier load at the branch's end
+        bf[kk][ct] = *reinterpret_cast<const bf16x8*>(brow + min(rank0, a.r - 8));
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -390,14 +391,22 @@ __global__ __launch_bounds__(128) void decode_finish_kernel(FinishArgs a) {
       }
     }
   }
+  // the rotation frequency (a double-precision exp2) while the loads are in flight
+  tile::sched_fence();
+  const bool rot = col0 < a.rot_end;
+  const double om = exp2(-(2.0 * (sub * 32 + l32) / a.D) * a.log2_theta) * 0.15915494309189533577;
+  tile::sched_fence();
+  if constexpr (VEC) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      if (kk * 16 + 8 * h32 >= a.r) bf[kk][0] = bf[kk][1] = bf16x8{};
+  }
   floatx16 lo[2] = {floatx16{}, floatx16{}};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) lo[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(uf[kk], bf[kk][ct], lo[ct], 0, 0, 0);
 
-  const bool rot = col0 < a.rot_end;
-  const double om = exp2(-(2.0 * (sub * 32 + l32) / a.D) * a.log2_theta) * 0.15915494309189533577;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int rsub = (v >> 2) * 8 + h32 * 4 + (v & 3);
