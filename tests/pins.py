@@ -305,8 +305,22 @@ def check_backward_finite_differences(o):
     _close(dx_sub, dx[[2, 0]], 1e-13, "dx row subset")
 
 
+def check_kv_cache_by_hand(o):
+    """Cache rows after a forward call writes its keys and values, written out by hand: 2 q heads,
+    1 kv head, head size 2 (columns q 0..3 | k 4, 5 | v 6, 7), four tokens, a cache of four rows
+    filled with -1.  Token 1 has a negative slot and token 3 a slot past the cache: neither is
+    written; rows 1 and 3 keep their old values; the caches passed in are not modified."""
+    spec = o.Spec(d_model=4, n_q_heads=2, n_kv_heads=1, head_dim=2)
+    out = np.arange(32, dtype=np.float64).reshape(4, 8)
+    k0, v0 = -np.ones((4, 2)), -np.ones((4, 2))
+    kc, vc = o.kv_cache_write(spec, out, [2, -1, 0, 5], k0, v0)
+    assert np.asarray(kc).tolist() == [[20.0, 21.0], [-1.0, -1.0], [4.0, 5.0], [-1.0, -1.0]]
+    assert np.asarray(vc).tolist() == [[22.0, 23.0], [-1.0, -1.0], [6.0, 7.0], [-1.0, -1.0]]
+    assert (k0 == -1.0).all() and (v0 == -1.0).all()
+
+
 ALL_CHECKS = [check_rms_closed_form, check_rms_constant_row, check_rms_torch, check_scale_invariance,
               check_lora_zero_b, check_lora_merged_weight, check_lora_only,
               check_rope_closed_form, check_rope_complex_form, check_rope_position_zero,
               check_rope_pair_norms_and_v, check_rope_relative, check_brute_force,
-              check_backward_finite_differences]
+              check_backward_finite_differences, check_kv_cache_by_hand]

@@ -121,6 +121,19 @@ def _bwd_no_unrotate(spec, dy, positions):
     return np.asarray(dy, np.float64).copy()
 
 
+def _kv_swapped(spec, out, slots, k_cache, v_cache):
+    kc, vc = _real_kv(spec, out, slots, k_cache, v_cache)
+    return vc, kc
+
+
+def _kv_clamped(spec, out, slots, k_cache, v_cache):
+    n = np.asarray(k_cache).shape[0]
+    return _real_kv(spec, out, np.clip(np.asarray(slots), 0, n - 1), k_cache, v_cache)
+
+
+_real_kv = o.kv_cache_write
+
+
 MUTANTS = {
     "eps outside sqrt": ("rms_inverse", _eps_outside),
     "sum instead of mean": ("rms_inverse", _sum_not_mean),
@@ -138,6 +151,8 @@ MUTANTS = {
     "dx missing inv^3 term": ("backward", _bwd_drop_inv3),
     "dB uses h instead of U": ("backward", _bwd_db_with_h),
     "gradient not un-rotated": ("unrotate_grad", _bwd_no_unrotate),
+    "k and v cache rows swapped": ("kv_cache_write", _kv_swapped),
+    "out-of-range slots clamped into the cache": ("kv_cache_write", _kv_clamped),
 }
 
 

@@ -50,18 +50,3 @@ def test_bf16_rounding_of_inputs():
     assert np.array_equal(i1["x"], i2["x"]) and np.array_equal(i1["w"], i2["w"])
     assert np.array_equal(wl.round_to_bf16(i1["x"]), i1["x"])
 
-
-def test_kv_cache_write_by_hand():
-    """Cache rows after a forward call writes its keys and values, written out by hand: 2 q heads,
-    1 kv head, head size 2 (columns q 0..3 | k 4, 5 | v 6, 7), four tokens, a cache of four rows
-    filled with -1.  Token 1 has a negative slot and token 3 a slot past the cache: neither is
-    written; rows 1 and 3 keep their old values."""
-    spec = o.Spec(d_model=4, n_q_heads=2, n_kv_heads=1, head_dim=2)
-    out = np.arange(32, dtype=np.float64).reshape(4, 8)
-    kc, vc = o.kv_cache_write(spec, out, [2, -1, 0, 5], -np.ones((4, 2)), -np.ones((4, 2)))
-    assert kc.tolist() == [[20.0, 21.0], [-1.0, -1.0], [4.0, 5.0], [-1.0, -1.0]]
-    assert vc.tolist() == [[22.0, 23.0], [-1.0, -1.0], [6.0, 7.0], [-1.0, -1.0]]
-    # the caches passed in are not modified
-    k0 = -np.ones((4, 2))
-    o.kv_cache_write(spec, out, [0, 1, 2, 3], k0, -np.ones((4, 2)))
-    assert (k0 == -1.0).all()
