@@ -132,7 +132,11 @@ struct PrepArgs {
 };
 
 __global__ __launch_bounds__(256) void prep_weights_kernel(PrepArgs a) {
-  __shared__ uint16_t tile_s[64][72];  // 144-byte rows: 16-byte aligned, banks spread
+  // [64][64] with the 16-byte chunks of row q stored at chunk (c ^ (q / 8) % 8): the 16-byte
+  // writes of a row and the column reads (8 rows q = 8 k + const, one chunk per wave) both
+  // hit distinct banks (a padded row pitch cannot do both and stay 16-byte aligned)
+  __shared__ uint16_t tile_s[64][64];
+  auto ts = [&](int q, int j) -> uint16_t& { return tile_s[q][(((j >> 3) ^ (q >> 3)) & 7) * 8 + (j & 7)]; };
   const int tid = threadIdx.x;
   if (static_cast<int>(blockIdx.x) < a.wt_blocks) {
     // transpose a 64 x 64 block: source rows q (LoRA-extended K index) x columns j, moved as
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(256) void prep_weights_kernel(PrepArgs a) {
             src = a.a[t] + static_cast<int64_t>(cq - a.off[t]) * a.d;
       }
       const uint4 v = src ? *reinterpret_cast<const uint4*>(src + j0 + jc) : uint4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<uint4*>(&tile_s[qi][jc]) = v;
+      *reinterpret_cast<uint4*>(&ts(qi, jc)) = v;
     }
     __syncthreads();
 #pragma unroll
@@ -165,7 +169,7 @@ __global__ __launch_bounds__(256) void prep_weights_kernel(PrepArgs a) {
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        w[e] = static_cast<uint32_t>(tile_s[qc + 2 * e][ji]) | (static_cast<uint32_t>(tile_s[qc + 2 * e + 1][ji]) << 16);
+        w[e] = static_cast<uint32_t>(ts(qc + 2 * e, ji)) | (static_cast<uint32_t>(ts(qc + 2 * e + 1, ji)) << 16);
       *reinterpret_cast<uint4*>(a.wt + static_cast<int64_t>(j0 + ji) * a.K + q0 + qc) = uint4{w[0], w[1], w[2], w[3]};
     }
     return;
