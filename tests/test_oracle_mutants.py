@@ -166,6 +166,8 @@ def _failures(checks):
     return failed
 
 
+# a mutant may divide by zero on the pins' all-zero rows; that is part of how it fails
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")
 @pytest.mark.parametrize("name", list(MUTANTS))
 def test_mutant_is_caught(name, monkeypatch):
     where, repl = MUTANTS[name]
