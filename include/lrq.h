@@ -45,7 +45,8 @@
  * reference after a call returns.  Work is enqueued asynchronously on `stream` (a
  * hipStream_t; NULL = the null stream) and nothing is synchronised.  The library allocates
  * no device memory; scratch space is the caller's `workspace` of at least
- * lrq_workspace_size() bytes (256-byte aligned), used only until the enqueued work ends.
+ * lrq_workspace_size() bytes, 256-byte aligned (LRQ_ERR_UNSUPPORTED otherwise), used only
+ * until the enqueued work ends.
  * Calls that share a workspace must be ordered on one stream.
  *
  * Errors: every entry point validates its arguments on the host before enqueuing

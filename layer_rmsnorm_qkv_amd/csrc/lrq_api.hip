@@ -80,6 +80,7 @@ lrq_status ok() {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
 // Largest token count sent to the decode family when the choice is automatic.
 constexpr int64_t kDecodeMaxTokens = 256;
@@ -260,6 +261,7 @@ lrq_status lrq_forward_kv(const lrq_desc* desc, const void* x, const void* gamma
   const size_t need = workspace_for(v, p, false);
   if (workspace_bytes < need) return fail(LRQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", workspace_bytes, need);
   if (need > 0 && !workspace) return fail(LRQ_ERR_INVALID_ARG, "workspace is NULL");
+  if (need > 0 && !aligned256(workspace)) return fail(LRQ_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
   if (p.T == 0) return ok();
   p.out = out;
   p.ws = workspace;
@@ -320,6 +322,7 @@ lrq_status lrq_backward(const lrq_desc* desc, const void* x, const void* gamma, 
   const size_t need = workspace_for(v, bp.f, true);
   if (workspace_bytes < need) return fail(LRQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", workspace_bytes, need);
   if (need > 0 && !workspace) return fail(LRQ_ERR_INVALID_ARG, "workspace is NULL");
+  if (need > 0 && !aligned256(workspace)) return fail(LRQ_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
   if (bp.f.T == 0 && !desc->lora_targets) return ok();
   bp.y = y;
   bp.dy = dy;

@@ -168,6 +168,27 @@ def test_backward_checks():
     expect(B.LRQ_ERR_UNSUPPORTED, bwd, good_desc(), dy=FAKE + 4)
 
 
+def test_workspace_alignment():
+    # the bf16 families need a workspace; one that is not 256-byte aligned is refused
+    desc = good_desc(dtype=B.LRQ_BF16, n_tokens=64, d_model=512, n_q_heads=4, n_kv_heads=4, head_dim=128)
+    need = B.lrq_workspace_size(desc)
+    assert need > 0
+    expect(B.LRQ_ERR_UNSUPPORTED, fwd, desc, workspace=FAKE + 16, workspace_bytes=need)
+    expect(B.LRQ_ERR_INVALID_ARG, fwd, desc, workspace=FAKE, workspace_bytes=need - 1)
+    bdesc = good_desc(dtype=B.LRQ_BF16, n_tokens=256, d_model=512, n_q_heads=4, n_kv_heads=4, head_dim=128)
+    bneed = B.lrq_workspace_size(bdesc, True)
+    assert bneed > 0
+
+    def bwd(**over):
+        args = dict(x=FAKE, gamma=FAKE, w_qkv=FAKE, bias=None, lora_a=[FAKE, None, FAKE],
+                    lora_b=[FAKE, None, FAKE], positions=FAKE, y=FAKE, dy=FAKE, dx=FAKE,
+                    d_lora_a=[FAKE, None, FAKE], d_lora_b=[FAKE, None, FAKE], workspace=FAKE + 256 + 16,
+                    workspace_bytes=bneed)
+        args.update(over)
+        B.lrq_backward(bdesc, **args)
+    expect(B.LRQ_ERR_UNSUPPORTED, bwd)
+
+
 def test_workspace_queries():
     assert B.lrq_workspace_size(good_desc()) == 0  # the generic family needs none
     assert B.lrq_workspace_size(good_desc(), True) == 0
