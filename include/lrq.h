@@ -17,7 +17,7 @@
  *    section 2.2 (1), RMSNorm + Rotary Embedding + Attention QKV fusion.
  *  - LoRA: frozen projection plus up(down(x)), with down A [r, d_in] and up B [d_out, r]:
  *    "Liger-Kernel内核级优化：GPU利用率飙升至90%以上", section on why conventional
- *    fine-tuning stalls (the y = Wx + B(Ax) formula and its unfused F.linear steps);
+ *    fine-tuning stalls (the y = Wx + B(Ax) formula and its unfused two-step form);
  *    rank r, alpha and the q/k/v target modules are the LoRA configuration fields shown
  *    on the same pages.  The scale alpha / r is the standard LoRA scale (the formula on the
  *    pages prints none).

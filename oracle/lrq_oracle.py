@@ -26,7 +26,7 @@ Sources (the web pages on Liger-Kernel, cited by title and section):
   提升训练效率", section 2.2 (1) "RMSNorm + Rotary Embedding + Attention QKV 融合";
   and the decoder-layer op sequence on the inference-engine page above.
 * LoRA as a frozen projection plus the product of a down matrix A [r, d_in] and
-  an up matrix B [d_out, r] (``F.linear(x, A)`` then ``F.linear(ax, B)``): page
+  an up matrix B [d_out, r] (down applied to x first, up to its result): page
   "Liger-Kernel内核级优化：GPU利用率飙升至90%以上", section "为什么传统微调会卡脖子"
   (the y = Wx + B(Ax) formula and its unfused decomposition).  The scale alpha/r
   and LoRA acting on the normalised input are readings (see below).
@@ -168,8 +168,8 @@ def lora_update(spec: Spec, h: np.ndarray, a: Mapping[int, np.ndarray],
                 b: Mapping[int, np.ndarray]) -> Dict[int, np.ndarray]:
     """For each target c: s * B_c (A_c h) ([T, N_c]).
 
-    LoRA page "Liger-Kernel内核级优化", y = Wx + B(Ax) and its ``F.linear(x, A)``,
-    ``F.linear(ax, B)`` decomposition; scale s = alpha / r (reading).
+    LoRA page "Liger-Kernel内核级优化", y = Wx + B(Ax) and its unfused two-step
+    decomposition (down, then up); scale s = alpha / r (reading).
     """
     out = {}
     for c in TARGETS:
