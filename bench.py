@@ -197,9 +197,14 @@ def cpu_baseline(w, inp, budget_s: float, rows_cap: int, gpu_rows_fn=None):
     n = int(min(T, rows_cap, max(probe, probe * budget_s / max(dt, 1e-6))))
     rows = np.sort(order[:n])
     dt, out = run(rows)
-    res = {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-           "sample": f"{n} of {T} rows (seeded), {'forward+backward' if w.backward else 'forward'}, "
-                     f"float64 numpy, {dt:.2f} s"}
+    # when the whole sample takes much less than the budget, repeat it (a steadier rate)
+    reps, total = 1, dt
+    while total < 0.8 * budget_s and reps < 256:
+        total += run(rows)[0]
+        reps += 1
+    res = {"value": n * reps / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n} of {T} rows (seeded) x {reps} passes, "
+                     f"{'forward+backward' if w.backward else 'forward'}, float64 numpy, {total:.2f} s"}
     if gpu_rows_fn is not None:  # the same rows from the GPU forward, for a parity figure
         res["gpu_parity_rel_fro"] = o.rel_frobenius(gpu_rows_fn(rows), out)
     return res
