@@ -32,6 +32,9 @@ CASES = {
     "bf16_gqa_t513_r24": TRAIN.replace(n_tokens=513, d_model=768, n_q_heads=4, n_kv_heads=2, lora_rank=24,
                                        lora_targets=TQ | TK, seq_len=0, max_position=9000),
     "bf16_noadapt_t77": TRAIN.replace(n_tokens=77, d_model=256, n_q_heads=2, n_kv_heads=2, lora_targets=0),
+    # a rank that is not a multiple of 8 (ragged rank columns in every LoRA pass)
+    "bf16_t200_r5_v": TRAIN.replace(n_tokens=200, d_model=512, n_q_heads=4, n_kv_heads=2, lora_rank=5,
+                                    lora_targets=TV),
 }
 
 
