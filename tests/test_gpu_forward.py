@@ -266,3 +266,25 @@ def test_forward_output_past_2_31_elements():
     errs = forward_errors(w, got, oracle_forward(w, inp, rows))
     log(f"  errors {errs}")
     assert max(errs.values()) <= TOL["bf16"], errs
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_forward_negative_positions(variant):
+    """Positions are not range-checked: a negative position rotates by a negative angle, in
+    every family as in the oracle (half of the rows negative, down to -9000)."""
+    w = SMALL_BF16["l3_t70"]
+    inp = wl.make_inputs(w)
+    pos = np.asarray(inp["positions"], dtype=np.int64)
+    rng = np.random.default_rng(7)
+    neg = rng.random(pos.shape[0]) < 0.5
+    pos = np.where(neg, -rng.integers(1, 9001, size=pos.shape[0]), pos)
+    inp["positions"] = pos.astype(np.int32)
+    desc = desc_for(w, variant=VARIANTS[variant])
+    if B.lrq_select_variant(desc) < 0:
+        pytest.skip(f"variant {variant} does not cover this shape")
+    log(f"[gpu] forward negative positions {w.name} variant={variant}")
+    prob = DeviceProblem(w, inp, variant=VARIANTS[variant])
+    got = to_np(prob.forward())
+    errs = forward_errors(w, got, oracle_forward(w, inp))
+    log(f"  errors {errs}")
+    assert max(errs.values()) <= TOL["bf16"], errs
