@@ -38,9 +38,15 @@ CASES = {
 }
 
 
-def run_backward(w, variant, dx_rows=None):
+def run_backward(w, variant, dx_rows=None, negative_positions=False):
     import torch
     inp = wl.make_inputs(w, with_dy=True)
+    if negative_positions:
+        # half of the rows at negative positions, down to -9000 (positions are not range-checked)
+        pos = np.asarray(inp["positions"], dtype=np.int64)
+        rng = np.random.default_rng(7)
+        neg = rng.random(pos.shape[0]) < 0.5
+        inp["positions"] = np.where(neg, -rng.integers(1, 9001, size=pos.shape[0]), pos).astype(np.int32)
     desc = desc_for(w, variant=variant)
     if B.lrq_select_variant(desc, True) < 0:
         pytest.skip(f"backward variant {variant} does not cover this shape")
@@ -150,3 +156,10 @@ def test_forward_and_backward_replay_in_a_hip_graph():
         assert all(torch.equal(g, r) for g, r in zip(got, ref))
         prob.forward()
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_backward_negative_positions(variant):
+    """The inverse rotation of the backward at negative positions, as in the oracle."""
+    errs = run_backward(CASES["bf16_train_small"], VARIANTS[variant], negative_positions=True)
+    assert max(errs.values()) <= TOL["bf16"], errs
