@@ -50,3 +50,21 @@ def test_bf16_rounding_of_inputs():
     assert np.array_equal(i1["x"], i2["x"]) and np.array_equal(i1["w"], i2["w"])
     assert np.array_equal(wl.round_to_bf16(i1["x"]), i1["x"])
 
+
+
+def test_rope_negative_positions_rotate_backwards():
+    """Rotating by a negative position -p is the inverse rotation by p (R(-phi) = R(phi)^T), and
+    the norm of every rotate-half pair is kept: the oracle's reading of negative positions,
+    which the GPU tests use as their reference."""
+    rng = np.random.default_rng(3)
+    D, heads, T = 16, 3, 9
+    y = rng.standard_normal((T, heads * D))
+    p = rng.integers(1, 9001, size=T).astype(np.int32)
+    neg = o.rope_rotate(y, -p, D, 1e4)
+    inv = o.rope_rotate(y, p, D, 1e4, inverse=True)
+    np.testing.assert_allclose(neg, inv, rtol=0, atol=1e-12)
+    back = o.rope_rotate(neg, p, D, 1e4)
+    np.testing.assert_allclose(back, y, rtol=0, atol=1e-12)
+    a = y.reshape(T, heads, 2, D // 2)
+    b = neg.reshape(T, heads, 2, D // 2)
+    np.testing.assert_allclose((b ** 2).sum(axis=2), (a ** 2).sum(axis=2), rtol=1e-12)
