@@ -271,6 +271,33 @@ def check_brute_force(o):
         _close(_fwd(o, spec, c), brute_forward(spec, c), 1e-12, f"brute force {kw}")
 
 
+# --------------------------------------------------------------------------- row subsets, chunks
+
+def check_forward_rows(o):
+    """forward_rows (the reference of every sampled-row GPU check) equals the scalar brute force
+    on exactly the rows asked for, in the order asked for -- unsorted and repeated rows included
+    -- so each row keeps its own position; and it equals forward()[rows] to within rounding (BLAS
+    picks a different kernel for a different row count, so the last bits may differ)."""
+    spec, c = tiny_case(o, seed=21, T=9, max_pos=300)
+    full = brute_forward(spec, c)
+    for rows in ([0], [8, 3, 3, 0, 5], list(range(9))[::-1], [4, 4, 4]):
+        got = o.forward_rows(spec, rows, c["x"], c["gamma"], c["w"], c["bias"], c["a"], c["b"], c["positions"])
+        _close(got, full[rows], 1e-12, f"forward_rows {rows} vs brute force")
+        _close(got, _fwd(o, spec, c)[rows], 1e-14, f"forward_rows {rows} vs forward()[rows]")
+
+
+def check_forward_chunked(o):
+    """forward_chunked (the reference of every full-output GPU check) equals the scalar brute
+    force on every row, for chunk lengths that leave a ragged last chunk (10 rows in chunks of
+    3), one chunk per row, and a single chunk longer than T."""
+    spec, c = tiny_case(o, seed=22, T=10, max_pos=500)
+    full = brute_forward(spec, c)
+    for chunk in (3, 1, 4, 64):
+        got = o.forward_chunked(spec, c["x"], c["gamma"], c["w"], c["bias"], c["a"], c["b"], c["positions"],
+                                chunk=chunk)
+        _close(got, full, 1e-12, f"forward_chunked chunk={chunk} vs brute force")
+
+
 # --------------------------------------------------------------------------- backward
 
 def check_backward_finite_differences(o):
@@ -323,4 +350,5 @@ ALL_CHECKS = [check_rms_closed_form, check_rms_constant_row, check_rms_torch, ch
               check_lora_zero_b, check_lora_merged_weight, check_lora_only,
               check_rope_closed_form, check_rope_complex_form, check_rope_position_zero,
               check_rope_pair_norms_and_v, check_rope_relative, check_brute_force,
+              check_forward_rows, check_forward_chunked,
               check_backward_finite_differences, check_kv_cache_by_hand]

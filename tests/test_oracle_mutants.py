@@ -134,6 +134,32 @@ def _kv_clamped(spec, out, slots, k_cache, v_cache):
 _real_kv = o.kv_cache_write
 
 
+def _rows_positions_unsliced(spec, rows, x, gamma, w, bias, a, b, positions):
+    # the rows' activations are taken, but the positions of the first len(rows) tokens
+    rows = np.asarray(rows, dtype=np.int64)
+    return o.forward(spec, np.asarray(x)[rows], gamma, w, bias, a, b, np.asarray(positions)[:len(rows)])
+
+
+def _chunks_restart_positions(spec, x, gamma, w, bias, a, b, positions, chunk=2048):
+    # every chunk is rotated with the positions of the first chunk (a chunk-boundary slip)
+    T = np.asarray(x).shape[0]
+    out = np.empty((T, spec.n_out))
+    for s0 in range(0, T, chunk):
+        s1 = min(T, s0 + chunk)
+        out[s0:s1] = o.forward(spec, np.asarray(x)[s0:s1], gamma, w, bias, a, b, np.asarray(positions)[0:s1 - s0])
+    return out
+
+
+def _chunks_overlapping_short(spec, x, gamma, w, bias, a, b, positions, chunk=2048):
+    # chunk bounds that step by chunk - 1: chunks overlap and the last row is never written
+    T = np.asarray(x).shape[0]
+    out = np.zeros((T, spec.n_out))
+    for s0 in range(0, max(T - 1, 1), max(chunk - 1, 1)):
+        s1 = min(T - 1, s0 + chunk)
+        out[s0:s1] = o.forward(spec, np.asarray(x)[s0:s1], gamma, w, bias, a, b, np.asarray(positions)[s0:s1])
+    return out
+
+
 MUTANTS = {
     "eps outside sqrt": ("rms_inverse", _eps_outside),
     "sum instead of mean": ("rms_inverse", _sum_not_mean),
@@ -153,6 +179,9 @@ MUTANTS = {
     "gradient not un-rotated": ("unrotate_grad", _bwd_no_unrotate),
     "k and v cache rows swapped": ("kv_cache_write", _kv_swapped),
     "out-of-range slots clamped into the cache": ("kv_cache_write", _kv_clamped),
+    "row subset keeps the first rows' positions": ("forward_rows", _rows_positions_unsliced),
+    "chunks restart the positions": ("forward_chunked", _chunks_restart_positions),
+    "overlapping chunks, last row unwritten": ("forward_chunked", _chunks_overlapping_short),
 }
 
 
