@@ -638,8 +638,9 @@ __global__ __launch_bounds__(256) void lora_reduce_kernel(ReduceArgs a) {
     const int64_t na = static_cast<int64_t>(a.r) * a.d;
     for (int64_t e = gid; e < na; e += stride) {
       const int64_t k = e / a.d, c = e % a.d;
-      const float s = a.chunks ? sum_chunks(a.pda + (a.off[t] + k) * a.d + c, sa, a.chunks) : 0.f;
-      a.da[t][e] = bf16_bits_to_f32(a.gamma[c]) * s;
+      // no token chunks (T == 0): gamma may be NULL and is not read
+      a.da[t][e] = a.chunks ? bf16_bits_to_f32(a.gamma[c]) * sum_chunks(a.pda + (a.off[t] + k) * a.d + c, sa, a.chunks)
+                            : 0.f;
     }
     const int64_t nb = static_cast<int64_t>(a.nt[t]) * a.r;
     const int64_t sb = nb;
