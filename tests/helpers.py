@@ -37,13 +37,66 @@ def oracle_forward(w, inp, rows=None):
                           inp["positions"])
 
 
+# Per-element bound |g - o| <= C_REL |o| + C_ABS rms(reference row), per dtype.  For bf16 the unit
+# roundoff is u = 2^-9: the output rounding contributes at most u |o| (C_REL = 2u leaves room for
+# the fp32 accumulation), and one rounding of each operand of a length-d dot product (the
+# weights with gamma folded in, the LoRA intermediate) adds a random error of about
+# u / sqrt(3) times the RMS of the row's values when W ~ N(0, 1/d) -- so C_ABS = 12u is about
+# 20 standard deviations of that part (a CPU emulation of the kernels' rounding points reaches
+# 0.45 of the bound on 3 million elements), far from a false alarm and still ~40x below the
+# O(rms) error of one wrong element.  Float32 (u = 2^-24) takes the same form with room
+# for the library's sin / cos and accumulation order: C_ABS = 2e-5 (twice the Frobenius bar).
+C_REL = {"bf16": 2.0 ** -8, "f32": 2.0 ** -23}
+C_ABS = {"bf16": 12 * 2.0 ** -9, "f32": 2e-5}
+ROW_FACTOR = 2.0  # per-row relative Frobenius error bar = ROW_FACTOR x the tensor bar
+
+
+def row_rel_errors(got: np.ndarray, ref: np.ndarray) -> float:
+    """Largest relative Frobenius error of one row (a row whose reference is all zero must be
+    reproduced exactly)."""
+    if got.size == 0:
+        return 0.0
+    num = np.linalg.norm(got - ref, axis=1)
+    den = np.linalg.norm(ref, axis=1)
+    zero = den == 0.0
+    rel = np.where(zero, np.where(num == 0.0, 0.0, np.inf), num / np.where(zero, 1.0, den))
+    return float(np.max(rel))
+
+
+def elem_ratio(got: np.ndarray, ref: np.ndarray, dtype: str, scale: str = "row") -> float:
+    """max over elements of |g - o| / (C_REL |o| + C_ABS s), s = the RMS of the element's reference
+    row (scale="row") or of the whole tensor ("tensor"); <= 1 passes."""
+    if got.size == 0:
+        return 0.0
+    err = np.abs(got - ref)
+    if scale == "row":
+        s = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
+    else:
+        s = np.sqrt(np.mean(ref * ref))
+    bound = C_REL[dtype] * np.abs(ref) + C_ABS[dtype] * s
+    ratio = np.where(bound > 0.0, err / np.where(bound > 0.0, bound, 1.0), np.where(err == 0.0, 0.0, np.inf))
+    return float(np.max(ratio))
+
+
 def forward_errors(w, got: np.ndarray, ref: np.ndarray):
-    """Relative Frobenius error of the whole output and of each of the q, k, v blocks."""
+    """Relative Frobenius error of the whole output and of each of the q, k, v blocks, plus the
+    worst row ("row": relative Frobenius error of one row) and the worst element ("elem": the
+    ratio to the per-element bound)."""
     errs = {"out": o.rel_frobenius(got, ref)}
     for name, t in (("q", wl.TARGET_Q), ("k", wl.TARGET_K), ("v", wl.TARGET_V)):
         lo, hi = w.target_columns()[t]
         errs[name] = o.rel_frobenius(got[:, lo:hi], ref[:, lo:hi])
+    errs["row"] = row_rel_errors(got, ref)
+    errs["elem"] = elem_ratio(got, ref, w.dtype)
     return errs
+
+
+def assert_parity(errs, dtype: str, what=""):
+    """Frobenius errors against the dtype's bar, per-row errors ("...row") against ROW_FACTOR
+    times it, per-element ratios ("...elem") against 1."""
+    for k, v in errs.items():
+        bar = 1.0 if k.endswith("elem") else (ROW_FACTOR * TOL[dtype] if k.endswith("row") else TOL[dtype])
+        assert v <= bar, (what, k, v, bar, errs)
 
 
 def sample_rows(T: int, n: int, seed: int = 0) -> np.ndarray:

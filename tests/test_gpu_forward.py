@@ -8,7 +8,7 @@ times."""
 import numpy as np
 import pytest
 
-from helpers import TOL, forward_errors, log, oracle_forward, sample_rows, to_np
+from helpers import TOL, assert_parity, forward_errors, log, oracle_forward, sample_rows, to_np
 from layer_rmsnorm_qkv_amd import binding as B
 from layer_rmsnorm_qkv_amd import workloads as wl
 from layer_rmsnorm_qkv_amd.device import DeviceProblem, desc_for
@@ -76,7 +76,7 @@ def test_forward_f32_small(name):
     got, ref, _ = run_case(w, B.LRQ_VARIANT_GENERIC)
     errs = forward_errors(w, got, ref)
     log(f"  errors {errs}")
-    assert max(errs.values()) <= TOL["f32"], errs
+    assert_parity(errs, "f32")
 
 
 @pytest.mark.parametrize("variant", list(VARIANTS))
@@ -86,7 +86,7 @@ def test_forward_bf16_small(name, variant):
     got, ref, _ = run_case(w, VARIANTS[variant])
     errs = forward_errors(w, got, ref)
     log(f"  errors {errs}")
-    assert max(errs.values()) <= TOL["bf16"], errs
+    assert_parity(errs, "bf16")
 
 
 @pytest.mark.parametrize("variant", list(VARIANTS))
@@ -100,7 +100,7 @@ def test_forward_full_size_sampled(name, variant):
     got, ref, _ = run_case(w, VARIANTS[variant], rows=rows)
     errs = forward_errors(w, got, ref)
     log(f"  errors {errs}")
-    assert max(errs.values()) <= TOL["bf16"], errs
+    assert_parity(errs, "bf16")
 
 
 @pytest.mark.parametrize("variant", list(VARIANTS))
@@ -148,7 +148,7 @@ def test_zero_rows_and_extreme_positions():
         torch.cuda.synchronize()
         ref = oracle_forward(w, inp)
         errs = forward_errors(w, got, ref)
-        assert max(errs.values()) <= TOL["bf16"], (variant, errs)
+        assert_parity(errs, "bf16", variant)
         assert np.all(np.isfinite(got))
 
 
@@ -207,7 +207,7 @@ def test_forward_at_size_limits(name, variant):
     got, ref, _ = run_case(w, VARIANTS[variant])
     errs = forward_errors(w, got, ref)
     log(f"  errors {errs}")
-    assert max(errs.values()) <= TOL["bf16"], errs
+    assert_parity(errs, "bf16")
 
 
 def test_forward_f32_largest_head():
@@ -217,7 +217,7 @@ def test_forward_f32_largest_head():
     got, ref, _ = run_case(w, B.LRQ_VARIANT_GENERIC)
     errs = forward_errors(w, got, ref)
     log(f"  errors {errs}")
-    assert max(errs.values()) <= TOL["f32"], errs
+    assert_parity(errs, "f32")
 
 
 @pytest.mark.parametrize("variant", ["tiled", "decode"])
@@ -265,7 +265,7 @@ def test_forward_output_past_2_31_elements():
     torch.cuda.synchronize()
     errs = forward_errors(w, got, oracle_forward(w, inp, rows))
     log(f"  errors {errs}")
-    assert max(errs.values()) <= TOL["bf16"], errs
+    assert_parity(errs, "bf16")
 
 
 @pytest.mark.parametrize("variant", list(VARIANTS))
@@ -287,4 +287,4 @@ def test_forward_negative_positions(variant):
     got = to_np(prob.forward())
     errs = forward_errors(w, got, oracle_forward(w, inp))
     log(f"  errors {errs}")
-    assert max(errs.values()) <= TOL["bf16"], errs
+    assert_parity(errs, "bf16")

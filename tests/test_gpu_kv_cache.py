@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import oracle.lrq_oracle as o
-from helpers import TOL, forward_errors, log, oracle_forward, spec_of, to_np
+from helpers import TOL, assert_parity, forward_errors, log, oracle_forward, spec_of, to_np
 from layer_rmsnorm_qkv_amd import binding as B
 from layer_rmsnorm_qkv_amd import workloads as wl
 from layer_rmsnorm_qkv_amd.device import DeviceProblem, desc_for, torch_dtype
@@ -85,7 +85,7 @@ def test_forward_kv_cache(name):
     got = to_np(out_kv)
     errs = forward_errors(w, got, oracle_forward(w, inp))
     log(f"  errors {errs}")
-    assert max(errs.values()) <= TOL[w.dtype], errs
+    assert_parity(errs, w.dtype)
     ek, ev = o.kv_cache_write(spec_of(w), got, slots, init[0], init[1])
     assert np.array_equal(to_np(kc), ek)
     assert np.array_equal(to_np(vc), ev)
