@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define LRQ_ABI_VERSION 2
+#define LRQ_ABI_VERSION 3
 #define LRQ_MAX_LORA_RANK 64
 
 typedef enum lrq_status {
@@ -174,6 +174,57 @@ lrq_status lrq_backward(const lrq_desc* desc, const void* x, const void* gamma, 
 
 /* Bytes of workspace the call needs (0 if none); 0 for an invalid descriptor. */
 size_t lrq_workspace_size(const lrq_desc* desc, int for_backward);
+
+/* ---- Prepared frozen weights.  In the fine-tuning setting the pages describe, the projection
+ * weights and the norm weight are frozen and only the LoRA factors train ("Liger-Kernel内核级优化：
+ * GPU利用率飙升至90%以上", section on why conventional fine-tuning stalls: W stays fixed, A and B
+ * are learned).  The MFMA families read W in layouts derived from (W, gamma) alone: the forward
+ * multiplies by W' = bf16(W * gamma) [N, d] (gamma scales the K dimension of the product, so it
+ * is folded into the weights), the backward by W^T [d, N].  Without preparation every call
+ * rebuilds them in its workspace; lrq_prepare_weights builds them once into a caller buffer that
+ * later calls reuse for as long as W and gamma stay unchanged.
+ *
+ * Bytes of the prepared buffer for descriptors of this shape and dtype (n_tokens and the LoRA
+ * fields do not matter): the forward layout, plus the backward one when for_backward != 0.
+ * 0 when no family that would run uses one (float32, shapes only the generic family covers),
+ * or for an invalid descriptor. */
+size_t lrq_prepared_size(const lrq_desc* desc, int for_backward);
+
+/* Writes the prepared layouts of (gamma, w_qkv) into `prepared` (device memory, 256-byte
+ * aligned, at least lrq_prepared_size(desc, for_backward) bytes, owned by the caller), enqueued
+ * on `stream`.  A no-op returning LRQ_OK when that size is 0.  INVALID_ARG for an invalid
+ * descriptor, NULL gamma / w_qkv / prepared, or a buffer below the size; UNSUPPORTED for
+ * misaligned pointers. */
+lrq_status lrq_prepare_weights(const lrq_desc* desc, int for_backward, const void* gamma, const void* w_qkv,
+                               void* prepared, size_t prepared_bytes, void* stream);
+
+/* lrq_forward_kv with prepared weights: the same operation and results, bit for bit, as the
+ * call without them (the layouts hold the same values).  prepared == NULL behaves exactly as
+ * lrq_forward_kv; kv may be NULL.  The kernel family chosen for the call reads `prepared` when
+ * it uses a prepared layout (the tiled family) and ignores it otherwise.  It must hold the
+ * output of lrq_prepare_weights for the same shape, gamma and w_qkv (not checked: stale or
+ * foreign contents give wrong results); w_qkv and gamma are still required, since other
+ * families and the adapters' fold read them.  The workspace may be as small as
+ * lrq_workspace_size_prepared(desc, 0).  Adds to lrq_forward_kv's errors: INVALID_ARG when
+ * prepared_bytes is below the layout the family reads; UNSUPPORTED for a prepared pointer that
+ * is not 256-byte aligned. */
+lrq_status lrq_forward_prepared(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,
+                                const void* prepared, size_t prepared_bytes, const void* bias,
+                                const void* const* lora_a, const void* const* lora_b, const int32_t* positions,
+                                void* out, const lrq_kv_cache* kv, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* lrq_backward with prepared weights (prepared with for_backward != 0); same results bit for
+ * bit, same rules as lrq_forward_prepared; the workspace may be as small as
+ * lrq_workspace_size_prepared(desc, 1). */
+lrq_status lrq_backward_prepared(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,
+                                 const void* prepared, size_t prepared_bytes, const void* bias,
+                                 const void* const* lora_a, const void* const* lora_b, const int32_t* positions,
+                                 const void* y, const void* dy, void* dx, float* const* d_lora_a,
+                                 float* const* d_lora_b, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of a call that passes prepared weights (<= lrq_workspace_size). */
+size_t lrq_workspace_size_prepared(const lrq_desc* desc, int for_backward);
 
 /* The kernel family lrq_forward (for_backward = 0) or lrq_backward (1) would run for this
  * descriptor (an lrq_variant value), or -1 when the descriptor is invalid or the forced

@@ -23,7 +23,8 @@ VARIANT_NAMES = {LRQ_VARIANT_GENERIC: "generic", LRQ_VARIANT_TILED: "tiled", LRQ
 # every symbol include/lrq.h declares
 EXPORTED = ("lrq_forward", "lrq_forward_kv", "lrq_backward", "lrq_workspace_size", "lrq_select_variant",
             "lrq_status_string", "lrq_last_error", "lrq_abi_version", "lrq_kernel_timing",
-            "lrq_kernel_time_ms")
+            "lrq_kernel_time_ms", "lrq_prepared_size", "lrq_prepare_weights", "lrq_forward_prepared",
+            "lrq_backward_prepared", "lrq_workspace_size_prepared")
 
 
 class LrqDesc(ctypes.Structure):
@@ -76,6 +77,18 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.lrq_backward.restype = ctypes.c_int
         lib.lrq_workspace_size.argtypes = [ctypes.POINTER(LrqDesc), ctypes.c_int]
         lib.lrq_workspace_size.restype = ctypes.c_size_t
+        lib.lrq_workspace_size_prepared.argtypes = [ctypes.POINTER(LrqDesc), ctypes.c_int]
+        lib.lrq_workspace_size_prepared.restype = ctypes.c_size_t
+        lib.lrq_prepared_size.argtypes = [ctypes.POINTER(LrqDesc), ctypes.c_int]
+        lib.lrq_prepared_size.restype = ctypes.c_size_t
+        lib.lrq_prepare_weights.argtypes = [ctypes.POINTER(LrqDesc), ctypes.c_int, P, P, P, S, P]
+        lib.lrq_prepare_weights.restype = ctypes.c_int
+        lib.lrq_forward_prepared.argtypes = [ctypes.POINTER(LrqDesc), P, P, P, P, S, P, PP, PP, P, P,
+                                             ctypes.POINTER(LrqKvCache), P, S, P]
+        lib.lrq_forward_prepared.restype = ctypes.c_int
+        lib.lrq_backward_prepared.argtypes = [ctypes.POINTER(LrqDesc), P, P, P, P, S, P, PP, PP, P, P, P, P, PP,
+                                              PP, P, S, P]
+        lib.lrq_backward_prepared.restype = ctypes.c_int
         lib.lrq_select_variant.argtypes = [ctypes.POINTER(LrqDesc), ctypes.c_int]
         lib.lrq_select_variant.restype = ctypes.c_int
         lib.lrq_status_string.argtypes = [ctypes.c_int]
@@ -169,6 +182,48 @@ def lrq_backward(desc: LrqDesc, x, gamma, w_qkv, bias, lora_a, lora_b, positions
                           _ptr3(lora_a), _ptr3(lora_b), _ptr(positions), _ptr(y), _ptr(dy), _ptr(dx),
                           _ptr3(d_lora_a), _ptr3(d_lora_b), _ptr(workspace), int(workspace_bytes),
                           _stream(stream, (x, dx)))
+    _check(st)
+
+
+def lrq_prepared_size(desc: LrqDesc, for_backward: bool = False) -> int:
+    return int(load().lrq_prepared_size(ctypes.byref(desc), int(bool(for_backward))))
+
+
+def lrq_workspace_size_prepared(desc: LrqDesc, for_backward: bool = False) -> int:
+    return int(load().lrq_workspace_size_prepared(ctypes.byref(desc), int(bool(for_backward))))
+
+
+def lrq_prepare_weights(desc: LrqDesc, for_backward: bool, gamma, w_qkv, prepared,
+                        prepared_bytes: Optional[int] = None, stream=None) -> None:
+    lib = load()
+    nbytes = _ws_bytes(prepared, prepared_bytes)
+    _check(lib.lrq_prepare_weights(ctypes.byref(desc), int(bool(for_backward)), _ptr(gamma), _ptr(w_qkv),
+                                   _ptr(prepared), int(nbytes), _stream(stream, (w_qkv,))))
+
+
+def lrq_forward_prepared(desc: LrqDesc, x, gamma, w_qkv, prepared, bias, lora_a, lora_b, positions, out,
+                         kv: Optional[tuple] = None, workspace=None, workspace_bytes: Optional[int] = None,
+                         prepared_bytes: Optional[int] = None, stream=None) -> None:
+    """kv: None or (k_cache, v_cache, slots, num_slots)."""
+    lib = load()
+    kvs = None if kv is None else LrqKvCache(_ptr(kv[0]), _ptr(kv[1]), _ptr(kv[2]), int(kv[3]))
+    st = lib.lrq_forward_prepared(ctypes.byref(desc), _ptr(x), _ptr(gamma), _ptr(w_qkv), _ptr(prepared),
+                                  int(_ws_bytes(prepared, prepared_bytes)), _ptr(bias), _ptr3(lora_a),
+                                  _ptr3(lora_b), _ptr(positions), _ptr(out),
+                                  ctypes.byref(kvs) if kvs is not None else None, _ptr(workspace),
+                                  int(_ws_bytes(workspace, workspace_bytes)), _stream(stream, (x, out)))
+    _check(st)
+
+
+def lrq_backward_prepared(desc: LrqDesc, x, gamma, w_qkv, prepared, bias, lora_a, lora_b, positions, y, dy, dx,
+                          d_lora_a, d_lora_b, workspace=None, workspace_bytes: Optional[int] = None,
+                          prepared_bytes: Optional[int] = None, stream=None) -> None:
+    lib = load()
+    st = lib.lrq_backward_prepared(ctypes.byref(desc), _ptr(x), _ptr(gamma), _ptr(w_qkv), _ptr(prepared),
+                                   int(_ws_bytes(prepared, prepared_bytes)), _ptr(bias), _ptr3(lora_a),
+                                   _ptr3(lora_b), _ptr(positions), _ptr(y), _ptr(dy), _ptr(dx), _ptr3(d_lora_a),
+                                   _ptr3(d_lora_b), _ptr(workspace), int(_ws_bytes(workspace, workspace_bytes)),
+                                   _stream(stream, (x, dx)))
     _check(st)
 
 

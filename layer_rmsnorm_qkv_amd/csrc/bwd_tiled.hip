@@ -14,12 +14,13 @@
 // the rotated W_eff h), so the RMSNorm backward needs no second pass over dh.
 //
 // Kernels, in launch order (all on the caller's stream):
-//   prep_weights  WT = [W^T | A_q^T | A_k^T | A_v^T | 0] [d][K] with K = N + (sum r rounded
-//                 up to 64), B_t^T [r][N_t] and A'_t = bf16(A_t * gamma) [r][d]
+//   prep_weights  WT = W^T [d][N] (unless the call brings it prepared), AT = [A_q^T | A_k^T |
+//                 A_v^T | 0] [d][Rp] with Rp = sum r rounded up to 64, B_t^T [r][N_t] and
+//                 A'_t = bf16(A_t * gamma) [r][d]
 //   rows          per token: inv, m, G (bf16) into Gcat[:, 0:N)
 //   rank (V)      V'_t = bf16(s G_t B_t) into Gcat[:, N + off_t ...) (+ zero padding)
 //   rank (U)      U_t = bf16(inv * x A'_t^T) into U[T][R]
-//   main          dh = Gcat WT^T over K (shared tile pipeline), epilogue dx
+//   main          dh = Gcat [WT | AT]^T over K = N + Rp (shared tile pipeline), epilogue dx
 //   lora_partial  per chunk of tokens: sum V'^T h (all targets) and G_t^T U_t (MFMA)
 //   lora_reduce   dA_t, dB_t = sums over chunks (deterministic order), dB scaled by s
 // h and U are recomputed from x; G and V' live only in the workspace of this call.
@@ -46,7 +47,7 @@ struct BwdLayout {
   int groups[4];  // work groups per LoRA-gradient job (dA, then each target's dB)
   int chunk;    // tokens per partial sum (multiple of 16)
   int chunks;   // token chunks of the LoRA-gradient partial sums
-  size_t wt, bt[3], ap_all, ap[3], gcat, u, inv, m, pda, pdb[3], total;
+  size_t wt, at, bt[3], ap_all, ap[3], gcat, u, inv, m, pda, pdb[3], total;
 };
 
 size_t al256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
@@ -83,7 +84,8 @@ BwdLayout bwd_layout(const FwdParams& p) {
     o += al256(bytes);
     return at;
   };
-  L.wt = take(static_cast<size_t>(p.d) * L.K * 2);
+  L.wt = take(p.use_prepared ? 0 : static_cast<size_t>(p.d) * p.N * 2);
+  L.at = take(static_cast<size_t>(p.d) * L.Rp * 2);
   for (int t = 0; t < 3; ++t) {
     int lo, hi;
     target_cols(p, t, lo, hi);
@@ -113,19 +115,22 @@ T* at(void* base, size_t off) {
 }
 
 // ---------------------------------------------------------------- prep_weights
-// WT[j][n] = W[n][j] (n < N), WT[j][N + off_t + k] = A_t[k][j] (k < r), WT[j][N + R ..) = 0;
+// WT[j][n] = W[n][j] (n < N), AT[j][off_t + k] = A_t[k][j] (k < r), AT[j][R ..) = 0;
 // BT_t[k][n] = B_t[n][k]; AP_t[k][j] = bf16(A_t[k][j] * gamma[j]).
-// 64 x 64 tiles of the [N + Rp, d] source through LDS; the small B^T / A' products are
-// done by the blocks past the WT grid.
+// 64 x 64 tiles of the source rows [q_begin, N + Rp) -- W rows, then the targets' A rows,
+// then zeros -- through LDS; the small B^T / A' products are done by the blocks past the
+// transpose grid.
 struct PrepArgs {
   const uint16_t* w;
   const uint16_t* a[3];
   const uint16_t* b[3];
   const uint16_t* gamma;
-  uint16_t* wt;
+  uint16_t* wt;  // [d][N], written for source rows < N
+  uint16_t* at;  // [d][Rp], written for source rows >= N
   uint16_t* bt[3];
   uint16_t* ap[3];
-  int N, d, r, K, R;
+  int N, d, r, Rp, R;
+  int q_begin;   // first source row (0, or N when W^T is not transposed)
   int off[3], lo[3], nt[3];  // per target: LoRA column offset, first output column, width
   uint32_t targets;
   int wt_blocks;  // blocks of the transpose part
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(256) void prep_weights_kernel(PrepArgs a) {
     // 16-byte vectors (8 columns of a source row in, 8 rows of a destination row out)
     const int jb = a.d / 64;
     const int kb = static_cast<int>(blockIdx.x) / jb, cb = static_cast<int>(blockIdx.x) % jb;
-    const int q0 = kb * 64, j0 = cb * 64;
+    const int q0 = a.q_begin + kb * 64, j0 = cb * 64;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int c = tid + 256 * h;
@@ -162,6 +167,9 @@ __global__ __launch_bounds__(256) void prep_weights_kernel(PrepArgs a) {
       *reinterpret_cast<uint4*>(&ts(qi, jc)) = v;
     }
     __syncthreads();
+    // N is a multiple of 64, so a block lies wholly in W^T or wholly in A^T
+    uint16_t* dst = q0 < a.N ? a.wt + q0 : a.at + (q0 - a.N);
+    const int64_t ldd = q0 < a.N ? a.N : a.Rp;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int c = tid + 256 * h;
@@ -170,7 +178,7 @@ __global__ __launch_bounds__(256) void prep_weights_kernel(PrepArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         w[e] = static_cast<uint32_t>(ts(qc + 2 * e, ji)) | (static_cast<uint32_t>(ts(qc + 2 * e + 1, ji)) << 16);
-      *reinterpret_cast<uint4*>(a.wt + static_cast<int64_t>(j0 + ji) * a.K + q0 + qc) = uint4{w[0], w[1], w[2], w[3]};
+      *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(j0 + ji) * ldd + qc) = uint4{w[0], w[1], w[2], w[3]};
     }
     return;
   }
@@ -339,7 +347,9 @@ __global__ __launch_bounds__(kThreads, 1) void rank_kernel(RankArgs a) {
 // ---------------------------------------------------------------- main: dh and dx
 struct MainArgs {
   const uint16_t* gcat;  // [T][K]
-  const uint16_t* wt;    // [d][K]
+  const uint16_t* wt;    // [d][N]
+  const uint16_t* at;    // [d][Rp]
+  int N, Rp;
   const uint16_t* x;
   const uint16_t* gamma;
   const float* inv;
@@ -372,7 +382,7 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_main_kernel(MainArgs a) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) ta.acc[i][j] = floatx16{};
-  const Src8 src = make_src8(a.gcat, a.K, row0, a.T, a.wt, a.K, wave, lane);
+  const Src8 src = make_src8(a.gcat, a.K, row0, a.T, a.wt, a.N, a.N / BK, a.at, a.Rp, wave, lane);
   kloop8(smem, ta, src, col0, static_cast<int>(a.K / BK), wave, lane);
 
   // epilogue: dx = inv * gamma * dh - m * x for the lane's rows and columns
@@ -661,6 +671,22 @@ bool bwd_tiled_supports(const FwdParams& p) {
 
 size_t bwd_tiled_workspace_bytes(const FwdParams& p) { return bwd_layout(p).total; }
 
+// Prepared backward weights: W^T [d][N] bf16.
+size_t bwd_tiled_prepared_bytes(const FwdParams& p) { return al256(static_cast<size_t>(p.d) * p.N * 2); }
+
+hipError_t prepare_bwd_tiled(const FwdParams& p, void* dst, hipStream_t s) {
+  PrepArgs pa{};
+  pa.w = static_cast<const uint16_t*>(p.w);
+  pa.wt = static_cast<uint16_t*>(dst);
+  pa.N = p.N;
+  pa.d = static_cast<int>(p.d);
+  pa.q_begin = 0;
+  pa.targets = 0;
+  pa.wt_blocks = (p.N / 64) * static_cast<int>(p.d / 64);
+  hipLaunchKernelGGL(prep_weights_kernel, dim3(pa.wt_blocks), dim3(256), 0, s, pa);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
   const FwdParams& p = bp.f;
   const BwdLayout L = bwd_layout(p);
@@ -680,6 +706,7 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
     pa.w = static_cast<const uint16_t*>(p.w);
     pa.gamma = static_cast<const uint16_t*>(p.gamma);
     pa.wt = at<uint16_t>(ws, L.wt);
+    pa.at = at<uint16_t>(ws, L.at);
     for (int t = 0; t < 3; ++t) {
       pa.a[t] = static_cast<const uint16_t*>(p.a[t]);
       pa.b[t] = static_cast<const uint16_t*>(p.b[t]);
@@ -692,11 +719,13 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
     pa.N = p.N;
     pa.d = static_cast<int>(p.d);
     pa.r = p.r;
-    pa.K = static_cast<int>(L.K);
+    pa.Rp = L.Rp;
     pa.R = L.R;
+    pa.q_begin = p.use_prepared ? p.N : 0;
     pa.targets = p.targets;
-    pa.wt_blocks = static_cast<int>(L.K / 64) * static_cast<int>(p.d / 64);
-    hipLaunchKernelGGL(prep_weights_kernel, dim3(pa.wt_blocks + (lora ? 256 : 0)), dim3(256), 0, s, pa);
+    pa.wt_blocks = static_cast<int>((L.K - pa.q_begin) / 64) * static_cast<int>(p.d / 64);
+    if (pa.wt_blocks + (lora ? 256 : 0) > 0)
+      hipLaunchKernelGGL(prep_weights_kernel, dim3(pa.wt_blocks + (lora ? 256 : 0)), dim3(256), 0, s, pa);
 
     // ---- rows
     RowsArgs ra{};
@@ -768,7 +797,10 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
     // ---- dh and dx
     MainArgs ma{};
     ma.gcat = at<uint16_t>(ws, L.gcat);
-    ma.wt = at<uint16_t>(ws, L.wt);
+    ma.wt = p.use_prepared ? static_cast<const uint16_t*>(p.prepared) : at<uint16_t>(ws, L.wt);
+    ma.at = at<uint16_t>(ws, L.at);
+    ma.N = p.N;
+    ma.Rp = L.Rp;
     ma.x = static_cast<const uint16_t*>(p.x);
     ma.gamma = static_cast<const uint16_t*>(p.gamma);
     ma.inv = at<float>(ws, L.inv);

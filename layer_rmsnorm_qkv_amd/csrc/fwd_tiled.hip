@@ -264,8 +264,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiled_kernel(TiledArgs p) {
 }
 
 // W' = bf16(W * gamma) and A'_t = bf16(A_t * gamma): rows [0, N) of the destination
-// come from W, then r rows per target from A_q, A_k, A_v (targets only).  Each thread
-// scales 8 consecutive elements of one row (d % 8 == 0).
+// come from W (N = 0: W is not folded), then r rows per target from A_q, A_k, A_v (targets
+// only).  Each thread scales 8 consecutive elements of one row (d % 8 == 0).
 struct FoldArgs {
   const uint16_t* w;
   const uint16_t* a[3];
@@ -329,39 +329,68 @@ int n_targets(const FwdParams& p) { return (p.targets & 1u) + ((p.targets >> 1) 
 size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 }  // namespace
 
-// W' then A'_t for every target, bf16, d elements per row.
+// Workspace: W' (unless the call brings prepared weights) then A'_t for every target, bf16,
+// d elements per row.
 size_t tiled_workspace_bytes(const FwdParams& p) {
-  return align256(static_cast<size_t>(p.N + n_targets(p) * p.r) * static_cast<size_t>(p.d) * 2);
+  const int64_t w_rows = p.use_prepared ? 0 : p.N;
+  return align256(static_cast<size_t>(w_rows + n_targets(p) * p.r) * static_cast<size_t>(p.d) * 2);
+}
+
+// Prepared forward weights: W' = bf16(W * gamma) [N][d], first in the prepared buffer.
+size_t tiled_prepared_bytes(const FwdParams& p) { return align256(static_cast<size_t>(p.N) * p.d * 2); }
+
+namespace {
+void launch_fold(const uint16_t* w, int w_rows, const uint16_t* const a[3], int na, const int slot_t[3], int r,
+                 const uint16_t* gamma, uint16_t* dst, int64_t d, hipStream_t s) {
+  FoldArgs f;
+  f.w = w;
+  f.gamma = gamma;
+  f.dst = dst;
+  f.N = w_rows;
+  f.r = r;
+  f.d = static_cast<int>(d);
+  for (int t = 0; t < 3; ++t) {
+    f.a[t] = a[t];
+    f.slot_t[t] = slot_t[t];
+  }
+  f.rows = static_cast<int64_t>(w_rows) + static_cast<int64_t>(na) * r;
+  const int64_t chunks = f.rows * (d / 8);
+  if (chunks == 0) return;
+  const int fold_blocks = static_cast<int>(std::min<int64_t>((chunks + 255) / 256, 8 * 1024));
+  hipLaunchKernelGGL(fold_gamma_kernel, dim3(fold_blocks), dim3(256), 0, s, f);
+}
+}  // namespace
+
+hipError_t prepare_fwd_tiled(const FwdParams& p, void* prepared, hipStream_t s) {
+  const uint16_t* none[3] = {nullptr, nullptr, nullptr};
+  const int slot_t[3] = {0, 0, 0};
+  launch_fold(static_cast<const uint16_t*>(p.w), p.N, none, 0, slot_t, 0, static_cast<const uint16_t*>(p.gamma),
+              static_cast<uint16_t*>(prepared), p.d, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_fwd_tiled(const FwdParams& p, hipStream_t s) {
   uint16_t* ws = static_cast<uint16_t*>(p.ws);
-  FoldArgs f;
-  f.w = static_cast<const uint16_t*>(p.w);
-  f.gamma = static_cast<const uint16_t*>(p.gamma);
-  f.dst = ws;
-  f.N = p.N;
-  f.r = p.r;
-  f.d = static_cast<int>(p.d);
+  // W' comes prepared, or is folded into the workspace ahead of the A'_t rows
+  const int w_rows = p.use_prepared ? 0 : p.N;
+  const uint16_t* srcs[3];
+  int slot_t[3] = {0, 0, 0};
   int slots = 0;
   TiledArgs a;
   for (int t = 0; t < 3; ++t) {
-    f.a[t] = static_cast<const uint16_t*>(p.a[t]);
-    f.slot_t[t] = 0;
+    srcs[t] = static_cast<const uint16_t*>(p.a[t]);
     a.ag[t] = nullptr;
     a.b[t] = static_cast<const uint16_t*>(p.b[t]);
     if (p.targets & (1u << t)) {
-      a.ag[t] = ws + (static_cast<int64_t>(p.N) + static_cast<int64_t>(slots) * p.r) * p.d;
-      f.slot_t[slots++] = t;
+      a.ag[t] = ws + (static_cast<int64_t>(w_rows) + static_cast<int64_t>(slots) * p.r) * p.d;
+      slot_t[slots++] = t;
     }
   }
-  f.rows = static_cast<int64_t>(p.N) + static_cast<int64_t>(slots) * p.r;
-  const int64_t chunks = f.rows * (p.d / 8);
-  const int fold_blocks = static_cast<int>(std::min<int64_t>((chunks + 255) / 256, 8 * 1024));
-  hipLaunchKernelGGL(fold_gamma_kernel, dim3(fold_blocks), dim3(256), 0, s, f);
+  launch_fold(static_cast<const uint16_t*>(p.w), w_rows, srcs, slots, slot_t, p.r,
+              static_cast<const uint16_t*>(p.gamma), ws, p.d, s);
 
   a.x = static_cast<const uint16_t*>(p.x);
-  a.wg = ws;
+  a.wg = p.use_prepared ? static_cast<const uint16_t*>(p.prepared) : ws;
   a.bias = p.has_bias ? static_cast<const uint16_t*>(p.bias) : nullptr;
   a.pos = p.pos;
   a.out = static_cast<uint16_t*>(p.out);

@@ -17,6 +17,10 @@ bool bwd_tiled_supports(const FwdParams& p);
 size_t tiled_workspace_bytes(const FwdParams& p);
 size_t decode_workspace_bytes(const FwdParams& p);
 size_t bwd_tiled_workspace_bytes(const FwdParams& p);
+size_t tiled_prepared_bytes(const FwdParams& p);
+size_t bwd_tiled_prepared_bytes(const FwdParams& p);
+hipError_t prepare_fwd_tiled(const FwdParams& p, void* dst, hipStream_t s);
+hipError_t prepare_bwd_tiled(const FwdParams& p, void* dst, hipStream_t s);
 hipError_t launch_fwd_tiled(const FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_decode(const FwdParams& p, hipStream_t s);
 hipError_t launch_bwd_tiled(const BwdParams& p, hipStream_t s);
@@ -167,6 +171,24 @@ int select(const lrq_desc* d, const lrq::FwdParams& p, bool backward) {
   return -1;
 }
 
+// Prepared-weight buffer: the tiled forward's W' first (when that family covers the shape),
+// then, for a backward preparation, the tiled backward's W^T.  Independent of T.
+struct PrepLayout {
+  size_t fwd_off, fwd_bytes, bwd_off, bwd_bytes, total;
+};
+
+PrepLayout prep_layout(const lrq_desc* d, const lrq::FwdParams& p, bool for_backward) {
+  PrepLayout L{};
+  if (d->dtype != LRQ_BF16) return L;
+  lrq::FwdParams q = p;
+  q.T = 0;
+  if (lrq::tiled_supports(q)) L.fwd_bytes = lrq::tiled_prepared_bytes(q);
+  L.bwd_off = L.fwd_bytes;
+  if (for_backward && lrq::bwd_tiled_supports(q)) L.bwd_bytes = lrq::bwd_tiled_prepared_bytes(q);
+  L.total = L.bwd_off + L.bwd_bytes;
+  return L;
+}
+
 size_t workspace_for(int variant, const lrq::FwdParams& p, bool backward) {
   if (backward) return variant == LRQ_VARIANT_TILED ? lrq::bwd_tiled_workspace_bytes(p) : 0;
   if (variant == LRQ_VARIANT_TILED) return lrq::tiled_workspace_bytes(p);
@@ -237,15 +259,56 @@ size_t lrq_workspace_size(const lrq_desc* desc, int for_backward) {
   return workspace_for(v, p, for_backward != 0);
 }
 
-lrq_status lrq_forward_kv(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,
-                          const void* bias, const void* const* lora_a, const void* const* lora_b,
-                          const int32_t* positions, void* out, const lrq_kv_cache* kv, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+size_t lrq_prepared_size(const lrq_desc* desc, int for_backward) {
+  lrq::FwdParams p;
+  if (check_desc(desc, p) != LRQ_OK) return 0;
+  return prep_layout(desc, p, for_backward != 0).total;
+}
+
+size_t lrq_workspace_size_prepared(const lrq_desc* desc, int for_backward) {
+  lrq::FwdParams p;
+  if (check_desc(desc, p) != LRQ_OK) return 0;
+  const int v = select(desc, p, for_backward != 0);
+  if (v < 0) return 0;
+  const PrepLayout L = prep_layout(desc, p, for_backward != 0);
+  p.use_prepared = v == LRQ_VARIANT_TILED && (for_backward ? L.bwd_bytes : L.fwd_bytes) > 0;
+  return workspace_for(v, p, for_backward != 0);
+}
+
+lrq_status lrq_prepare_weights(const lrq_desc* desc, int for_backward, const void* gamma, const void* w_qkv,
+                               void* prepared, size_t prepared_bytes, void* stream) {
+  lrq::FwdParams p;
+  lrq_status st = check_desc(desc, p);
+  if (st != LRQ_OK) return st;
+  const PrepLayout L = prep_layout(desc, p, for_backward != 0);
+  if (L.total == 0) return ok();
+  if (!gamma || !w_qkv) return fail(LRQ_ERR_INVALID_ARG, "gamma and w_qkv are required");
+  if (!prepared) return fail(LRQ_ERR_INVALID_ARG, "prepared is NULL");
+  if (prepared_bytes < L.total)
+    return fail(LRQ_ERR_INVALID_ARG, "prepared buffer too small: %zu < %zu", prepared_bytes, L.total);
+  if (!aligned16(gamma) || !aligned16(w_qkv)) return fail(LRQ_ERR_UNSUPPORTED, "array pointers must be 16-byte aligned");
+  if (!aligned256(prepared)) return fail(LRQ_ERR_UNSUPPORTED, "prepared must be 256-byte aligned");
+  p.gamma = gamma;
+  p.w = w_qkv;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char* base = static_cast<unsigned char*>(prepared);
+  hipError_t e = hipSuccess;
+  if (L.fwd_bytes) e = lrq::prepare_fwd_tiled(p, base + L.fwd_off, s);
+  if (e == hipSuccess && L.bwd_bytes) e = lrq::prepare_bwd_tiled(p, base + L.bwd_off, s);
+  return hip_status(e, "weight preparation");
+}
+
+lrq_status lrq_forward_prepared(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,
+                                const void* prepared, size_t prepared_bytes, const void* bias,
+                                const void* const* lora_a, const void* const* lora_b, const int32_t* positions,
+                                void* out, const lrq_kv_cache* kv, void* workspace, size_t workspace_bytes,
+                                void* stream) {
   lrq::FwdParams p;
   lrq_status st = check_desc(desc, p);
   if (st != LRQ_OK) return st;
   st = check_common_ptrs(desc, p, x, gamma, w_qkv, bias, lora_a, lora_b, positions);
   if (st != LRQ_OK) return st;
+  if (prepared && !aligned256(prepared)) return fail(LRQ_ERR_UNSUPPORTED, "prepared must be 256-byte aligned");
   if (p.T > 0 && !out) return fail(LRQ_ERR_INVALID_ARG, "out is NULL");
   if (out && !aligned16(out)) return fail(LRQ_ERR_UNSUPPORTED, "out must be 16-byte aligned");
   if (kv) {
@@ -258,6 +321,16 @@ lrq_status lrq_forward_kv(const lrq_desc* desc, const void* x, const void* gamma
   }
   const int v = select(desc, p, false);
   if (v < 0) return LRQ_ERR_UNSUPPORTED;
+  if (prepared && v == LRQ_VARIANT_TILED) {
+    const PrepLayout L = prep_layout(desc, p, false);
+    if (L.fwd_bytes) {
+      if (prepared_bytes < L.fwd_off + L.fwd_bytes)
+        return fail(LRQ_ERR_INVALID_ARG, "prepared buffer too small: %zu < %zu", prepared_bytes,
+                    L.fwd_off + L.fwd_bytes);
+      p.prepared = static_cast<const unsigned char*>(prepared) + L.fwd_off;
+      p.use_prepared = true;
+    }
+  }
   const size_t need = workspace_for(v, p, false);
   if (workspace_bytes < need) return fail(LRQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", workspace_bytes, need);
   if (need > 0 && !workspace) return fail(LRQ_ERR_INVALID_ARG, "workspace is NULL");
@@ -286,25 +359,34 @@ lrq_status lrq_forward_kv(const lrq_desc* desc, const void* x, const void* gamma
   return hip_status(e, "forward launch");
 }
 
+lrq_status lrq_forward_kv(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,
+                          const void* bias, const void* const* lora_a, const void* const* lora_b,
+                          const int32_t* positions, void* out, const lrq_kv_cache* kv, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return lrq_forward_prepared(desc, x, gamma, w_qkv, nullptr, 0, bias, lora_a, lora_b, positions, out, kv,
+                              workspace, workspace_bytes, stream);
+}
+
 lrq_status lrq_forward(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,
                        const void* bias, const void* const* lora_a, const void* const* lora_b,
                        const int32_t* positions, void* out, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  return lrq_forward_kv(desc, x, gamma, w_qkv, bias, lora_a, lora_b, positions, out, nullptr, workspace,
-                        workspace_bytes, stream);
+  return lrq_forward_prepared(desc, x, gamma, w_qkv, nullptr, 0, bias, lora_a, lora_b, positions, out, nullptr,
+                              workspace, workspace_bytes, stream);
 }
 
-lrq_status lrq_backward(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,
-                        const void* bias, const void* const* lora_a, const void* const* lora_b,
-                        const int32_t* positions, const void* y, const void* dy, void* dx,
-                        float* const* d_lora_a, float* const* d_lora_b, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+lrq_status lrq_backward_prepared(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,
+                                 const void* prepared, size_t prepared_bytes, const void* bias,
+                                 const void* const* lora_a, const void* const* lora_b, const int32_t* positions,
+                                 const void* y, const void* dy, void* dx, float* const* d_lora_a,
+                                 float* const* d_lora_b, void* workspace, size_t workspace_bytes, void* stream) {
   lrq::BwdParams bp;
   std::memset(&bp, 0, sizeof bp);
   lrq_status st = check_desc(desc, bp.f);
   if (st != LRQ_OK) return st;
   st = check_common_ptrs(desc, bp.f, x, gamma, w_qkv, bias, lora_a, lora_b, positions);
   if (st != LRQ_OK) return st;
+  if (prepared && !aligned256(prepared)) return fail(LRQ_ERR_UNSUPPORTED, "prepared must be 256-byte aligned");
   if (bp.f.T > 0 && (!y || !dy || !dx)) return fail(LRQ_ERR_INVALID_ARG, "y, dy and dx are required");
   for (const void* q : {y, dy, static_cast<const void*>(dx)})
     if (q && !aligned16(q)) return fail(LRQ_ERR_UNSUPPORTED, "y, dy, dx must be 16-byte aligned");
@@ -319,6 +401,16 @@ lrq_status lrq_backward(const lrq_desc* desc, const void* x, const void* gamma, 
   }
   const int v = select(desc, bp.f, true);
   if (v < 0) return LRQ_ERR_UNSUPPORTED;
+  if (prepared && v == LRQ_VARIANT_TILED) {
+    const PrepLayout L = prep_layout(desc, bp.f, true);
+    if (L.bwd_bytes) {
+      if (prepared_bytes < L.bwd_off + L.bwd_bytes)
+        return fail(LRQ_ERR_INVALID_ARG, "prepared buffer too small for the backward: %zu < %zu", prepared_bytes,
+                    L.bwd_off + L.bwd_bytes);
+      bp.f.prepared = static_cast<const unsigned char*>(prepared) + L.bwd_off;
+      bp.f.use_prepared = true;
+    }
+  }
   const size_t need = workspace_for(v, bp.f, true);
   if (workspace_bytes < need) return fail(LRQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", workspace_bytes, need);
   if (need > 0 && !workspace) return fail(LRQ_ERR_INVALID_ARG, "workspace is NULL");
@@ -337,6 +429,15 @@ lrq_status lrq_backward(const lrq_desc* desc, const void* x, const void* gamma, 
   else
     e = desc->dtype == LRQ_F32 ? lrq::launch_bwd_generic_f32(bp, s) : lrq::launch_bwd_generic_bf16(bp, s);
   return hip_status(e, "backward launch");
+}
+
+lrq_status lrq_backward(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,
+                        const void* bias, const void* const* lora_a, const void* const* lora_b,
+                        const int32_t* positions, const void* y, const void* dy, void* dx,
+                        float* const* d_lora_a, float* const* d_lora_b, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return lrq_backward_prepared(desc, x, gamma, w_qkv, nullptr, 0, bias, lora_a, lora_b, positions, y, dy, dx,
+                               d_lora_a, d_lora_b, workspace, workspace_bytes, stream);
 }
 
 lrq_status lrq_kernel_timing(int enable) {

@@ -32,6 +32,8 @@ struct FwdParams {
   const void* b[3];
   const int32_t* pos;
   void* out;
+  const void* prepared;     // frozen-weight layout of this call's family, or nullptr
+  bool use_prepared;        // sizes and launches assume `prepared` (set with it)
   void* ws;
   size_t ws_bytes;
   int esize;                // bytes per element of the call's dtype

@@ -312,10 +312,18 @@ struct Src8 {
   const uint16_t* a[4];  // A rows; rows past the panel's end re-read its last row
   const uint16_t* b[4];  // B rows of column tile 0
   int64_t ldb;
+  // K steps >= nk1 read B from a second matrix `tail` (row stride ld_tail) at K offset
+  // 64 (ks - nk1); its per-lane pointers are formed in those steps only
+  const uint16_t* tail;
+  int64_t ld_tail;
+  int nk1;
+  int lc[4];  // logical 16-byte chunk of each instruction's row
 };
 
+// B = [B1 | B2]: K steps [0, nk1) from B1 (stride ldb), the rest from B2 (stride ld2).
 __device__ __forceinline__ Src8 make_src8(const uint16_t* A, int64_t lda, int64_t row0, int64_t rows_valid,
-                                          const uint16_t* B, int64_t ldb, int wave, int lane) {
+                                          const uint16_t* B, int64_t ldb, int nk1, const uint16_t* B2,
+                                          int64_t ld2, int wave, int lane) {
   Src8 s;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -323,8 +331,12 @@ __device__ __forceinline__ Src8 make_src8(const uint16_t* A, int64_t lda, int64_
     const int lc = (lane & 7) ^ chunk_xor(R);
     s.a[c] = A + min(row0 + R, rows_valid - 1) * lda + lc * 8;
     s.b[c] = B + static_cast<int64_t>(R) * ldb + lc * 8;
+    s.lc[c] = lc;
   }
   s.ldb = ldb;
+  s.tail = B2;
+  s.ld_tail = ld2;
+  s.nk1 = nk1;
   return s;
 }
 
@@ -335,7 +347,8 @@ __device__ __forceinline__ void fenced_barrier() {
   sched_fence();
 }
 
-// kloop with 8 wavefronts: acc = A_panel B_tile^T, B_tile = B rows [col0, col0 + 256).
+// kloop with 8 wavefronts: acc = A_panel B_tile^T, B_tile = B rows [col0, col0 + 256) (B as
+// set up by make_src8: two matrices side by side along K).
 // Called by all 8 wavefronts; leaves the stage ring free.
 //
 // Step ks is two intervals between workgroup barriers.  Group 0 reads the fragments of
@@ -356,10 +369,20 @@ __device__ __forceinline__ void kloop8(unsigned char* smem, Acc8& ta, const Src8
   auto issue = [&](int ks) {
     const uint32_t xa = sbase + kStageA + (ks & 1) * kTileBytes + wave * 4096;
     const uint32_t xb = sbase + kStageB + (ks & 1) * kTileBytes + wave * 4096;
+    if (ks < src.nk1) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      dma16(src.a[c] + ks * BK, xa + c * 1024);
-      dma16(src.b[c] + boff + ks * BK, xb + c * 1024);
+      for (int c = 0; c < 4; ++c) {
+        dma16(src.a[c] + ks * BK, xa + c * 1024);
+        dma16(src.b[c] + boff + ks * BK, xb + c * 1024);
+      }
+    } else {
+      const int64_t kt = static_cast<int64_t>(ks - src.nk1) * BK;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int64_t R = col0 + 32 * wave + 8 * c + (lane >> 3);
+        dma16(src.a[c] + ks * BK, xa + c * 1024);
+        dma16(src.tail + R * src.ld_tail + src.lc[c] * 8 + kt, xb + c * 1024);
+      }
     }
   };
   bf16x8 fa[kSlices][2], fb[kSlices][4];

@@ -62,14 +62,37 @@ class DeviceProblem:
             self.bwd_variant = B.lrq_select_variant(self.desc, True)
             ws = max(ws, B.lrq_workspace_size(self.desc, True))
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device) if ws > 0 else None
+        self.backward_enabled = backward
+        self.prepared = None  # set by prepare(): forward/backward then pass the prepared weights
+
+    def prepare(self, stream=None):
+        """Build the prepared frozen-weight layouts of (gamma, w_qkv) once; later forward and
+        backward calls pass them (the library then skips its per-call weight preparation)."""
+        import torch
+        n = B.lrq_prepared_size(self.desc, self.backward_enabled)
+        self.prepared = torch.empty(max(n, 1), dtype=torch.uint8, device=self.x.device) if n > 0 else None
+        if self.prepared is not None:
+            B.lrq_prepare_weights(self.desc, self.backward_enabled, self.gamma, self.w_qkv, self.prepared,
+                                  stream=stream)
+        return self.prepared
 
     def forward(self, stream=None, out=None):
-        B.lrq_forward(self.desc, self.x, self.gamma, self.w_qkv, self.bias, self.a, self.b, self.positions,
-                      self.out if out is None else out, self.workspace, stream=stream)
-        return self.out if out is None else out
+        o = self.out if out is None else out
+        if self.prepared is None:
+            B.lrq_forward(self.desc, self.x, self.gamma, self.w_qkv, self.bias, self.a, self.b, self.positions,
+                          o, self.workspace, stream=stream)
+        else:
+            B.lrq_forward_prepared(self.desc, self.x, self.gamma, self.w_qkv, self.prepared, self.bias, self.a,
+                                   self.b, self.positions, o, None, self.workspace, stream=stream)
+        return o
 
     def backward(self, y=None, stream=None):
-        B.lrq_backward(self.desc, self.x, self.gamma, self.w_qkv, self.bias, self.a, self.b, self.positions,
-                       self.out if y is None else y, self.dy, self.dx, self.da, self.db, self.workspace,
-                       stream=stream)
+        yy = self.out if y is None else y
+        if self.prepared is None:
+            B.lrq_backward(self.desc, self.x, self.gamma, self.w_qkv, self.bias, self.a, self.b, self.positions,
+                           yy, self.dy, self.dx, self.da, self.db, self.workspace, stream=stream)
+        else:
+            B.lrq_backward_prepared(self.desc, self.x, self.gamma, self.w_qkv, self.prepared, self.bias, self.a,
+                                    self.b, self.positions, yy, self.dy, self.dx, self.da, self.db,
+                                    self.workspace, stream=stream)
         return self.dx, self.da, self.db

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol():
     assert set(syms) == set(B.EXPORTED), syms
     for s in syms:
         assert hasattr(lib, s), s
-    assert B.lrq_abi_version() == 2
+    assert B.lrq_abi_version() == 3
 
 
 def test_desc_layout_matches_header(tmp_path):
@@ -207,3 +207,50 @@ def test_timing_hook_without_calls():
     assert lib.lrq_kernel_time_ms(1, ctypes.byref(ms), None) == B.LRQ_ERR_INVALID_ARG
     B.lrq_kernel_timing(False)
     assert B.lrq_kernel_time_ms(False) == (0.0, 0)
+
+
+def test_prepared_weight_checks():
+    """Prepared frozen weights: sizes, and every argument check of the preparation and of the
+    calls that take the buffer (each call below fails validation before any launch)."""
+    assert B.lrq_prepared_size(good_desc()) == 0  # float32: only the generic family runs
+    B.lrq_prepare_weights(good_desc(), True, FAKE, FAKE, None)  # size 0: a no-op
+    desc = good_desc(dtype=B.LRQ_BF16, n_tokens=4096, d_model=512, n_q_heads=4, n_kv_heads=4, head_dim=128)
+    N, d = 12 * 128, 512
+    assert B.lrq_prepared_size(desc) == N * d * 2  # W' for the tiled forward
+    assert B.lrq_prepared_size(desc, True) == 2 * N * d * 2  # + W^T for the tiled backward
+    # independent of the token count (and of the family the call's T would pick)
+    assert B.lrq_prepared_size(good_desc(dtype=B.LRQ_BF16, n_tokens=1, d_model=512, n_q_heads=4, n_kv_heads=4,
+                                         head_dim=128), True) == 2 * N * d * 2
+    need = B.lrq_prepared_size(desc, True)
+    expect(B.LRQ_ERR_INVALID_ARG, B.lrq_prepare_weights, desc, True, None, FAKE, FAKE, need)
+    expect(B.LRQ_ERR_INVALID_ARG, B.lrq_prepare_weights, desc, True, FAKE, FAKE, None, need)
+    expect(B.LRQ_ERR_INVALID_ARG, B.lrq_prepare_weights, desc, True, FAKE, FAKE, FAKE, need - 1)
+    expect(B.LRQ_ERR_UNSUPPORTED, B.lrq_prepare_weights, desc, True, FAKE, FAKE, FAKE + 16, need)
+    # the prepared call's workspace is smaller (no per-call W' / W^T)
+    assert 0 < B.lrq_workspace_size_prepared(desc) < B.lrq_workspace_size(desc)
+    assert 0 < B.lrq_workspace_size_prepared(desc, True) < B.lrq_workspace_size(desc, True)
+    ws = B.lrq_workspace_size_prepared(desc)
+
+    def fwdp(**over):
+        args = dict(x=FAKE, gamma=FAKE, w_qkv=FAKE, prepared=FAKE, bias=None, lora_a=[FAKE, None, FAKE],
+                    lora_b=[FAKE, None, FAKE], positions=FAKE, out=FAKE, kv=None, workspace=FAKE,
+                    workspace_bytes=ws, prepared_bytes=need)
+        args.update(over)
+        B.lrq_forward_prepared(desc, **args)
+    expect(B.LRQ_ERR_INVALID_ARG, fwdp, prepared_bytes=N * d * 2 - 1)  # below the forward layout
+    expect(B.LRQ_ERR_UNSUPPORTED, fwdp, prepared=FAKE + 16)
+    expect(B.LRQ_ERR_INVALID_ARG, fwdp, workspace_bytes=ws - 1)
+    expect(B.LRQ_ERR_INVALID_ARG, fwdp, x=None)
+    bws = B.lrq_workspace_size_prepared(desc, True)
+
+    def bwdp(**over):
+        args = dict(x=FAKE, gamma=FAKE, w_qkv=FAKE, prepared=FAKE, bias=None, lora_a=[FAKE, None, FAKE],
+                    lora_b=[FAKE, None, FAKE], positions=FAKE, y=FAKE, dy=FAKE, dx=FAKE,
+                    d_lora_a=[FAKE, None, FAKE], d_lora_b=[FAKE, None, FAKE], workspace=FAKE,
+                    workspace_bytes=bws, prepared_bytes=need)
+        args.update(over)
+        B.lrq_backward_prepared(desc, **args)
+    # a buffer prepared for the forward only is too small for the backward
+    expect(B.LRQ_ERR_INVALID_ARG, bwdp, prepared_bytes=N * d * 2)
+    expect(B.LRQ_ERR_UNSUPPORTED, bwdp, prepared=FAKE + 16)
+    expect(B.LRQ_ERR_INVALID_ARG, bwdp, workspace_bytes=bws - 1)
