@@ -1,25 +1,32 @@
 #!/usr/bin/env python3
 """Benchmark of the fused RMSNorm -> QKV(+LoRA) -> RoPE operator on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama3|llama2|decode|train|tiny]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all|llama2|tiny|llama3|decode|train]
 
 A step is one call of the whole operator on one batch of synthetic, seeded input that is
 already resident in HBM: the forward for the layer and decode workloads, forward then
-backward for the training workload.  W untimed warm-up steps, then K timed steps between
-two device synchronisations; one JSON line is printed.  The K steps are launched as one
-replay of a HIP graph that holds them (``--graph off``: eager calls), so the host's launch
-cost neither bounds a decode step nor leaves gaps between the kernels of a layer step.
+backward for the training workload.  The frozen weights (W, gamma) are prepared once before
+the steps, as at model load.  W untimed warm-up steps, then K timed steps between two device
+synchronisations.  The K steps are launched as one replay of a HIP graph that holds them
+(``--graph off``: eager calls), so the host's launch cost neither bounds a decode step nor
+leaves gaps between the kernels of a layer step.  Consecutive steps read different copies of
+the streamed operands, so none of them is left in the 256 MB MALL by the step before.
+
+By default every workload is measured; one JSON line is printed whose top level is the
+headline workload, llama2 (LLaMA-2-7B layer, 16384 tokens: the largest), and whose
+``configs`` holds all five (tiny, llama3, llama2, decode, train) in the same form.
 
 * ``value``: tokens per second of the whole job (one GPU).
 * ``roofline``: the dominant kernel's algorithmic FLOPs (or bytes, for the bandwidth-bound
   decode workload) per launch over its average launch duration, against MI355X's published
-  peak (bf16 dense MFMA 2500 TFLOP/s, HBM 8000 GB/s).  The duration comes from the
-  library's measurement hook (HIP events recorded on the launch stream around that one
-  kernel in every timed call); ``call_ms`` is the whole library call, timed the same way
-  from here.  ``traffic`` comes from rocprofv3 FETCH_SIZE/WRITE_SIZE counters recorded
-  under profiles/ for the same kernel source (null if the source changed).
+  peak (bf16 dense MFMA 2500 TFLOP/s, HBM 8000 GB/s).  The duration is the mean of the
+  library's measurement hook (HIP events recorded on the launch stream around that one kernel)
+  over a separate eager pass of K steps, clamped to the graph-timed step;
+  ``call_ms_eager`` are the whole library calls of that pass.  ``traffic`` comes from
+  rocprofv3 FETCH_SIZE/WRITE_SIZE counters recorded under profiles/ for the same kernel source
+  (null if the source changed).
 * ``cpu_baseline``: the CPU oracle (float64 numpy, untuned) timed on this host on a bounded
-  sample of the same workload's rows.
+  sample of the same workload's rows, BLAS threads pinned to the process's cores.
 
 ``--copy-probe`` instead runs a plain device copy of known size (the calibration kernel for
 the FETCH_SIZE / WRITE_SIZE counters).  ``--record-traffic`` turns the counter files of
@@ -167,15 +174,27 @@ def record_traffic(args):
     print(json.dumps(rec))
 
 
-def cpu_baseline(w, inp, budget_s: float, rows_cap: int, gpu_rows_fn=None):
-    """Time the float64 oracle on a bounded, seeded sample of rows of the same workload."""
+def cpu_threads() -> int:
+    """Cores this process may run on (the affinity mask; a container's CPU share may be smaller
+    than os.cpu_count())."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(w, inp, budget_s: float, gpu_rows_fn=None):
+    """Time the float64 oracle on a bounded, seeded sample of rows of the same workload, with
+    the BLAS pool pinned to this process's cores (the count used is reported)."""
     import numpy as np
     import oracle.lrq_oracle as o
+    n_threads = cpu_threads()
     try:
         import threadpoolctl
-        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+        limiter = threadpoolctl.threadpool_limits(limits=n_threads)
+        used = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
     except Exception:  # noqa: BLE001
-        threads = 1
+        limiter, used = None, 1
     spec = o.Spec(d_model=w.d_model, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
                   lora_rank=w.lora_rank if w.lora_targets else 0, lora_alpha=w.lora_alpha,
                   lora_targets=w.lora_targets, eps=w.eps, rope_theta=w.rope_theta)
@@ -192,19 +211,24 @@ def cpu_baseline(w, inp, budget_s: float, rows_cap: int, gpu_rows_fn=None):
                        inp["positions"][rows], inp["dy"][rows])
         return time.perf_counter() - t0, out
 
-    probe = min(T, 32)
-    dt, _ = run(np.sort(order[:probe]))
-    n = int(min(T, rows_cap, max(probe, probe * budget_s / max(dt, 1e-6))))
-    rows = np.sort(order[:n])
-    dt, out = run(rows)
-    # when the whole sample takes much less than the budget, repeat it (a steadier rate)
-    reps, total = 1, dt
-    while total < 0.8 * budget_s and reps < 256:
-        total += run(rows)[0]
-        reps += 1
-    res = {"value": n * reps / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    try:
+        probe = min(T, 32)
+        dt, _ = run(np.sort(order[:probe]))
+        n = int(min(T, max(probe, probe * budget_s / max(dt, 1e-6))))
+        rows = np.sort(order[:n])
+        dt, out = run(rows)
+        # when the whole sample takes much less than the budget, repeat it (a steadier rate)
+        reps, total = 1, dt
+        while total < 0.8 * budget_s and reps < 256:
+            total += run(rows)[0]
+            reps += 1
+    finally:
+        if limiter is not None:
+            limiter.unregister() if hasattr(limiter, "unregister") else None
+    res = {"value": n * reps / total, "unit": "tokens/s", "cores": used, "kind": "oracle",
            "sample": f"{n} of {T} rows (seeded) x {reps} passes, "
-                     f"{'forward+backward' if w.backward else 'forward'}, float64 numpy, {total:.2f} s"}
+                     f"{'forward+backward' if w.backward else 'forward'}, float64 numpy, {total:.2f} s, "
+                     f"BLAS threads pinned to {n_threads}"}
     if gpu_rows_fn is not None:  # the same rows from the GPU forward, for a parity figure
         res["gpu_parity_rel_fro"] = o.rel_frobenius(gpu_rows_fn(rows), out)
     return res
@@ -221,22 +245,211 @@ def copy_probe(nbytes: int, reps: int):
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}), flush=True)
 
 
+KERNEL_NAMES = {("tiled", False): "fwd_tiled_kernel", ("decode", False): "decode_main_kernel",
+                ("generic", False): "fwd_generic_kernel", ("tiled", True): "bwd_main_kernel",
+                ("generic", True): "bwd_generic_kernel"}
+HEADLINE = "llama2"
+ALL_WORKLOADS = ("llama2", "tiny", "llama3", "decode", "train")
+
+
+def working_set_copies(w, prob, n_copies: int):
+    """Independent copies of the operands a step streams (the prepared weights, or W for the
+    families that read it, and x), so that consecutive steps cannot find them in the 256 MB
+    MALL: each step reads the copy i % n of each."""
+    import torch
+    sets = []
+    for i in range(n_copies):
+        if i == 0:
+            sets.append((prob.w_qkv, prob.prepared, prob.x))
+            continue
+        sets.append((prob.w_qkv.clone(), None if prob.prepared is None else prob.prepared.clone(),
+                     prob.x.clone()))
+    torch.cuda.synchronize()
+    return sets
+
+
+def run_config(name, args, B, wl, DeviceProblem):
+    """Measure one workload: returns its result object (the shape of the top-level line)."""
+    import numpy as np
+    import torch
+
+    w = wl.get(name)
+    variant = {"auto": B.LRQ_VARIANT_AUTO, "generic": B.LRQ_VARIANT_GENERIC, "tiled": B.LRQ_VARIANT_TILED,
+               "decode": B.LRQ_VARIANT_DECODE}[args.variant]
+    inp = wl.make_inputs(w, with_dy=w.backward)
+    prob = DeviceProblem(w, inp, variant=variant, backward=w.backward)
+    vname = B.VARIANT_NAMES[prob.variant]
+    stream = torch.cuda.current_stream()
+    # frozen weights are prepared once, before any step (untimed setup, as at model load), for
+    # the families that read a prepared layout
+    uses_prepared = vname == "tiled" or (w.backward and B.VARIANT_NAMES[prob.bwd_variant] == "tiled")
+    if uses_prepared and not args.no_prepare:
+        prob.prepare()
+        ws = max(B.lrq_workspace_size_prepared(prob.desc, False),
+                 B.lrq_workspace_size_prepared(prob.desc, True) if w.backward else 0)
+        prob.workspace = torch.empty(ws, dtype=torch.uint8, device="cuda") if ws else None
+    # enough copies that one step's streamed operands are not left in the MALL by the last
+    per_copy = prob.x.numel() * prob.x.element_size() + \
+        (prob.prepared.numel() if prob.prepared is not None else prob.w_qkv.numel() * prob.w_qkv.element_size())
+    n_copies = args.copies or max(2, min(8, -(-400 * 2 ** 20 // per_copy)))
+    sets = working_set_copies(w, prob, n_copies)
+    kvw = w.n_kv_heads * w.head_dim
+    if args.kv_cache:
+        k_cache = torch.zeros((w.n_tokens, kvw), dtype=prob.out.dtype, device=prob.out.device)
+        v_cache = torch.zeros_like(k_cache)
+        slots = torch.arange(w.n_tokens, dtype=torch.int32, device=prob.out.device)
+
+    def forward(s):
+        if args.kv_cache:
+            B.lrq_forward_prepared(prob.desc, prob.x, prob.gamma, prob.w_qkv, prob.prepared, prob.bias, prob.a,
+                                   prob.b, prob.positions, prob.out, (k_cache, v_cache, slots, w.n_tokens),
+                                   prob.workspace, stream=s)
+        else:
+            prob.forward(stream=s)
+        return prob.out
+
+    def step(i, s):
+        prob.w_qkv, prob.prepared, prob.x = sets[i % n_copies]
+        forward(s)
+        if w.backward:
+            prob.backward(stream=s)
+
+    for i in range(args.warmup):
+        step(i, stream)
+    torch.cuda.synchronize()
+
+    # the K timed steps, captured once into a HIP graph (no events inside it)
+    graph = None
+    if args.graph == "on":
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(0, side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream()
+            for i in range(args.steps):
+                step(i, cap)
+        graph.replay()  # untimed
+        torch.cuda.synchronize()
+
+    # timed region: exactly K steps between two device synchronisations
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # separate eager pass (untimed for `value`): the library's events around the dominant
+    # kernel of every call, and events from here around every whole call
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    B.lrq_kernel_timing(True)
+    for i in range(args.steps):
+        e0, e1, e2 = ev[i]
+        prob.w_qkv, prob.prepared, prob.x = sets[i % n_copies]
+        e0.record(stream)
+        forward(stream)
+        e1.record(stream)
+        if w.backward:
+            prob.backward(stream=stream)
+        e2.record(stream)
+    torch.cuda.synchronize()
+    kfwd_ms, n_fwd = B.lrq_kernel_time_ms(False)
+    kbwd_ms, n_bwd = B.lrq_kernel_time_ms(True)
+    B.lrq_kernel_timing(False)
+    assert n_fwd == args.steps and n_bwd == (args.steps if w.backward else 0), (n_fwd, n_bwd)
+    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    bwd_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev])) if w.backward else 0.0
+    prob.w_qkv, prob.prepared, prob.x = sets[0]
+
+    tokens = w.n_tokens
+    f_fwd, f_bwd, bytes_fwd = algorithmic_work(w)
+    if args.kv_cache:
+        bytes_fwd += 2 * w.n_tokens * kvw * (4 if w.dtype == "f32" else 2)  # the cache rows written
+    res = {
+        "metric": METRIC, "value": tokens / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32" if w.dtype == "f32" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "tokens": tokens, "d_model": w.d_model,
+                   "n_out": w.n_out, "lora_rank": w.lora_rank, "lora_targets": w.lora_targets,
+                   "kernel_family": vname, "parallelism": "none (1 GPU)",
+                   "pass": "forward+backward" if w.backward else "forward",
+                   "kv_cache": bool(args.kv_cache),
+                   "weights": "prepared once before the steps" if prob.prepared is not None else
+                              "prepared inside every call",
+                   "operand_copies": n_copies,
+                   "launch": "one HIP graph replay of the K steps" if graph is not None else "eager calls"},
+        "tflops_step": (f_fwd + f_bwd * w.backward) / (ms_per_step * 1e-3) / 1e12,
+        "call_ms_eager": {"forward": fwd_ms},
+    }
+    if w.backward:
+        res["call_ms_eager"]["backward"] = bwd_ms
+    if w.name == "decode":
+        res["gbs_step"] = bytes_fwd / (ms_per_step * 1e-3) / 1e9
+    # dominant kernel: the longer of the forward and backward calls' dominant kernels.  Its
+    # duration is the mean of the library's events around it in the eager pass, never more
+    # than the graph-timed step (a kernel cannot outlast the step that contains it).
+    backward_dominant = w.backward and kbwd_ms > kfwd_ms
+    family = B.VARIANT_NAMES[prob.bwd_variant] if backward_dominant else vname
+    dom_eager = kbwd_ms if backward_dominant else kfwd_ms
+    dom_ms = min(dom_eager, ms_per_step)
+    assert dom_ms <= ms_per_step
+    work, kind = dominant_kernel_work(w, family, backward_dominant)
+    kname = KERNEL_NAMES[(family, backward_dominant)]
+    traffic = stored_traffic(w.name, ("bwd_" if backward_dominant else "") + family)
+    common = {"traffic": traffic, "kernel": kname, "launch_ms": dom_ms, "launch_ms_eager_events": dom_eager,
+              "launch_ms_clamped_to_step": dom_eager > ms_per_step,
+              "share_of_step": dom_ms / ms_per_step}
+    if kind == "bytes":
+        ach = work / (dom_ms * 1e-3) / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": ach / PEAK_HBM_GBS, "algorithmic_bytes": work, **common}
+    else:
+        peak = PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+        ach = work / (dom_ms * 1e-3) / 1e12
+        res["roofline"] = {"bound": "mfma" if w.dtype != "f32" else "alu", "achieved": ach, "peak": peak,
+                           "unit": "TFLOP/s", "frac": ach / peak, "algorithmic_flop": work, **common}
+    if not args.no_cpu_baseline:
+        got = forward(stream)
+        torch.cuda.synchronize()
+        got = got.float().cpu().numpy().astype(np.float64)
+        res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, gpu_rows_fn=lambda rows: got[rows])
+    del sets, prob, graph
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30, help="untimed steps first (the clocks settle within about 20 steps of sustained MFMA load)")
-    ap.add_argument("--workload", default="llama3", choices=["tiny", "llama3", "llama2", "decode", "train"])
+    ap.add_argument("--workload", default="all", choices=("all",) + ALL_WORKLOADS,
+                    help="all: every workload, the headline (llama2, the largest) on the top level and all five "
+                         "under 'configs'")
     ap.add_argument("--variant", default="auto", choices=["auto", "generic", "tiled", "decode"])
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for each cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--w-copies", type=int, default=0,
-                    help="rotate among this many W_qkv copies (defeats the 256 MB MALL; default 4 for decode)")
+    ap.add_argument("--no-prepare", action="store_true",
+                    help="let every call prepare the frozen weights itself (no lrq_prepare_weights)")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="rotate among this many copies of the streamed operands (default: enough for >= 400 MB, "
+                         "more than the 256 MB MALL)")
     ap.add_argument("--graph", choices=["on", "off"], default="on",
                     help="launch the K timed steps as one replay of a HIP graph that holds them (on), or as "
                          "eager library calls (off)")
     ap.add_argument("--kv-cache", action="store_true",
-                    help="forward through lrq_forward_kv: every token also writes its k and v rows to a "
+                    help="forward through the KV-cache entry: every token also writes its k and v rows to a "
                          "cache of T rows (slot t for token t)")
     ap.add_argument("--copy-probe", type=int, default=0, help="run a device copy of this many bytes and exit")
     ap.add_argument("--record-traffic", default="", help="workload name: store counter traffic and exit")
@@ -257,7 +470,6 @@ def main():
               f"(the path shards by tokens with no communication in the forward).", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     if args.copy_probe:
@@ -266,150 +478,24 @@ def main():
 
     from layer_rmsnorm_qkv_amd import binding as B
     from layer_rmsnorm_qkv_amd import workloads as wl
-    from layer_rmsnorm_qkv_amd.device import DeviceProblem, desc_for
+    from layer_rmsnorm_qkv_amd.device import DeviceProblem
 
     B.load()
-    w = wl.get(args.workload)
-    variant = {"auto": B.LRQ_VARIANT_AUTO, "generic": B.LRQ_VARIANT_GENERIC, "tiled": B.LRQ_VARIANT_TILED,
-               "decode": B.LRQ_VARIANT_DECODE}[args.variant]
-    inp = wl.make_inputs(w, with_dy=w.backward)
-    prob = DeviceProblem(w, inp, variant=variant, backward=w.backward)
-    vname = B.VARIANT_NAMES[prob.variant]
-    stream = torch.cuda.current_stream()
-
-    n_copies = args.w_copies or (4 if w.name == "decode" else 1)
-    w_list = [prob.w_qkv] + [prob.w_qkv.clone() for _ in range(n_copies - 1)]
-    kvw = w.n_kv_heads * w.head_dim
-    if args.kv_cache:
-        k_cache = torch.zeros((w.n_tokens, kvw), dtype=prob.out.dtype, device=prob.out.device)
-        v_cache = torch.zeros_like(k_cache)
-        slots = torch.arange(w.n_tokens, dtype=torch.int32, device=prob.out.device)
-
-    def forward(s=None):
-        s = stream if s is None else s
-        if args.kv_cache:
-            B.lrq_forward_kv(prob.desc, prob.x, prob.gamma, prob.w_qkv, prob.bias, prob.a, prob.b, prob.positions,
-                             prob.out, k_cache, v_cache, slots, w.n_tokens, prob.workspace, stream=s)
-        else:
-            prob.forward(stream=s)
-        return prob.out
-
-    def step(i, s=None):
-        prob.w_qkv = w_list[i % n_copies]
-        forward(s)
-        if w.backward:
-            prob.backward(stream=stream if s is None else s)
-
-    for i in range(args.warmup):
-        step(i)
-
-    use_graph = args.graph == "on"
-    if use_graph:
-        # One graph holds the K steps, each with the library's timing events around its dominant
-        # kernel (the events are created by an eager pass first: nothing is created during
-        # capture).  One untimed replay, then the timed one.
-        B.lrq_kernel_timing(True)
-        for i in range(args.steps):
-            step(i)
-        torch.cuda.synchronize()
-        B.lrq_kernel_timing(True)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            cap = torch.cuda.current_stream()
-            for i in range(args.steps):
-                step(i, cap)
-        graph.replay()
-        torch.cuda.synchronize()
-
-    # timed region: exactly K steps, nothing else on the stream but the library's own timing
-    # events around each call's dominant kernel (the roofline's per-launch duration)
-    torch.cuda.synchronize()
-    if not use_graph:
-        B.lrq_kernel_timing(True)
-    t0 = time.perf_counter()
-    if use_graph:
-        graph.replay()
-    else:
-        for i in range(args.steps):
-            step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kfwd_ms, n_fwd = B.lrq_kernel_time_ms(False)
-    kbwd_ms, n_bwd = B.lrq_kernel_time_ms(True)
-    B.lrq_kernel_timing(False)
-    assert n_fwd == args.steps and n_bwd == (args.steps if w.backward else 0), (n_fwd, n_bwd)
-
-    # whole library calls, timed with events on the stream in a separate (untimed) pass
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i in range(args.steps):
-        e0, e1, e2 = ev[i]
-        prob.w_qkv = w_list[i % n_copies]
-        e0.record(stream)
-        forward()
-        e1.record(stream)
-        if w.backward:
-            prob.backward(stream=stream)
-        e2.record(stream)
-    torch.cuda.synchronize()
-    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
-    bwd_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev])) if w.backward else 0.0
-
-    ms_per_step = wall * 1e3 / args.steps
-    tokens = w.n_tokens
-    f_fwd, f_bwd, bytes_fwd = algorithmic_work(w)
-    if args.kv_cache:
-        bytes_fwd += 2 * w.n_tokens * kvw * (4 if w.dtype == "f32" else 2)  # the cache rows written
-    result = {
-        "metric": METRIC, "value": tokens / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32" if w.dtype == "f32" else "bf16",
-        "data": "synthetic",
-        "config": {"workload": w.name, "description": w.description, "tokens": tokens, "d_model": w.d_model,
-                   "n_out": w.n_out, "lora_rank": w.lora_rank, "lora_targets": w.lora_targets,
-                   "kernel_family": vname, "parallelism": "none (1 GPU)",
-                   "pass": "forward+backward" if w.backward else "forward",
-                   "kv_cache": bool(args.kv_cache),
-                   "launch": "one HIP graph replay of the K steps" if use_graph else "eager calls"},
-    }
-    # call-level rates (whole library calls)
-    tflops_fwd = f_fwd / (fwd_ms * 1e-3) / 1e12
-    result["tflops_forward"] = tflops_fwd
-    result["call_ms"] = {"forward": fwd_ms}
-    if w.backward:
-        result["tflops_backward"] = f_bwd / (bwd_ms * 1e-3) / 1e12
-        result["tflops_step"] = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
-        result["call_ms"]["backward"] = bwd_ms
-    if w.name == "decode":
-        result["gbs_forward_call"] = bytes_fwd / (fwd_ms * 1e-3) / 1e9
-    # dominant kernel: the longer of the forward and backward calls' dominant kernels
-    backward_dominant = w.backward and kbwd_ms > kfwd_ms
-    family = B.VARIANT_NAMES[prob.bwd_variant] if backward_dominant else vname
-    dom_ms = kbwd_ms if backward_dominant else kfwd_ms
-    work, kind = dominant_kernel_work(w, family, backward_dominant)
-    kname = {("tiled", False): "fwd_tiled_kernel", ("decode", False): "decode_main_kernel",
-             ("generic", False): "fwd_generic_kernel", ("tiled", True): "bwd_main_kernel",
-             ("generic", True): "bwd_generic_kernel"}[(family, backward_dominant)]
-    traffic = stored_traffic(w.name, ("bwd_" if backward_dominant else "") + family)
-    if kind == "bytes":
-        ach = work / (dom_ms * 1e-3) / 1e9
-        result["roofline"] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                              "frac": ach / PEAK_HBM_GBS, "traffic": traffic, "kernel": kname,
-                              "launch_ms": dom_ms, "algorithmic_bytes": work}
-    else:
-        peak = PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
-        ach = work / (dom_ms * 1e-3) / 1e12
-        result["roofline"] = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
-                              "frac": ach / peak, "traffic": traffic, "kernel": kname,
-                              "launch_ms": dom_ms, "algorithmic_flop": work}
-    if not args.no_cpu_baseline:
-        prob.w_qkv = w_list[0]
-        got = forward()
-        torch.cuda.synchronize()
-        got = got.float().cpu().numpy().astype(np.float64)
-        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, rows_cap=w.n_tokens,
-                                              gpu_rows_fn=lambda rows: got[rows])
-    print(json.dumps(result), flush=True)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    names = ALL_WORKLOADS if args.workload == "all" else (args.workload,)
+    results = {}
+    for name in names:
+        print(f"[bench] {name}: measuring", file=sys.stderr, flush=True)
+        results[name] = run_config(name, args, B, wl, DeviceProblem)
+        r = results[name]
+        print(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step, {r['value']:.4g} tokens/s, roofline "
+              f"{r['roofline']['frac']:.3f} of {r['roofline']['kernel']}", file=sys.stderr, flush=True)
+    top = dict(results[names[0]])
+    if len(names) > 1:
+        top["configs"] = {n: {k: v for k, v in results[n].items()
+                              if k not in ("metric", "n_gpus", "higher_is_better", "scaling", "data", "steps",
+                                           "warmup")} for n in names}
+    print(json.dumps(top), flush=True)
 
 
 if __name__ == "__main__":
