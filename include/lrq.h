@@ -226,6 +226,26 @@ lrq_status lrq_backward_prepared(const lrq_desc* desc, const void* x, const void
 /* Workspace bytes of a call that passes prepared weights (<= lrq_workspace_size). */
 size_t lrq_workspace_size_prepared(const lrq_desc* desc, int for_backward);
 
+/* ---- For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  lrq_forward_prepared with no workspace
+ * argument: the scratch the call needs comes from an array the library holds on each GPU
+ * (LRQ_NOALLOC_SCRATCH_BYTES, part of its device code, kept until the process ends); the call
+ * runs on the current device (the stream must belong to it) and allocates nothing.  The
+ * tiled family needs the scratch only for the adapters' folded A rows when weights are
+ * prepared (without prepared weights its W' does not fit and the call is refused); the decode
+ * family keeps its per-call intermediates there.  Every call on a GPU shares that GPU's array:
+ * calls that overlap on one GPU (other streams, other threads) race and give wrong results;
+ * order them.  No part of the scratch needs to start at zero: every call writes what it
+ * reads.  Same results, bit for bit, as lrq_forward_prepared; same errors, plus UNSUPPORTED
+ * when the call needs more than LRQ_NOALLOC_SCRATCH_BYTES of scratch (lrq_workspace_size or
+ * lrq_workspace_size_prepared tells how much), and LRQ_ERR_HIP if the array's device address
+ * cannot be looked up. */
+#define LRQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+lrq_status lrq_forward_noalloc(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,
+                               const void* prepared, size_t prepared_bytes, const void* bias,
+                               const void* const* lora_a, const void* const* lora_b, const int32_t* positions,
+                               void* out, const lrq_kv_cache* kv, void* stream);
+
 /* The kernel family lrq_forward (for_backward = 0) or lrq_backward (1) would run for this
  * descriptor (an lrq_variant value), or -1 when the descriptor is invalid or the forced
  * variant cannot run.  Host-only; enqueues nothing. */

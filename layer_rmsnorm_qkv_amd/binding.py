@@ -24,7 +24,7 @@ VARIANT_NAMES = {LRQ_VARIANT_GENERIC: "generic", LRQ_VARIANT_TILED: "tiled", LRQ
 EXPORTED = ("lrq_forward", "lrq_forward_kv", "lrq_backward", "lrq_workspace_size", "lrq_select_variant",
             "lrq_status_string", "lrq_last_error", "lrq_abi_version", "lrq_kernel_timing",
             "lrq_kernel_time_ms", "lrq_prepared_size", "lrq_prepare_weights", "lrq_forward_prepared",
-            "lrq_backward_prepared", "lrq_workspace_size_prepared")
+            "lrq_backward_prepared", "lrq_workspace_size_prepared", "lrq_forward_noalloc")
 
 
 class LrqDesc(ctypes.Structure):
@@ -89,6 +89,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.lrq_backward_prepared.argtypes = [ctypes.POINTER(LrqDesc), P, P, P, P, S, P, PP, PP, P, P, P, P, PP,
                                               PP, P, S, P]
         lib.lrq_backward_prepared.restype = ctypes.c_int
+        lib.lrq_forward_noalloc.argtypes = [ctypes.POINTER(LrqDesc), P, P, P, P, S, P, PP, PP, P, P,
+                                            ctypes.POINTER(LrqKvCache), P]
+        lib.lrq_forward_noalloc.restype = ctypes.c_int
         lib.lrq_select_variant.argtypes = [ctypes.POINTER(LrqDesc), ctypes.c_int]
         lib.lrq_select_variant.restype = ctypes.c_int
         lib.lrq_status_string.argtypes = [ctypes.c_int]
@@ -212,6 +215,21 @@ def lrq_forward_prepared(desc: LrqDesc, x, gamma, w_qkv, prepared, bias, lora_a,
                                   _ptr3(lora_b), _ptr(positions), _ptr(out),
                                   ctypes.byref(kvs) if kvs is not None else None, _ptr(workspace),
                                   int(_ws_bytes(workspace, workspace_bytes)), _stream(stream, (x, out)))
+    _check(st)
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # LRQ_NOALLOC_SCRATCH_BYTES
+
+
+def lrq_forward_noalloc(desc: LrqDesc, x, gamma, w_qkv, prepared, bias, lora_a, lora_b, positions, out,
+                        kv: Optional[tuple] = None, prepared_bytes: Optional[int] = None, stream=None) -> None:
+    """lrq_forward_prepared with the library's own scratch (no workspace argument)."""
+    lib = load()
+    kvs = None if kv is None else LrqKvCache(_ptr(kv[0]), _ptr(kv[1]), _ptr(kv[2]), int(kv[3]))
+    st = lib.lrq_forward_noalloc(ctypes.byref(desc), _ptr(x), _ptr(gamma), _ptr(w_qkv), _ptr(prepared),
+                                 int(_ws_bytes(prepared, prepared_bytes)), _ptr(bias), _ptr3(lora_a),
+                                 _ptr3(lora_b), _ptr(positions), _ptr(out),
+                                 ctypes.byref(kvs) if kvs is not None else None, _stream(stream, (x, out)))
     _check(st)
 
 

@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "lrq.h"
@@ -65,6 +66,39 @@ void timing_end(hipStream_t s) {
 }
 
 }  // namespace lrq
+
+// ---- the no-allocation entry point's scratch (lrq_forward_noalloc)
+// One array per GPU, part of the library's device code object: it exists on every device the
+// library is loaded on and lives until the process ends.  Host code never uses its name as an
+// address; it uses the device address that hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = size_t{16} << 20;  // LRQ_NOALLOC_SCRATCH_BYTES
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device.
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
 
 namespace {
 
@@ -373,6 +407,34 @@ lrq_status lrq_forward(const lrq_desc* desc, const void* x, const void* gamma, c
                        void* stream) {
   return lrq_forward_prepared(desc, x, gamma, w_qkv, nullptr, 0, bias, lora_a, lora_b, positions, out, nullptr,
                               workspace, workspace_bytes, stream);
+}
+
+lrq_status lrq_forward_noalloc(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,
+                               const void* prepared, size_t prepared_bytes, const void* bias,
+                               const void* const* lora_a, const void* const* lora_b, const int32_t* positions,
+                               void* out, const lrq_kv_cache* kv, void* stream) {
+  // every argument check of lrq_forward_prepared, plus the scratch bound, before any HIP call
+  lrq::FwdParams p;
+  lrq_status st = check_desc(desc, p);
+  if (st != LRQ_OK) return st;
+  st = check_common_ptrs(desc, p, x, gamma, w_qkv, bias, lora_a, lora_b, positions);
+  if (st != LRQ_OK) return st;
+  const int v = select(desc, p, false);
+  if (v < 0) return LRQ_ERR_UNSUPPORTED;
+  if (prepared && v == LRQ_VARIANT_TILED && prep_layout(desc, p, false).fwd_bytes) p.use_prepared = true;
+  const size_t need = workspace_for(v, p, false);
+  if (need > kScratchBytes)
+    return fail(LRQ_ERR_UNSUPPORTED,
+                "lrq_forward_noalloc: this call needs %zu bytes of scratch, above the library's %zu "
+                "(pass prepared weights, or use lrq_forward_prepared with a workspace)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return hip_status(e, "scratch address");
+  }
+  return lrq_forward_prepared(desc, x, gamma, w_qkv, prepared, prepared_bytes, bias, lora_a, lora_b, positions,
+                              out, kv, ws, need > 0 ? kScratchBytes : 0, stream);
 }
 
 lrq_status lrq_backward_prepared(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,

@@ -254,3 +254,24 @@ def test_prepared_weight_checks():
     expect(B.LRQ_ERR_INVALID_ARG, bwdp, prepared_bytes=N * d * 2)
     expect(B.LRQ_ERR_UNSUPPORTED, bwdp, prepared=FAKE + 16)
     expect(B.LRQ_ERR_INVALID_ARG, bwdp, workspace_bytes=bws - 1)
+
+
+def test_noalloc_checks():
+    """The no-allocation forward validates like lrq_forward_prepared and refuses a call whose
+    scratch would exceed the library's array, before any HIP call."""
+    assert B.NOALLOC_SCRATCH_BYTES == 16 << 20
+    text = open(HEADER).read()
+    assert "#define LRQ_NOALLOC_SCRATCH_BYTES (16u << 20)" in text
+
+    def noalloc(desc, **over):
+        args = dict(x=FAKE, gamma=FAKE, w_qkv=FAKE, prepared=None, bias=None, lora_a=[FAKE, None, FAKE],
+                    lora_b=[FAKE, None, FAKE], positions=FAKE, out=FAKE, kv=None)
+        args.update(over)
+        B.lrq_forward_noalloc(desc, **args)
+    expect(B.LRQ_ERR_INVALID_ARG, noalloc, good_desc(n_q_heads=3))
+    expect(B.LRQ_ERR_INVALID_ARG, noalloc, good_desc(), x=None)
+    # tiled family without prepared weights: W' (8192 x 1536 bf16 = 24 MiB) does not fit
+    big = good_desc(dtype=B.LRQ_BF16, n_tokens=4096, d_model=8192, n_q_heads=4, n_kv_heads=4, head_dim=128)
+    assert B.lrq_workspace_size(big) > B.NOALLOC_SCRATCH_BYTES
+    expect(B.LRQ_ERR_UNSUPPORTED, noalloc, big)
+    assert "scratch" in B.lrq_last_error()
