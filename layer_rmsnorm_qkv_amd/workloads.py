@@ -197,3 +197,79 @@ def make_inputs(w: Workload, n_tokens: Optional[int] = None, seed: Optional[int]
     if w.backward if with_dy is None else with_dy:
         out["dy"] = to_dtype(_normal(_rng(w, "dy", seed), (T, N), 1.0), dt)
     return out
+
+
+# --------------------------------------------------------------------------- SwiGLU MLP workloads
+#
+# The LoRA-adapted SwiGLU MLP of a Llama-3-8B layer (d = 4096, intermediate 14336), fed by
+# 16 x 512 tokens as the attention projection's llama3 workload; LoRA on gate, up and down
+# with r = 16, alpha 32.  The MLP input is the output of the layer's second RMSNorm, so
+# h ~ N(0, 1) (unit RMS); W_g, W_u ~ N(0, 1/d), W_d ~ N(0, 1/F); A ~ U(+-1/64); B ~ N(0, 0.02).
+
+MLP_TARGET_GATE = 1
+MLP_TARGET_UP = 2
+MLP_TARGET_DOWN = 4
+
+_MLP_TID = {"h": 21, "wg": 22, "wu": 23, "wd": 24, "a_g": 25, "a_u": 26, "a_d": 27, "b_g": 28, "b_u": 29,
+            "b_d": 30}
+
+
+@dataclasses.dataclass(frozen=True)
+class MlpWorkload:
+    name: str
+    index: int
+    n_tokens: int
+    d_model: int
+    d_ff: int
+    lora_rank: int
+    lora_alpha: float
+    lora_targets: int
+    a_scale: float = 1.0 / 64
+    b_var: float = 0.02
+    dtype: str = "bf16"
+    description: str = ""
+
+    @property
+    def seed(self) -> int:
+        return BASE_SEED + self.index
+
+    def replace(self, **kw) -> "MlpWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+MLP_WORKLOADS = [
+    MlpWorkload("mlp_llama3", 10, 16 * 512, 4096, 14336, 16, 32.0,
+                MLP_TARGET_GATE | MLP_TARGET_UP | MLP_TARGET_DOWN,
+                description="Llama-3-8B SwiGLU MLP: 16x512 tokens, d=4096, F=14336, r=16 on gate, up, down"),
+]
+MLP_BY_NAME = {w.name: w for w in MLP_WORKLOADS}
+
+
+def get_mlp(name: str) -> MlpWorkload:
+    return MLP_BY_NAME[name]
+
+
+def make_mlp_inputs(w: MlpWorkload, n_tokens: Optional[int] = None, seed: Optional[int] = None) -> Dict[str, object]:
+    """Every input of one MLP call: h [T, d], w_gate / w_up [F, d], w_down [d, F], and dicts
+    target -> A_t [r, d_in] / B_t [d_out, r] for the adapted projections (float32 holding
+    values exactly representable in the workload dtype)."""
+    T = w.n_tokens if n_tokens is None else n_tokens
+    d, F, r, dt = w.d_model, w.d_ff, w.lora_rank, w.dtype
+
+    def rng(name):
+        return np.random.default_rng([w.seed if seed is None else seed, _MLP_TID[name]])
+
+    out: Dict[str, object] = {
+        "h": to_dtype(_normal(rng("h"), (T, d), 1.0), dt),
+        "w_gate": to_dtype(_normal(rng("wg"), (F, d), 1.0 / d), dt),
+        "w_up": to_dtype(_normal(rng("wu"), (F, d), 1.0 / d), dt),
+        "w_down": to_dtype(_normal(rng("wd"), (d, F), 1.0 / F), dt),
+    }
+    a, b = {}, {}
+    for t, an, bn, din, dout in ((MLP_TARGET_GATE, "a_g", "b_g", d, F), (MLP_TARGET_UP, "a_u", "b_u", d, F),
+                                 (MLP_TARGET_DOWN, "a_d", "b_d", F, d)):
+        if w.lora_targets & t:
+            a[t] = to_dtype(rng(an).uniform(-w.a_scale, w.a_scale, size=(r, din)), dt)
+            b[t] = to_dtype(_normal(rng(bn), (dout, r), w.b_var), dt)
+    out["a"], out["b"] = a, b
+    return out
