@@ -429,6 +429,107 @@ def run_config(name, args, B, wl, DeviceProblem):
     return res
 
 
+def mlp_work(w):
+    """Matmul FLOPs of one MLP call and of its fused gate/up/SwiGLU kernel (algorithmic:
+    gate, up and down products plus the adapters' down and up products)."""
+    T, d, F, r = w.n_tokens, w.d_model, w.d_ff, w.lora_rank
+    lora = {1: (d, F), 2: (d, F), 4: (F, d)}
+    f_gu = 4.0 * T * d * F
+    f_dn = 2.0 * T * F * d
+    for t, (din, dout) in lora.items():
+        if w.lora_targets & t:
+            extra = 2.0 * T * din * r + 2.0 * T * r * dout
+            if t == 4:
+                f_dn += extra
+            else:
+                f_gu += extra
+    return f_gu, f_dn
+
+
+def run_mlp_config(name, args, B, wl):
+    """The LoRA-adapted SwiGLU MLP (a next row beside the projection): whole calls and the fused
+    gate/up/SwiGLU kernel, timed like the projection's workloads."""
+    import numpy as np
+    import torch
+    from layer_rmsnorm_qkv_amd.device import DeviceMlp
+
+    w = wl.get_mlp(name)
+    inp = wl.make_mlp_inputs(w)
+    prob = DeviceMlp(w, inp)
+    stream = torch.cuda.current_stream()
+    h_copies = [prob.h] + [prob.h.clone() for _ in range(1)]
+
+    def step(i, s):
+        prob.h = h_copies[i % len(h_copies)]
+        prob.forward(stream=s)
+
+    for i in range(args.warmup):
+        step(i, stream)
+    torch.cuda.synchronize()
+    graph = None
+    if args.graph == "on":
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(0, side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream()
+            for i in range(args.steps):
+                step(i, cap)
+        graph.replay()
+        torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i, stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    B.lrq_kernel_timing(True)
+    for i in range(args.steps):
+        step(i, stream)
+    torch.cuda.synchronize()
+    k_ms, n = B.lrq_kernel_time_ms(False)
+    B.lrq_kernel_timing(False)
+    assert n == args.steps
+    dom = min(k_ms, ms_per_step)
+    f_gu, f_dn = mlp_work(w)
+    res = {"value": w.n_tokens / (ms_per_step * 1e-3), "unit": "tokens/s", "ms_per_step": ms_per_step,
+           "dtype": "bf16",
+           "config": {"workload": w.name, "description": w.description, "tokens": w.n_tokens, "d_model": w.d_model,
+                      "d_ff": w.d_ff, "lora_rank": w.lora_rank, "lora_targets": w.lora_targets,
+                      "kernel_family": "mlp tiled (gate/up/SwiGLU, then down)",
+                      "launch": "one HIP graph replay of the K steps" if graph is not None else "eager calls"},
+           "tflops_step": (f_gu + f_dn) / (ms_per_step * 1e-3) / 1e12,
+           "roofline": {"bound": "mfma", "achieved": f_gu / (dom * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": f_gu / (dom * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "traffic": None,
+                        "kernel": "mlp_gate_up_kernel", "launch_ms": dom, "launch_ms_eager_events": k_ms,
+                        "algorithmic_flop": f_gu}}
+    if not args.no_cpu_baseline:
+        import oracle.mlp_oracle as mo
+        spec = mo.MlpSpec(d_model=w.d_model, d_ff=w.d_ff, lora_rank=w.lora_rank, lora_alpha=w.lora_alpha,
+                          lora_targets=w.lora_targets)
+        prob.h = h_copies[0]
+        got = prob.forward().float().cpu().numpy().astype(np.float64)
+        n_threads = cpu_threads()
+        rows = np.sort(np.random.default_rng(5).permutation(w.n_tokens)[:64])
+        t0 = time.perf_counter()
+        ref = mo.mlp_forward_rows(spec, rows, inp["h"], inp["w_gate"], inp["w_up"], inp["w_down"], inp["a"], inp["b"])
+        dt = time.perf_counter() - t0
+        from oracle.lrq_oracle import rel_frobenius
+        res["cpu_baseline"] = {"value": len(rows) / dt, "unit": "tokens/s", "cores": n_threads, "kind": "oracle",
+                               "sample": f"{len(rows)} of {w.n_tokens} rows (seeded), float64 numpy, {dt:.2f} s",
+                               "gpu_parity_rel_fro": rel_frobenius(got[rows], ref)}
+    del graph, prob, h_copies
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -440,6 +541,7 @@ def main():
     ap.add_argument("--variant", default="auto", choices=["auto", "generic", "tiled", "decode"])
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for each cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mlp", action="store_true", help="leave the SwiGLU-MLP workload out of the default run")
     ap.add_argument("--no-prepare", action="store_true",
                     help="let every call prepare the frozen weights itself (no lrq_prepare_weights)")
     ap.add_argument("--copies", type=int, default=0,
@@ -490,6 +592,13 @@ def main():
         r = results[name]
         print(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step, {r['value']:.4g} tokens/s, roofline "
               f"{r['roofline']['frac']:.3f} of {r['roofline']['kernel']}", file=sys.stderr, flush=True)
+    if args.workload == "all" and not args.no_mlp:
+        print("[bench] mlp_llama3: measuring", file=sys.stderr, flush=True)
+        results["mlp_llama3"] = run_mlp_config("mlp_llama3", args, B, wl)
+        r = results["mlp_llama3"]
+        print(f"[bench] mlp_llama3: {r['ms_per_step']:.4f} ms/step, roofline {r['roofline']['frac']:.3f}",
+              file=sys.stderr, flush=True)
+        names = names + ("mlp_llama3",)
     top = dict(results[names[0]])
     if len(names) > 1:
         top["configs"] = {n: {k: v for k, v in results[n].items()

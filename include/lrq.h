@@ -260,11 +260,49 @@ const char* lrq_last_error(void);
 /* LRQ_ABI_VERSION of the loaded library. */
 int lrq_abi_version(void);
 
+/* ---- LoRA-adapted SwiGLU MLP, the fused MLP the pages list beside the fused norm/QKV/RoPE
+ * kernel: "Swift-All一文详解：如何用Liger-Kernel提升训练效率", section 2.2 (2) (Linear ->
+ * SwiGLU -> Linear fused end to end for LLaMA-family FFNs, without storing the intermediate
+ * activations); "Liger-Kernel内核级优化：GPU利用率飙升至90%以上", section "内核融合" (a LoRA
+ * linear, frozen W plus up(down(x)), with SiLU fused into its last step);
+ * "Liger-Kernel底层优化：新一代内核级推理加速引擎深度解析", fused-kernel list (fused MLP with
+ * SwiGLU; gate_proj / up_proj / down_proj).  Per token row h:
+ *   g = W_g h + s B_g (A_g h),   u = W_u h + s B_u (A_u h),   a = SiLU(g) * u,
+ *   y = W_d a + s B_d (A_d a),   SiLU(z) = z / (1 + exp(-z)),  s = alpha / r,
+ * each adapter present when its target bit is set.  bf16 operands, fp32 accumulation; g and u
+ * stay on chip, a is rounded once to bf16 (the workspace holds it: a full down projection
+ * needs whole rows of a), y once.  Layouts (row-major): h, out [T, d]; w_gate, w_up [F, d];
+ * w_down [d, F]; lora_a = {A_g [r, d], A_u [r, d], A_d [r, F]}, lora_b = {B_g [F, r],
+ * B_u [F, r], B_d [d, r]}.  Same ownership, stream and error rules as lrq_forward; covered
+ * shapes: bf16, d % 256 == 0, d_ff % 128 == 0, rank <= 32 (UNSUPPORTED otherwise). */
+enum { LRQ_MLP_GATE = 1, LRQ_MLP_UP = 2, LRQ_MLP_DOWN = 4 };
+
+typedef struct lrq_mlp_desc {
+  int64_t n_tokens;      /* T >= 0; T == 0 is a no-op                                  */
+  int64_t d_model;       /* d                                                           */
+  int64_t d_ff;          /* F, the intermediate size                                    */
+  int32_t dtype;         /* lrq_dtype (LRQ_BF16)                                        */
+  int32_t lora_rank;     /* r; 1..32 when lora_targets != 0                             */
+  float lora_alpha;      /* the update is scaled by alpha / r                           */
+  uint32_t lora_targets; /* OR of LRQ_MLP_*; 0 = no adapters                            */
+} lrq_mlp_desc;
+
+/* Bytes of workspace lrq_mlp_forward needs (T * d_ff * 2); 0 for an invalid descriptor. */
+size_t lrq_mlp_workspace_size(const lrq_mlp_desc* desc);
+
+/* out = down(SiLU(gate(h)) * up(h)).  INVALID_ARG for a malformed descriptor, a NULL required
+ * pointer (h, the three weights and out when T > 0; a target's lora_a / lora_b), or a workspace
+ * below lrq_mlp_workspace_size; UNSUPPORTED for an uncovered shape, float32, or misalignment. */
+lrq_status lrq_mlp_forward(const lrq_mlp_desc* desc, const void* h, const void* w_gate, const void* w_up,
+                           const void* w_down, const void* const* lora_a, const void* const* lora_b, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Measurement hook (not part of the operator).  While enabled, every lrq_forward /
  * lrq_backward call records a pair of HIP events on the caller's stream around the call's
  * dominant kernel: the fused tile kernel of the tiled forward, the streaming kernel of the
  * decode forward, the dh/dx product of the tiled backward, the single kernel of the
- * generic family.  Enabling (or disabling) discards what was recorded.  Events are created
+ * generic family, the fused gate/up/SwiGLU kernel of lrq_mlp_forward (as a forward).
+ * Enabling (or disabling) discards what was recorded.  Events are created
  * on demand (at most 4096 pairs per direction) and kept until the process ends.  Not
  * thread-safe: meant for one benchmarking thread.  Always LRQ_OK. */
 lrq_status lrq_kernel_timing(int enable);

@@ -24,7 +24,9 @@ VARIANT_NAMES = {LRQ_VARIANT_GENERIC: "generic", LRQ_VARIANT_TILED: "tiled", LRQ
 EXPORTED = ("lrq_forward", "lrq_forward_kv", "lrq_backward", "lrq_workspace_size", "lrq_select_variant",
             "lrq_status_string", "lrq_last_error", "lrq_abi_version", "lrq_kernel_timing",
             "lrq_kernel_time_ms", "lrq_prepared_size", "lrq_prepare_weights", "lrq_forward_prepared",
-            "lrq_backward_prepared", "lrq_workspace_size_prepared", "lrq_forward_noalloc")
+            "lrq_backward_prepared", "lrq_workspace_size_prepared", "lrq_forward_noalloc",
+            "lrq_mlp_workspace_size", "lrq_mlp_forward")
+LRQ_MLP_GATE, LRQ_MLP_UP, LRQ_MLP_DOWN = 1, 2, 4
 
 
 class LrqDesc(ctypes.Structure):
@@ -35,6 +37,12 @@ class LrqDesc(ctypes.Structure):
                 ("lora_rank", ctypes.c_int32), ("lora_alpha", ctypes.c_float),
                 ("lora_targets", ctypes.c_uint32), ("has_bias", ctypes.c_int32),
                 ("variant", ctypes.c_int32)]
+
+
+class LrqMlpDesc(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int64), ("d_model", ctypes.c_int64), ("d_ff", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("lora_rank", ctypes.c_int32), ("lora_alpha", ctypes.c_float),
+                ("lora_targets", ctypes.c_uint32)]
 
 
 class LrqKvCache(ctypes.Structure):
@@ -92,6 +100,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.lrq_forward_noalloc.argtypes = [ctypes.POINTER(LrqDesc), P, P, P, P, S, P, PP, PP, P, P,
                                             ctypes.POINTER(LrqKvCache), P]
         lib.lrq_forward_noalloc.restype = ctypes.c_int
+        lib.lrq_mlp_workspace_size.argtypes = [ctypes.POINTER(LrqMlpDesc)]
+        lib.lrq_mlp_workspace_size.restype = ctypes.c_size_t
+        lib.lrq_mlp_forward.argtypes = [ctypes.POINTER(LrqMlpDesc), P, P, P, P, PP, PP, P, P, S, P]
+        lib.lrq_mlp_forward.restype = ctypes.c_int
         lib.lrq_select_variant.argtypes = [ctypes.POINTER(LrqDesc), ctypes.c_int]
         lib.lrq_select_variant.restype = ctypes.c_int
         lib.lrq_status_string.argtypes = [ctypes.c_int]
@@ -274,3 +286,21 @@ def lrq_kernel_time_ms(for_backward: bool = False):
     ms, n = ctypes.c_double(0.0), ctypes.c_int(0)
     _check(load().lrq_kernel_time_ms(1 if for_backward else 0, ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def make_mlp_desc(n_tokens, d_model, d_ff, dtype=LRQ_BF16, lora_rank=0, lora_alpha=0.0, lora_targets=0) -> LrqMlpDesc:
+    return LrqMlpDesc(int(n_tokens), int(d_model), int(d_ff), int(dtype), int(lora_rank), float(lora_alpha),
+                      int(lora_targets))
+
+
+def lrq_mlp_workspace_size(desc: LrqMlpDesc) -> int:
+    return int(load().lrq_mlp_workspace_size(ctypes.byref(desc)))
+
+
+def lrq_mlp_forward(desc: LrqMlpDesc, h, w_gate, w_up, w_down, lora_a, lora_b, out, workspace=None,
+                    workspace_bytes: Optional[int] = None, stream=None) -> None:
+    lib = load()
+    st = lib.lrq_mlp_forward(ctypes.byref(desc), _ptr(h), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr3(lora_a),
+                             _ptr3(lora_b), _ptr(out), _ptr(workspace), int(_ws_bytes(workspace, workspace_bytes)),
+                             _stream(stream, (h, out)))
+    _check(st)

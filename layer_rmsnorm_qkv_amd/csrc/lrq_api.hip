@@ -502,6 +502,73 @@ lrq_status lrq_backward(const lrq_desc* desc, const void* x, const void* gamma, 
                                d_lora_a, d_lora_b, workspace, workspace_bytes, stream);
 }
 
+// ---- SwiGLU MLP
+namespace {
+lrq_status check_mlp_desc(const lrq_mlp_desc* d, lrq::MlpParams& p) {
+  if (!d) return fail(LRQ_ERR_INVALID_ARG, "desc is NULL");
+  if (d->n_tokens < 0) return fail(LRQ_ERR_INVALID_ARG, "n_tokens < 0");
+  if (d->d_model < 1 || d->d_ff < 1) return fail(LRQ_ERR_INVALID_ARG, "d_model and d_ff must be >= 1");
+  if (d->dtype != LRQ_F32 && d->dtype != LRQ_BF16) return fail(LRQ_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
+  if (d->lora_targets & ~7u) return fail(LRQ_ERR_INVALID_ARG, "lora_targets has unknown bits");
+  if (d->lora_targets) {
+    if (d->lora_rank < 1) return fail(LRQ_ERR_INVALID_ARG, "lora_rank < 1 with targets set");
+    if (!std::isfinite(d->lora_alpha)) return fail(LRQ_ERR_INVALID_ARG, "lora_alpha not finite");
+  }
+  std::memset(&p, 0, sizeof p);
+  p.T = d->n_tokens;
+  p.d = d->d_model;
+  p.F = d->d_ff;
+  p.targets = d->lora_targets;
+  p.r = d->lora_targets ? d->lora_rank : 0;
+  p.scale = d->lora_targets ? d->lora_alpha / static_cast<float>(d->lora_rank) : 0.f;
+  if (d->dtype != LRQ_BF16) return fail(LRQ_ERR_UNSUPPORTED, "the MLP kernels take bf16 only");
+  if (!lrq::mlp_supports(p))
+    return fail(LRQ_ERR_UNSUPPORTED, "MLP shape not covered (d %% 256, d_ff %% 128, rank <= 32, T <= 2^24)");
+  return LRQ_OK;
+}
+}  // namespace
+
+size_t lrq_mlp_workspace_size(const lrq_mlp_desc* desc) {
+  lrq::MlpParams p;
+  if (check_mlp_desc(desc, p) != LRQ_OK) return 0;
+  return lrq::mlp_workspace_bytes(p);
+}
+
+lrq_status lrq_mlp_forward(const lrq_mlp_desc* desc, const void* h, const void* w_gate, const void* w_up,
+                           const void* w_down, const void* const* lora_a, const void* const* lora_b, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  lrq::MlpParams p;
+  lrq_status st = check_mlp_desc(desc, p);
+  if (st != LRQ_OK) return st;
+  if (p.T > 0 && (!h || !w_gate || !w_up || !w_down || !out))
+    return fail(LRQ_ERR_INVALID_ARG, "h, w_gate, w_up, w_down and out are required");
+  if (desc->lora_targets && (!lora_a || !lora_b)) return fail(LRQ_ERR_INVALID_ARG, "lora_a / lora_b arrays are NULL");
+  for (int t = 0; t < 3; ++t) {
+    if (!(desc->lora_targets & (1u << t))) continue;
+    if (!lora_a[t] || !lora_b[t]) return fail(LRQ_ERR_INVALID_ARG, "lora_a[%d] / lora_b[%d] is NULL for a target", t, t);
+    if (!aligned16(lora_a[t]) || !aligned16(lora_b[t]))
+      return fail(LRQ_ERR_UNSUPPORTED, "LoRA pointers must be 16-byte aligned");
+    p.a[t] = lora_a[t];
+    p.b[t] = lora_b[t];
+  }
+  for (const void* q : {h, w_gate, w_up, w_down, static_cast<const void*>(out)})
+    if (q && !aligned16(q)) return fail(LRQ_ERR_UNSUPPORTED, "array pointers must be 16-byte aligned");
+  const size_t need = lrq::mlp_workspace_bytes(p);
+  if (workspace_bytes < need) return fail(LRQ_ERR_INVALID_ARG, "workspace too small: %zu < %zu", workspace_bytes, need);
+  if (need > 0 && !workspace) return fail(LRQ_ERR_INVALID_ARG, "workspace is NULL");
+  if (need > 0 && !aligned256(workspace)) return fail(LRQ_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  if (p.T == 0) return ok();
+  p.h = h;
+  p.wg = w_gate;
+  p.wu = w_up;
+  p.wd = w_down;
+  p.out = out;
+  p.ws = workspace;
+  p.ws_bytes = workspace_bytes;
+  g_timing.kind = 0;
+  return hip_status(lrq::launch_mlp(p, static_cast<hipStream_t>(stream)), "MLP launch");
+}
+
 lrq_status lrq_kernel_timing(int enable) {
   g_timing.on = enable != 0;
   g_timing.used[0] = g_timing.used[1] = 0;

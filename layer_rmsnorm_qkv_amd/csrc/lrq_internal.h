@@ -53,6 +53,26 @@ struct BwdParams {
   float* db[3];
 };
 
+// The LoRA-adapted SwiGLU MLP: y = down(SiLU(gate(h)) * up(h)) (mlp_tiled.hip).
+struct MlpParams {
+  int64_t T, d, F;        // tokens, model size, intermediate size
+  int r;                  // LoRA rank (0 without targets)
+  float scale;            // alpha / r
+  uint32_t targets;       // bit 0 gate, 1 up, 2 down
+  const void* h;          // [T][d]
+  const void* wg;         // [F][d]
+  const void* wu;         // [F][d]
+  const void* wd;         // [d][F]
+  const void* a[3];       // gate, up: [r][d]; down: [r][F]
+  const void* b[3];       // gate, up: [F][r]; down: [d][r]
+  void* out;              // [T][d]
+  void* ws;               // a = SiLU(g) * u, [T][F] bf16
+  size_t ws_bytes;
+};
+bool mlp_supports(const MlpParams& p);
+size_t mlp_workspace_bytes(const MlpParams& p);
+hipError_t launch_mlp(const MlpParams& p, hipStream_t s);
+
 // Column range [lo, hi) of target t.
 __host__ __device__ inline void target_cols(const FwdParams& p, int t, int& lo, int& hi) {
   lo = t == 0 ? 0 : (t == 1 ? p.col_k : p.col_v);

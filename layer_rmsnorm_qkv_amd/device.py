@@ -96,3 +96,32 @@ class DeviceProblem:
                                     self.b, self.positions, yy, self.dy, self.dx, self.da, self.db,
                                     self.workspace, stream=stream)
         return self.dx, self.da, self.db
+
+
+class DeviceMlp:
+    """Device tensors of one call of the LoRA-adapted SwiGLU MLP (lrq_mlp_forward)."""
+
+    def __init__(self, w, inputs: Dict[str, object], device: str = "cuda"):
+        import torch
+        from .workloads import MLP_TARGET_DOWN, MLP_TARGET_GATE, MLP_TARGET_UP
+        self.w = w
+        T = inputs["h"].shape[0]
+        self.desc = B.make_mlp_desc(T, w.d_model, w.d_ff, B.LRQ_BF16, w.lora_rank if w.lora_targets else 0,
+                                    w.lora_alpha, w.lora_targets)
+
+        def up(a):
+            return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device=device,
+                                                                                         dtype=torch.bfloat16)
+
+        self.h = up(inputs["h"])
+        self.w_gate, self.w_up, self.w_down = up(inputs["w_gate"]), up(inputs["w_up"]), up(inputs["w_down"])
+        self.a = [up(inputs["a"].get(t)) for t in (MLP_TARGET_GATE, MLP_TARGET_UP, MLP_TARGET_DOWN)]
+        self.b = [up(inputs["b"].get(t)) for t in (MLP_TARGET_GATE, MLP_TARGET_UP, MLP_TARGET_DOWN)]
+        self.out = torch.empty((T, w.d_model), dtype=torch.bfloat16, device=device)
+        ws = B.lrq_mlp_workspace_size(self.desc)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device) if ws else None
+
+    def forward(self, stream=None):
+        B.lrq_mlp_forward(self.desc, self.h, self.w_gate, self.w_up, self.w_down, self.a, self.b, self.out,
+                          self.workspace, stream=stream)
+        return self.out

@@ -275,3 +275,44 @@ def test_noalloc_checks():
     assert B.lrq_workspace_size(big) > B.NOALLOC_SCRATCH_BYTES
     expect(B.LRQ_ERR_UNSUPPORTED, noalloc, big)
     assert "scratch" in B.lrq_last_error()
+
+
+def test_mlp_desc_layout_and_checks(tmp_path):
+    """lrq_mlp_desc matches the header's layout; lrq_mlp_forward validates before any launch."""
+    fields = [f for f, _ in B.LrqMlpDesc._fields_]
+    src = tmp_path / "mlp_layout.c"
+    body = "\n".join(f'  printf("{f} %zu\\n", offsetof(lrq_mlp_desc, {f}));' for f in fields)
+    src.write_text(f'#include <stdio.h>\n#include <stddef.h>\n#include "lrq.h"\n'
+                   f'int main(void) {{\n{body}\n  printf("size %zu\\n", sizeof(lrq_mlp_desc));\n  return 0;\n}}\n')
+    exe = tmp_path / "mlp_layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src),
+                    "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                       check=True).stdout.splitlines())
+    for f in fields:
+        assert int(got[f]) == getattr(B.LrqMlpDesc, f).offset, f
+    assert int(got["size"]) == ctypes.sizeof(B.LrqMlpDesc)
+
+    good = dict(n_tokens=300, d_model=512, d_ff=384, dtype=B.LRQ_BF16, lora_rank=16, lora_alpha=32.0, lora_targets=7)
+    desc = B.make_mlp_desc(**good)
+    assert B.lrq_mlp_workspace_size(desc) == 300 * 384 * 2
+    ws = B.lrq_mlp_workspace_size(desc)
+
+    def call(d, **over):
+        args = dict(h=FAKE, w_gate=FAKE, w_up=FAKE, w_down=FAKE, lora_a=[FAKE, FAKE, FAKE],
+                    lora_b=[FAKE, FAKE, FAKE], out=FAKE, workspace=FAKE, workspace_bytes=ws)
+        args.update(over)
+        B.lrq_mlp_forward(d, **args)
+    for field, value in (("n_tokens", -1), ("d_model", 0), ("dtype", 5), ("lora_targets", 8), ("lora_rank", 0)):
+        expect(B.LRQ_ERR_INVALID_ARG, call, B.make_mlp_desc(**dict(good, **{field: value})))
+        assert B.lrq_mlp_workspace_size(B.make_mlp_desc(**dict(good, **{field: value}))) == 0
+    expect(B.LRQ_ERR_UNSUPPORTED, call, B.make_mlp_desc(**dict(good, dtype=B.LRQ_F32)))
+    expect(B.LRQ_ERR_UNSUPPORTED, call, B.make_mlp_desc(**dict(good, lora_rank=33)))
+    expect(B.LRQ_ERR_UNSUPPORTED, call, B.make_mlp_desc(**dict(good, d_model=500)))
+    expect(B.LRQ_ERR_INVALID_ARG, call, desc, h=None)
+    expect(B.LRQ_ERR_INVALID_ARG, call, desc, lora_b=[FAKE, None, FAKE])
+    expect(B.LRQ_ERR_INVALID_ARG, call, desc, workspace_bytes=ws - 1)
+    expect(B.LRQ_ERR_UNSUPPORTED, call, desc, out=FAKE + 2)
+    # T == 0: a no-op with NULL arrays
+    B.lrq_mlp_forward(B.make_mlp_desc(**dict(good, n_tokens=0)), None, None, None, None, [FAKE] * 3, [FAKE] * 3,
+                      None)
