@@ -39,8 +39,10 @@ Sources (the web pages on Liger-Kernel, cited by title and section):
 
 Readings where the pages are silent or garbled: LoRA scale s = alpha / r; LoRA
 applied to the normalised activations h (the input of q_proj/k_proj/v_proj);
-dropout is the identity; the output columns are q heads | k heads | v heads,
-head-major; v is never rotated; bias (if any) is added before RoPE.
+LoRA dropout (when a ``Dropout`` is given) on each adapter's input only, with its own
+Philox4x32-10 mask (section "LoRA dropout" below), the identity otherwise; the output
+columns are q heads | k heads | v heads, head-major; v is never rotated; bias (if any) is
+added before RoPE.
 
 Backward (frozen W, gamma and b; upstream gradient dy w.r.t. the rotated
 output): G = RoPE^-1(dy) on q and k blocks (dy on v); V_c = G_c B_c;
@@ -162,61 +164,150 @@ def rope_rotate(y: np.ndarray, positions: np.ndarray, head_dim: int, theta: floa
     return out.reshape(T, n)
 
 
+# --------------------------------------------------------------------------- LoRA dropout
+#
+# The LoRA configuration on the pages carries a dropout rate (lora_dropout 0.05 in the
+# Swift-All page's SftArguments, section 3.2; 0.1 in the LoRAConfig of the inference-engine
+# page's usage section).  Reading: as in the standard LoRA training recipe, dropout acts on the
+# adapter's input only -- the frozen projection sees h itself -- with an independent mask per
+# adapted projection (q, k, v each have their own), kept values scaled by 1 / (1 - p).
+# The masks come from the counter-based generator Philox4x32-10 (Salmon, Moraes, Dror and
+# Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011), so that a backward pass can
+# regenerate them: counter (j // 4, row, target, offset), key (seed low, seed high); word
+# j % 4 of the output keeps feature j of that row iff it is >= floor(p * 2^32).
+
+_PHILOX_M0, _PHILOX_M1 = 0xD2511F53, 0xCD9E8D57
+_PHILOX_W0, _PHILOX_W1 = 0x9E3779B9, 0xBB67AE85
+_U32 = np.uint64(0xFFFFFFFF)
+
+
+def philox4x32_10(ctr: np.ndarray, key: Tuple[int, int]) -> np.ndarray:
+    """Philox4x32 with 10 rounds on counters ``ctr`` ([..., 4] of uint32 values), one key
+    (k0, k1): each round multiplies words 0 and 2 by the two multipliers (64-bit products),
+    and the new words are (hi(M1 x2) ^ x1 ^ k0, lo(M1 x2), hi(M0 x0) ^ x3 ^ k1, lo(M0 x0));
+    the key is bumped by the two Weyl constants between rounds.  Returns uint32 words."""
+    x = np.asarray(ctr, dtype=np.uint64) & _U32
+    x0, x1, x2, x3 = x[..., 0], x[..., 1], x[..., 2], x[..., 3]
+    k0, k1 = np.uint64(key[0] & 0xFFFFFFFF), np.uint64(key[1] & 0xFFFFFFFF)
+    for rnd in range(10):
+        if rnd > 0:
+            k0 = (k0 + np.uint64(_PHILOX_W0)) & _U32
+            k1 = (k1 + np.uint64(_PHILOX_W1)) & _U32
+        p0 = np.uint64(_PHILOX_M0) * x0
+        p1 = np.uint64(_PHILOX_M1) * x2
+        hi0, lo0 = p0 >> np.uint64(32), p0 & _U32
+        hi1, lo1 = p1 >> np.uint64(32), p1 & _U32
+        x0, x1, x2, x3 = hi1 ^ x1 ^ k0, lo1, hi0 ^ x3 ^ k1, lo0
+    return np.stack([x0, x1, x2, x3], axis=-1).astype(np.uint32)
+
+
+def dropout_threshold(p: float) -> int:
+    """floor(p * 2^32): a generator word below it drops its feature."""
+    return int(np.floor(float(p) * 4294967296.0))
+
+
+def dropout_keep(n_rows: int, d: int, target_index: int, p: float, seed: int, offset: int,
+                 rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Boolean keep mask [rows, d] of adapter ``target_index`` (0 q, 1 k, 2 v) for the call's
+    token rows (all n_rows rows, or the given subset)."""
+    rows = np.arange(n_rows) if rows is None else np.asarray(rows, dtype=np.int64)
+    nq = (d + 3) // 4
+    ctr = np.zeros((len(rows), nq, 4), dtype=np.uint64)
+    ctr[..., 0] = np.arange(nq, dtype=np.uint64)[None, :]
+    ctr[..., 1] = rows.astype(np.uint64)[:, None]
+    ctr[..., 2] = np.uint64(target_index)
+    ctr[..., 3] = np.uint64(offset & 0xFFFFFFFF)
+    words = philox4x32_10(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)).reshape(len(rows), nq * 4)[:, :d]
+    return words >= np.uint32(dropout_threshold(p)) if p > 0 else np.ones((len(rows), d), dtype=bool)
+
+
+@dataclass(frozen=True)
+class Dropout:
+    """LoRA dropout of one call: rate p in [0, 1), generator seed and per-call offset."""
+    p: float
+    seed: int = 0
+    offset: int = 0
+
+
+def _adapter_inputs(spec: Spec, h: np.ndarray, dropout: Optional[Dropout], rows=None) -> Dict[int, np.ndarray]:
+    """The input each adapter sees: h, or h * mask / (1 - p) under dropout."""
+    out = {}
+    for i, c in enumerate(TARGETS):
+        if not (spec.lora_targets & c):
+            continue
+        if dropout is None or dropout.p == 0.0:
+            out[c] = h
+        else:
+            r_idx = np.arange(h.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+            keep = dropout_keep(h.shape[0], spec.d_model, i, dropout.p, dropout.seed, dropout.offset, rows=r_idx)
+            out[c] = h * keep / (1.0 - dropout.p)
+    return out
+
+
 # --------------------------------------------------------------------------- forward
 
 def lora_update(spec: Spec, h: np.ndarray, a: Mapping[int, np.ndarray],
-                b: Mapping[int, np.ndarray]) -> Dict[int, np.ndarray]:
-    """For each target c: s * B_c (A_c h) ([T, N_c]).
+                b: Mapping[int, np.ndarray], dropout: Optional[Dropout] = None,
+                rows=None) -> Dict[int, np.ndarray]:
+    """For each target c: s * B_c (A_c h_c) ([T, N_c]), h_c the adapter's input (h, or h
+    with dropout applied; ``rows`` are the call's row indices of h's rows).
 
     LoRA page "Liger-Kernel内核级优化", y = Wx + B(Ax) and its unfused two-step
     decomposition (down, then up); scale s = alpha / r (reading).
     """
     out = {}
+    ins = _adapter_inputs(spec, h, dropout, rows)
     for c in TARGETS:
         if spec.lora_targets & c:
-            u = h @ _f64(a[c]).T            # [T, r]   down projection
+            u = ins[c] @ _f64(a[c]).T       # [T, r]   down projection
             out[c] = spec.lora_scale * (u @ _f64(b[c]).T)   # [T, N_c] up projection
     return out
 
 
-def pre_rope(spec: Spec, x, gamma, w, bias, a, b) -> np.ndarray:
+def pre_rope(spec: Spec, x, gamma, w, bias, a, b, dropout: Optional[Dropout] = None, rows=None) -> np.ndarray:
     """y = W h + b + LoRA updates, before the rotation ([T, N])."""
     h = rms_normalise(x, gamma, spec.eps)
     y = h @ _f64(w).T
     if bias is not None:
         y = y + _f64(bias)[None, :]
-    for c, upd in lora_update(spec, h, a, b).items():
+    for c, upd in lora_update(spec, h, a, b, dropout, rows).items():
         lo, hi = spec.columns(c)
         y[:, lo:hi] += upd
     return y
 
 
-def forward(spec: Spec, x, gamma, w, bias, a, b, positions) -> np.ndarray:
+def forward(spec: Spec, x, gamma, w, bias, a, b, positions, dropout: Optional[Dropout] = None,
+            rows=None) -> np.ndarray:
     """out = RoPE(W h + b + s B(A h)) with h = RMSNorm(x) * gamma; [T, N] float64.
 
     The unfused chain of the Swift-All page, section 2.2 (1), plus the LoRA
-    branch of the LoRA page; v columns are not rotated.
+    branch of the LoRA page; v columns are not rotated.  With ``dropout``, each adapter
+    sees its own dropped-out copy of h (``rows``: the call's row indices of x's rows, for
+    the mask; default 0..T-1).
     """
-    y = pre_rope(spec, x, gamma, w, bias, a, b)
+    y = pre_rope(spec, x, gamma, w, bias, a, b, dropout, rows)
     lo, hi = spec.rotated_columns()
     y[:, lo:hi] = rope_rotate(y[:, lo:hi], positions, spec.head_dim, spec.rope_theta)
     return y
 
 
-def forward_rows(spec: Spec, rows: Sequence[int], x, gamma, w, bias, a, b, positions) -> np.ndarray:
+def forward_rows(spec: Spec, rows: Sequence[int], x, gamma, w, bias, a, b, positions,
+                 dropout: Optional[Dropout] = None) -> np.ndarray:
     """``forward`` on a subset of token rows (rows are independent given their positions)."""
     rows = np.asarray(rows, dtype=np.int64)
-    return forward(spec, np.asarray(x)[rows], gamma, w, bias, a, b, np.asarray(positions)[rows])
+    return forward(spec, np.asarray(x)[rows], gamma, w, bias, a, b, np.asarray(positions)[rows], dropout,
+                   rows=rows)
 
 
-def forward_chunked(spec: Spec, x, gamma, w, bias, a, b, positions, chunk: int = 2048) -> np.ndarray:
+def forward_chunked(spec: Spec, x, gamma, w, bias, a, b, positions, chunk: int = 2048,
+                    dropout: Optional[Dropout] = None) -> np.ndarray:
     """``forward`` over all rows, ``chunk`` rows at a time to bound float64 memory."""
     T = np.asarray(x).shape[0]
     out = np.empty((T, spec.n_out), dtype=np.float64)
     for s0 in range(0, T, chunk):
         s1 = min(T, s0 + chunk)
         out[s0:s1] = forward(spec, np.asarray(x)[s0:s1], gamma, w, bias, a, b,
-                             np.asarray(positions)[s0:s1])
+                             np.asarray(positions)[s0:s1], dropout, rows=np.arange(s0, s1))
     return out
 
 
@@ -253,13 +344,15 @@ def unrotate_grad(spec: Spec, dy, positions) -> np.ndarray:
 
 
 def backward(spec: Spec, x, gamma, w, bias, a, b, positions, dy,
-             dx_rows: Optional[Sequence[int]] = None):
+             dx_rows: Optional[Sequence[int]] = None, dropout: Optional[Dropout] = None):
     """Gradients of <dy, forward(x)> w.r.t. x and the LoRA factors (W, gamma, b frozen).
 
     Returns (dx, dA, dB): dx [T, d] (or [len(dx_rows), d]); dA[c] [r, d] and dB[c]
     [N_c, r] for every target c, summed over all tokens.  The LoRA page notes
     that the fused backward recomputes rather than stores; here everything is
-    simply recomputed from x.  ``bias`` does not enter the gradients.
+    simply recomputed from x.  ``bias`` does not enter the gradients.  With ``dropout``
+    the same masks as the forward's are regenerated; an adapter's gradient then reaches
+    h only through the kept features (its input is h * mask / (1 - p)).
     """
     del bias
     x = _f64(x)
@@ -267,19 +360,27 @@ def backward(spec: Spec, x, gamma, w, bias, a, b, positions, dy,
     inv = rms_inverse(x, spec.eps)
     h = rms_normalise(x, gamma, spec.eps)
     G = unrotate_grad(spec, dy, positions)
+    ins = _adapter_inputs(spec, h, dropout)
     dA, dB, V = {}, {}, {}
     for c in TARGETS:
         if spec.lora_targets & c:
             lo, hi = spec.columns(c)
             Ac, Bc = _f64(a[c]), _f64(b[c])
             V[c] = G[:, lo:hi] @ Bc                 # [T, r]
-            U = h @ Ac.T                            # [T, r]
-            dA[c] = s * (V[c].T @ h)                # [r, d]
+            U = ins[c] @ Ac.T                       # [T, r]
+            dA[c] = s * (V[c].T @ ins[c])           # [r, d]
             dB[c] = s * (G[:, lo:hi].T @ U)         # [N_c, r]
     rows = np.arange(x.shape[0]) if dx_rows is None else np.asarray(dx_rows, dtype=np.int64)
     dh = G[rows] @ _f64(w)
-    for c in V:
-        dh += s * (V[c][rows] @ _f64(a[c]))
+    for i, c in enumerate(TARGETS):
+        if c not in V:
+            continue
+        term = s * (V[c][rows] @ _f64(a[c]))
+        if dropout is not None and dropout.p > 0.0:
+            # d(input)/dh = mask / (1 - p): the adapter's gradient flows through kept features
+            keep = dropout_keep(x.shape[0], spec.d_model, i, dropout.p, dropout.seed, dropout.offset, rows=rows)
+            term = term * keep / (1.0 - dropout.p)
+        dh += term
     gam = _f64(gamma)
     xr, invr = x[rows], inv[rows]
     c_row = np.sum(gam[None, :] * xr * dh, axis=1)      # <gamma x, dh> per row

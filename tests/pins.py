@@ -346,9 +346,144 @@ def check_kv_cache_by_hand(o):
     assert (k0 == -1.0).all() and (v0 == -1.0).all()
 
 
+# --------------------------------------------------------------------------- LoRA dropout
+
+def check_philox_known_answers(o):
+    """Philox4x32-10 against the known-answer vectors published with the generator's reference
+    implementation (Random123): zero counter and key; all-ones counter and key; the digits of
+    pi as counter and key."""
+    cases = [((0, 0, 0, 0), (0, 0), (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+             ((0xFFFFFFFF,) * 4, (0xFFFFFFFF, 0xFFFFFFFF), (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+             ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+              (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1))]
+    for ctr, key, want in cases:
+        got = [int(v) for v in o.philox4x32_10(np.array(ctr, dtype=np.uint64), key)]
+        assert got == list(want), (ctr, [hex(g) for g in got])
+
+
+def check_dropout_mask_by_hand(o):
+    """Seed 0, offset 0, target q, row 0: features 0..3 use counter (0, 0, 0, 0) and key (0, 0),
+    whose words are the first known answer above; with p = 1/2 (threshold 2^31) word
+    0x6627e8d5 drops feature 0 and the other three keep theirs; with p = 0.1 all four are kept;
+    p = 0 keeps everything."""
+    assert o.dropout_threshold(0.5) == 2 ** 31 and o.dropout_threshold(0.0) == 0
+    assert o.dropout_keep(1, 4, 0, 0.5, 0, 0).tolist() == [[False, True, True, True]]
+    assert o.dropout_keep(1, 4, 0, 0.1, 0, 0).tolist() == [[True, True, True, True]]
+    assert o.dropout_keep(3, 10, 2, 0.0, 5, 9).all()
+
+
+def check_dropout_statistics(o):
+    """Keep rate within 5 standard deviations of 1 - p over 2^19 features; the masks of the
+    three adapters, and of two offsets, are different (and equal for equal arguments); a row
+    subset gets exactly the rows of the full mask."""
+    n = 512 * 1024
+    for p in (0.05, 0.1, 0.5):
+        keep = o.dropout_keep(512, 1024, 1, p, 1234567890123, 77)
+        sd = math.sqrt(p * (1 - p) / n)
+        assert abs(keep.mean() - (1 - p)) < 5 * sd, (p, keep.mean())
+    m = [o.dropout_keep(64, 256, t, 0.3, 42, 5) for t in range(3)]
+    assert not np.array_equal(m[0], m[1]) and not np.array_equal(m[1], m[2])
+    assert not np.array_equal(m[0], o.dropout_keep(64, 256, 0, 0.3, 42, 6))
+    assert np.array_equal(m[0], o.dropout_keep(64, 256, 0, 0.3, 42, 5))
+    assert np.array_equal(o.dropout_keep(64, 256, 0, 0.3, 42, 5, rows=[63, 7, 7]), m[0][[63, 7, 7]])
+
+
+def brute_forward_masked(spec, c, inputs):
+    """brute_forward with each adapter's input given explicitly (a dict target -> [T, d])."""
+    x, g, w, bias, A, B, pos = (c["x"], c["gamma"], c["w"], c["bias"], c["a"], c["b"], c["positions"])
+    T, d = x.shape
+    D, N = spec.head_dim, spec.n_out
+    s = spec.lora_alpha / spec.lora_rank if spec.lora_rank else 0.0
+    nq, nkv = spec.n_q_heads * D, spec.n_kv_heads * D
+    blocks = {TQ: (0, nq), TK: (nq, nq + nkv), TV: (nq + nkv, nq + 2 * nkv)}
+    out = []
+    for t in range(T):
+        inv = 1.0 / math.sqrt(sum(x[t][j] * x[t][j] for j in range(d)) / d + spec.eps)
+        h = [x[t][j] * inv * g[j] for j in range(d)]
+        y = [sum(w[n][j] * h[j] for j in range(d)) + (bias[n] if bias is not None else 0.0) for n in range(N)]
+        for tg, (lo, hi) in blocks.items():
+            if spec.lora_targets & tg:
+                hin = inputs[tg][t]
+                u = [sum(A[tg][k][j] * hin[j] for j in range(d)) for k in range(spec.lora_rank)]
+                for n in range(lo, hi):
+                    y[n] += s * sum(B[tg][n - lo][k] * u[k] for k in range(spec.lora_rank))
+        for hs in range(0, nq + nkv, D):
+            for i in range(D // 2):
+                ang = pos[t] * spec.rope_theta ** (-(2.0 * i) / D)
+                a_, b_ = y[hs + i], y[hs + i + D // 2]
+                y[hs + i] = a_ * math.cos(ang) - b_ * math.sin(ang)
+                y[hs + i + D // 2] = b_ * math.cos(ang) + a_ * math.sin(ang)
+        out.append(y)
+    return np.array(out)
+
+
+def check_dropout_forward(o):
+    """With dropout the forward equals scalar loops fed each adapter's masked, rescaled copy of h
+    (the frozen projection sees h itself); p = 0 equals the no-dropout forward bit for bit; a
+    row subset and chunks use the rows' own masks."""
+    spec, c = tiny_case(o, seed=31, T=6, d=12)
+    drop = o.Dropout(p=0.4, seed=987654321, offset=3)
+    h = o.rms_normalise(c["x"], c["gamma"], spec.eps)
+    inputs = {}
+    for i, tg in enumerate((TQ, TK, TV)):
+        keep = [[None] * 12 for _ in range(6)]
+        km = o.dropout_keep(6, 12, i, 0.4, 987654321, 3)
+        inputs[tg] = [[h[t][j] * (1.0 if km[t][j] else 0.0) / 0.6 for j in range(12)] for t in range(6)]
+        del keep
+    got = o.forward(spec, c["x"], c["gamma"], c["w"], c["bias"], c["a"], c["b"], c["positions"], drop)
+    _close(got, brute_forward_masked(spec, c, inputs), 1e-12, "dropout brute force")
+    assert np.array_equal(o.forward(spec, c["x"], c["gamma"], c["w"], c["bias"], c["a"], c["b"], c["positions"],
+                                    o.Dropout(0.0, 99, 1)), _fwd(o, spec, c))
+    rows = [5, 1, 1]
+    _close(o.forward_rows(spec, rows, c["x"], c["gamma"], c["w"], c["bias"], c["a"], c["b"], c["positions"], drop),
+           got[rows], 1e-14, "dropout row subset")
+    _close(o.forward_chunked(spec, c["x"], c["gamma"], c["w"], c["bias"], c["a"], c["b"], c["positions"], chunk=4,
+                             dropout=drop), got, 1e-14, "dropout chunks")
+
+
+def check_dropout_backward_finite_differences(o):
+    """dx, dA, dB with dropout equal central finite differences of <dy, forward> at the same
+    (fixed) masks; p = 0 gives the no-dropout gradients bit for bit."""
+    spec, c = tiny_case(o, seed=32, T=3, d=8, hq=2, hkv=1, D=4, r=2, targets=TQ | TK | TV, max_pos=40)
+    drop = o.Dropout(p=0.3, seed=2024, offset=11)
+    dy = np.random.default_rng(33).standard_normal((3, spec.n_out))
+
+    def loss(cc):
+        return float(np.sum(dy * o.forward(spec, cc["x"], cc["gamma"], cc["w"], cc["bias"], cc["a"], cc["b"],
+                                           cc["positions"], drop)))
+
+    dx, dA, dB = o.backward(spec, c["x"], c["gamma"], c["w"], c["bias"], c["a"], c["b"], c["positions"], dy,
+                            dropout=drop)
+    step = 1e-6
+
+    def fd(get, put):
+        base = get()
+        g = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            plus, minus = base.copy(), base.copy()
+            plus[idx] += step
+            minus[idx] -= step
+            g[idx] = (loss(put(plus)) - loss(put(minus))) / (2 * step)
+        return g
+
+    _close(dx, fd(lambda: c["x"], lambda v: dict(c, x=v)), 1e-7, "dropout dx")
+    for t in c["a"]:
+        _close(dA[t], fd(lambda: c["a"][t], lambda v: dict(c, a={**c["a"], t: v})), 1e-7, f"dropout dA[{t}]")
+        _close(dB[t], fd(lambda: c["b"][t], lambda v: dict(c, b={**c["b"], t: v})), 1e-7, f"dropout dB[{t}]")
+    dx_sub, _, _ = o.backward(spec, c["x"], c["gamma"], c["w"], c["bias"], c["a"], c["b"], c["positions"], dy,
+                              dx_rows=[2, 0], dropout=drop)
+    _close(dx_sub, dx[[2, 0]], 1e-13, "dropout dx row subset")
+    plain = o.backward(spec, c["x"], c["gamma"], c["w"], c["bias"], c["a"], c["b"], c["positions"], dy)
+    zero = o.backward(spec, c["x"], c["gamma"], c["w"], c["bias"], c["a"], c["b"], c["positions"], dy,
+                      dropout=o.Dropout(0.0, 5, 5))
+    assert np.array_equal(plain[0], zero[0])
+
+
 ALL_CHECKS = [check_rms_closed_form, check_rms_constant_row, check_rms_torch, check_scale_invariance,
               check_lora_zero_b, check_lora_merged_weight, check_lora_only,
               check_rope_closed_form, check_rope_complex_form, check_rope_position_zero,
               check_rope_pair_norms_and_v, check_rope_relative, check_brute_force,
               check_forward_rows, check_forward_chunked,
-              check_backward_finite_differences, check_kv_cache_by_hand]
+              check_backward_finite_differences, check_kv_cache_by_hand,
+              check_philox_known_answers, check_dropout_mask_by_hand, check_dropout_statistics,
+              check_dropout_forward, check_dropout_backward_finite_differences]

@@ -160,6 +160,43 @@ def _chunks_overlapping_short(spec, x, gamma, w, bias, a, b, positions, chunk=20
     return out
 
 
+_real_keep = o.dropout_keep
+_real_inputs = o._adapter_inputs
+
+
+def _keep_inverted(n_rows, d, target_index, p, seed, offset, rows=None):
+    m = _real_keep(n_rows, d, target_index, p, seed, offset, rows)
+    return ~m if p > 0 else m
+
+
+def _keep_shared_across_targets(n_rows, d, target_index, p, seed, offset, rows=None):
+    return _real_keep(n_rows, d, 0, p, seed, offset, rows)
+
+
+def _keep_offset_ignored(n_rows, d, target_index, p, seed, offset, rows=None):
+    return _real_keep(n_rows, d, target_index, p, seed, 0, rows)
+
+
+def _dropout_unscaled(spec, h, dropout, rows=None):
+    out = _real_inputs(spec, h, dropout, rows)
+    if dropout is not None and dropout.p > 0:
+        out = {c: v * (1.0 - dropout.p) for c, v in out.items()}
+    return out
+
+
+def _philox_nine_rounds(ctr, key):
+    x = np.asarray(ctr, dtype=np.uint64) & np.uint64(0xFFFFFFFF)
+    x0, x1, x2, x3 = x[..., 0], x[..., 1], x[..., 2], x[..., 3]
+    k0, k1 = np.uint64(key[0]), np.uint64(key[1])
+    m = np.uint64(0xFFFFFFFF)
+    for rnd in range(9):
+        if rnd > 0:
+            k0, k1 = (k0 + np.uint64(0x9E3779B9)) & m, (k1 + np.uint64(0xBB67AE85)) & m
+        p0, p1 = np.uint64(0xD2511F53) * x0, np.uint64(0xCD9E8D57) * x2
+        x0, x1, x2, x3 = (p1 >> np.uint64(32)) ^ x1 ^ k0, p1 & m, (p0 >> np.uint64(32)) ^ x3 ^ k1, p0 & m
+    return np.stack([x0, x1, x2, x3], axis=-1).astype(np.uint32)
+
+
 MUTANTS = {
     "eps outside sqrt": ("rms_inverse", _eps_outside),
     "sum instead of mean": ("rms_inverse", _sum_not_mean),
@@ -182,6 +219,11 @@ MUTANTS = {
     "row subset keeps the first rows' positions": ("forward_rows", _rows_positions_unsliced),
     "chunks restart the positions": ("forward_chunked", _chunks_restart_positions),
     "overlapping chunks, last row unwritten": ("forward_chunked", _chunks_overlapping_short),
+    "dropout keeps the words below the threshold": ("dropout_keep", _keep_inverted),
+    "one dropout mask for all adapters": ("dropout_keep", _keep_shared_across_targets),
+    "dropout offset ignored": ("dropout_keep", _keep_offset_ignored),
+    "dropout without the 1/(1-p) scale": ("_adapter_inputs", _dropout_unscaled),
+    "Philox with nine rounds": ("philox4x32_10", _philox_nine_rounds),
 }
 
 
