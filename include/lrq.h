@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define LRQ_ABI_VERSION 3
+#define LRQ_ABI_VERSION 4
 #define LRQ_MAX_LORA_RANK 64
 
 typedef enum lrq_status {
@@ -109,6 +109,22 @@ typedef struct lrq_desc {
   uint32_t lora_targets; /* OR of LRQ_TARGET_*; 0 = no adapters                       */
   int32_t has_bias;      /* 0 or 1                                                    */
   int32_t variant;       /* lrq_variant; LRQ_VARIANT_AUTO (0) normally                 */
+  /* LoRA dropout (training).  The LoRA configurations on the pages carry a dropout rate
+   * ("Swift-All一文详解：如何用Liger-Kernel提升训练效率", section 3.2, SftArguments; the
+   * LoRAConfig in the usage section of "Liger-Kernel底层优化：新一代内核级推理加速引擎深度解析").
+   * The library's reading: each adapter's input is h * keep_t / (1 - p) with its own keep
+   * mask per target t (the frozen projection sees h itself), which makes the adapter scale
+   * alpha / r / (1 - p).  Feature j of token row i is kept for target t (0 q, 1 k, 2 v) iff
+   * word j % 4 of Philox4x32-10 (Salmon et al., SC 2011) on the counter
+   * (j / 4, i, t, dropout_offset) under the key (low, high 32 bits of dropout_seed) is
+   * >= floor(lora_dropout * 2^32), the rate taken as this float32 value.  Rows are the
+   * call's own token indices 0 .. T-1.  A backward call with the same seed and offset
+   * regenerates the forward's masks.  0 turns dropout off (bit-identical to no dropout);
+   * the decode family does not run dropout (AUTO picks another family; forcing it fails
+   * with UNSUPPORTED).  Inference callers leave these fields 0. */
+  float lora_dropout;      /* p, finite, 0 <= p < 1                                   */
+  uint32_t dropout_offset; /* per-call counter word (e.g. the training step)         */
+  uint64_t dropout_seed;   /* generator key                                           */
 } lrq_desc;
 
 /* Forward: out = RoPE(W h + b + (alpha/r) B (A h)), h = x * inv_rms(x) * gamma.
@@ -118,7 +134,7 @@ typedef struct lrq_desc {
  * INVALID_ARG when: desc is NULL; T < 0; d < 1; Hq < 1; Hkv < 1; Hq % Hkv != 0; D < 2
  *   or odd; dtype unknown; eps < 0 or not finite; theta <= 0 or not finite; lora_targets
  *   has bits other than q|k|v; targets set with r < 1 or alpha not finite; has_bias not
- *   0/1; variant unknown; x, gamma, w_qkv, positions or out NULL (T > 0); bias NULL with
+ *   0/1; variant unknown; lora_dropout not finite or outside [0, 1); x, gamma, w_qkv, positions or out NULL (T > 0); bias NULL with
  *   has_bias; a target's lora_a / lora_b NULL; workspace_bytes below
  *   lrq_workspace_size(desc, 0) or workspace NULL when that size is > 0. */
 lrq_status lrq_forward(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,

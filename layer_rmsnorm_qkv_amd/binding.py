@@ -36,7 +36,8 @@ class LrqDesc(ctypes.Structure):
                 ("eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
                 ("lora_rank", ctypes.c_int32), ("lora_alpha", ctypes.c_float),
                 ("lora_targets", ctypes.c_uint32), ("has_bias", ctypes.c_int32),
-                ("variant", ctypes.c_int32)]
+                ("variant", ctypes.c_int32), ("lora_dropout", ctypes.c_float),
+                ("dropout_offset", ctypes.c_uint32), ("dropout_seed", ctypes.c_uint64)]
 
 
 class LrqMlpDesc(ctypes.Structure):
@@ -122,10 +123,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
 
 
 def make_desc(n_tokens, d_model, n_q_heads, n_kv_heads, head_dim, dtype, eps=1e-6, rope_theta=10000.0,
-              lora_rank=0, lora_alpha=0.0, lora_targets=0, has_bias=0, variant=LRQ_VARIANT_AUTO) -> LrqDesc:
+              lora_rank=0, lora_alpha=0.0, lora_targets=0, has_bias=0, variant=LRQ_VARIANT_AUTO,
+              lora_dropout=0.0, dropout_offset=0, dropout_seed=0) -> LrqDesc:
     return LrqDesc(int(n_tokens), int(d_model), int(n_q_heads), int(n_kv_heads), int(head_dim), int(dtype),
                    float(eps), float(rope_theta), int(lora_rank), float(lora_alpha), int(lora_targets),
-                   int(has_bias), int(variant))
+                   int(has_bias), int(variant), float(lora_dropout), int(dropout_offset) & 0xFFFFFFFF,
+                   int(dropout_seed) & 0xFFFFFFFFFFFFFFFF)
 
 
 def _ptr(t) -> Optional[int]:

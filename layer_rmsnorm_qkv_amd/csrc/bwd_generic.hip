@@ -11,7 +11,8 @@
 // In the bf16 path h, U, G and V are rounded once to bf16 (they are the operands of the
 // products) and everything else stays in fp32.  dA / dB are zeroed by a fill kernel first,
 // so they are overwritten.  The atomics make the summation order of dA / dB vary between
-// runs (within rounding).
+// runs (within rounding).  With LoRA dropout, U_t, dA_t and target t's dh term see only the
+// features that t's keep bits keep, and s = alpha / r / (1 - p).
 #include <algorithm>
 
 #include "lrq_internal.h"
@@ -68,6 +69,13 @@ __global__ __launch_bounds__(kThreads) void bwd_generic_kernel(BwdParams bp) {
     float v = load_elem(x, (row0 + rr) * d + j) * s_inv[rr] * load_elem(gamma, j);
     return kBf16 ? round_bf16(v) : v;
   };
+  // LoRA dropout: does target t's adapter keep feature j of row rr?
+  const int64_t dw = (d + 31) / 32;
+  auto kept = [&](int t, int rr, int64_t j) -> bool {
+    if (!p.dropout) return true;
+    const uint32_t w = p.drop_bits_r[(static_cast<int64_t>(target_slot(p.targets, t)) * p.T + row0 + rr) * dw + j / 32];
+    return (w >> (j % 32)) & 1u;
+  };
 
   // U_t[row][k] = A_t[k] . h[row]: one wave per dot product
   for (int t = 0; t < 3; ++t) {
@@ -77,7 +85,8 @@ __global__ __launch_bounds__(kThreads) void bwd_generic_kernel(BwdParams bp) {
       const int rr = e / p.r, k = e % p.r;
       float s = 0.f;
       if (rr < n_rows)
-        for (int64_t j = lane; j < d; j += 64) s = fmaf(h_at(rr, j), load_elem(a, k * d + j), s);
+        for (int64_t j = lane; j < d; j += 64)
+          if (kept(t, rr, j)) s = fmaf(h_at(rr, j), load_elem(a, k * d + j), s);
       for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
       if (lane == 0) s_u[rr][t * kMaxRank + k] = kBf16 ? round_bf16(s) : s;
     }
@@ -169,16 +178,22 @@ __global__ __launch_bounds__(kThreads) void bwd_generic_kernel(BwdParams bp) {
     for (int m = 0; m < kMaxCols; ++m) {
       const int64_t j = tid + static_cast<int64_t>(m) * kThreads;
       if (j >= d) continue;
-      float hj[kRows];
+      // the adapter's input feature and the factor of its dh term: h and s, or 0 and 0 where
+      // the adapter's dropout drops the feature
+      float hj[kRows], fk[kRows];
 #pragma unroll
-      for (int rr = 0; rr < kRows; ++rr) hj[rr] = rr < n_rows ? h_at(rr, j) : 0.f;
+      for (int rr = 0; rr < kRows; ++rr) {
+        const bool on = rr < n_rows && kept(t, rr, j);
+        hj[rr] = on ? h_at(rr, j) : 0.f;
+        fk[rr] = on ? p.scale : 0.f;
+      }
       for (int k = 0; k < p.r; ++k) {
         const float av = load_elem(a, k * d + j);
         float da = 0.f;
 #pragma unroll
         for (int rr = 0; rr < kRows; ++rr) {
           const float v = s_v[rr][t * kMaxRank + k];
-          acc[rr][m] = fmaf(p.scale * v, av, acc[rr][m]);
+          acc[rr][m] = fmaf(fk[rr] * v, av, acc[rr][m]);
           da = fmaf(v, hj[rr], da);
         }
         atomicAdd(&dat[k * d + j], p.scale * da);

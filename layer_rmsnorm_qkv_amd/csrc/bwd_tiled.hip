@@ -24,6 +24,12 @@
 //   lora_partial  per chunk of tokens: sum V'^T h (all targets) and G_t^T U_t (MFMA)
 //   lora_reduce   dA_t, dB_t = sums over chunks (deterministic order), dB scaled by s
 // h and U are recomputed from x; G and V' live only in the workspace of this call.
+//
+// LoRA dropout (keep masks made before this family runs; s = alpha / r / (1 - p)): the
+// adapters' input is x * keep_t per target t, so U_t and dA_t come from per-target jobs over
+// those masked copies, and target t's dh term keep_t * (V'_t A_t) is no longer one K segment
+// shared by all targets -- the main kernel then runs K over N only and adds each target's
+// masked rank-r product in its epilogue (column-major keep bits: one word per 32 rows).
 #include <algorithm>
 
 #include "lrq_internal.h"
@@ -45,6 +51,7 @@ struct BwdLayout {
   int cpl;      // LoRA gradients: columns per lane (8 when R <= 32, else 4)
   int rpass;    // ranks per pass over M (32 or 64)
   int groups[4];  // work groups per LoRA-gradient job (dA, then each target's dB)
+  int groups_da_t;  // with dropout: groups of each target's dA job (groups[0] = their sum)
   int chunk;    // tokens per partial sum (multiple of 16)
   int chunks;   // token chunks of the LoRA-gradient partial sums
   size_t wt, at, bt[3], ap_all, ap[3], gcat, u, inv, m, pda, pdb[3], total;
@@ -66,7 +73,10 @@ BwdLayout bwd_layout(const FwdParams& p) {
   L.rpass = L.cpl == 8 ? 32 : 64;
   const int colw = 32 * L.cpl;
   int G = 0;
-  L.groups[0] = static_cast<int>((p.d + colw - 1) / colw) * ((R + L.rpass - 1) / L.rpass);
+  // dA: one job over all ranks, or (dropout) one per target over its masked input
+  const int dcols = static_cast<int>((p.d + colw - 1) / colw);
+  L.groups_da_t = dcols * ((p.r + L.rpass - 1) / L.rpass);
+  L.groups[0] = p.dropout ? p.drop_nt * L.groups_da_t : dcols * ((R + L.rpass - 1) / L.rpass);
   G += L.groups[0];
   for (int t = 0; t < 3; ++t) {
     int lo, hi;
@@ -350,6 +360,11 @@ struct MainArgs {
   const uint16_t* wt;    // [d][N]
   const uint16_t* at;    // [d][Rp]
   int N, Rp;
+  // LoRA dropout (DROP): keep bits [slot][d][tw] and each slot's first LoRA column
+  const uint32_t* bits_c;
+  int64_t tw;
+  int nslots, r;
+  int loff[3];
   const uint16_t* x;
   const uint16_t* gamma;
   const float* inv;
@@ -363,6 +378,49 @@ struct MainArgs {
   int remap;
 };
 
+// Dropout epilogue term of one slot: acc += keep * (V'_slot A_slot) on the wave's 64 x 128
+// part of the tile, one 32 x 32 block at a time (K = r rounded up to 16; ranks >= r read 0).
+__device__ __forceinline__ void drop_lora_term(const MainArgs& a, Acc8& ta, int sl, int64_t row0, int64_t col0,
+                                               int wm, int wn, int l32, int h32) {
+  const int off = a.N + a.loff[sl];  // V'_slot's first column in Gcat
+  const uint32_t* __restrict__ bc = a.bits_c + static_cast<int64_t>(sl) * a.d * a.tw;
+  const int ksteps = (a.r + 15) >> 4;
+  const bool vec = (a.r & 7) == 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t rblk = row0 + wm * 64 + i * 32;  // a multiple of 32
+    const int64_t vrow = min(rblk + l32, a.T - 1);
+    const uint16_t* vsrc = a.gcat + vrow * a.K + off;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = col0 + wn * 128 + j * 32 + l32;
+      const uint32_t keep = rblk / 32 < a.tw ? bc[col * a.tw + rblk / 32] : 0u;
+      const uint16_t* asrc = a.at + col * a.Rp + a.loff[sl];
+      floatx16 tmp = floatx16{};
+      for (int kq = 0; kq < ksteps; ++kq) {
+        const int k0 = kq * 16 + h32 * 8;
+        bf16x8 vf, af;
+        if (vec && k0 < a.r) {
+          vf = *reinterpret_cast<const bf16x8*>(vsrc + k0);
+          af = *reinterpret_cast<const bf16x8*>(asrc + k0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const bool in = k0 + e < a.r;
+            vf[e] = __builtin_bit_cast(__bf16, in ? vsrc[k0 + e] : uint16_t{0});
+            af[e] = __builtin_bit_cast(__bf16, in ? asrc[k0 + e] : uint16_t{0});
+          }
+        }
+        tmp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, af, tmp, 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if ((keep >> ((v >> 2) * 8 + h32 * 4 + (v & 3))) & 1u) ta.acc[i][j][v] += tmp[v];
+    }
+  }
+}
+
+template <bool DROP>
 __global__ __launch_bounds__(kThreads8, 1) void bwd_main_kernel(MainArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kRingBytes];
   const int tid = threadIdx.x;
@@ -383,7 +441,12 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_main_kernel(MainArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) ta.acc[i][j] = floatx16{};
   const Src8 src = make_src8(a.gcat, a.K, row0, a.T, a.wt, a.N, a.N / BK, a.at, a.Rp, wave, lane);
-  kloop8(smem, ta, src, col0, static_cast<int>(a.K / BK), wave, lane);
+  if (DROP) {
+    kloop8(smem, ta, src, col0, a.N / BK, wave, lane);
+    for (int sl = 0; sl < a.nslots; ++sl) drop_lora_term(a, ta, sl, row0, col0, wm, wn, l32, h32);
+  } else {
+    kloop8(smem, ta, src, col0, static_cast<int>(a.K / BK), wave, lane);
+  }
 
   // epilogue: dx = inv * gamma * dh - m * x for the lane's rows and columns
   // (lane rows: 64 wm + 32 i + 8 (v / 4) + 4 h32 + v % 4; columns 128 wn + 32 j + l32)
@@ -428,13 +491,14 @@ struct LoraJob {
   int64_t ldp;
   int ranks;
   const float* inv;     // per-token factor folded into P, or nullptr
-  float* out;           // [chunks][ranks][cols]
+  float* out;           // [chunks][ranks][cols], chunk c at out + c * out_chunk
+  int64_t out_chunk;
   int col_groups;       // column groups of 32 * CPL
   int groups;           // col_groups * rank passes
 };
 
 struct LoraArgs {
-  LoraJob job[4];
+  LoraJob job[6];  // dA (one, or one per target with dropout), then each target's dB
   int njobs;
   int chunk;   // tokens per chunk, a multiple of 16
   int chunks;
@@ -593,7 +657,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void lo
     lora_steps<CPL, RB, false>(src, rows, acc);
 
   // lane: rank k0 + 32 b + l32; rows i of the 32x32 result are columns c0 + CPL * i + c
-  float* o = j.out + static_cast<int64_t>(chunk) * j.ranks * j.cols;
+  float* o = j.out + static_cast<int64_t>(chunk) * j.out_chunk;
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
     const int k = k0 + 32 * b + l32;
@@ -772,7 +836,24 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
         vj.scale = p.scale;
         vj.inv = nullptr;
       }
-      for (int c0 = 0; c0 < L.R; c0 += 32 * rb) {
+      for (int t = 0; t < 3 && p.dropout; ++t) {
+        // dropout: U_t = bf16(inv (x * keep_t) A'_t^T), one job per target
+        if (!(p.targets & (1u << t))) continue;
+        RankJob& uj = ra2.job[nj++];
+        uj.a = p.drop_xm + static_cast<int64_t>(target_slot(p.targets, t)) * p.T * p.d;
+        uj.lda = p.d;
+        uj.bs = at<uint16_t>(ws, L.ap[t]);
+        uj.ldb = p.d;
+        uj.r = p.r;
+        uj.nk = static_cast<int>(p.d / BK);
+        uj.out = at<uint16_t>(ws, L.u);
+        uj.ldo = L.R;
+        uj.col0 = L.off[t];
+        uj.pad_to = uj.col0 + p.r;
+        uj.scale = 1.0f;
+        uj.inv = at<float>(ws, L.inv);
+      }
+      for (int c0 = 0; c0 < L.R && !p.dropout; c0 += 32 * rb) {
         RankJob& uj = ra2.job[nj++];
         uj.a = static_cast<const uint16_t*>(p.x);
         uj.lda = p.d;
@@ -813,27 +894,56 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
     const int n_mt = static_cast<int>((p.T + BM - 1) / BM);
     ma.items = n_mt * ma.n_nt;
     ma.remap = ma.items % 8 == 0;
+    if (p.dropout) {
+      ma.bits_c = p.drop_bits_c;
+      ma.tw = (p.T + 31) / 32;
+      ma.r = p.r;
+      for (int t = 0; t < 3; ++t)
+        if (p.targets & (1u << t)) ma.loff[ma.nslots++] = L.off[t];
+    }
     timing_begin(s);
-    hipLaunchKernelGGL(bwd_main_kernel, dim3(ma.items), dim3(kThreads8), 0, s, ma);
+    if (p.dropout)
+      hipLaunchKernelGGL(bwd_main_kernel<true>, dim3(ma.items), dim3(kThreads8), 0, s, ma);
+    else
+      hipLaunchKernelGGL(bwd_main_kernel<false>, dim3(ma.items), dim3(kThreads8), 0, s, ma);
     timing_end(s);
 
     if (lora) {
       // ---- LoRA gradient partial sums
       LoraArgs la{};
       int nj = 0, items = 0;
-      LoraJob& ja = la.job[nj];
-      ja.mat = static_cast<const uint16_t*>(p.x);
-      ja.ldm = p.d;
-      ja.cols = static_cast<int>(p.d);
-      ja.pv = at<uint16_t>(ws, L.gcat) + p.N;
-      ja.ldp = L.K;
-      ja.ranks = L.R;
-      ja.inv = at<float>(ws, L.inv);
-      ja.out = at<float>(ws, L.pda);
-      ja.groups = L.groups[0];
-      ja.col_groups = static_cast<int>(p.d / (32 * L.cpl));
-      items += ja.groups;
-      ++nj;
+      if (!p.dropout) {
+        LoraJob& ja = la.job[nj++];
+        ja.mat = static_cast<const uint16_t*>(p.x);
+        ja.ldm = p.d;
+        ja.cols = static_cast<int>(p.d);
+        ja.pv = at<uint16_t>(ws, L.gcat) + p.N;
+        ja.ldp = L.K;
+        ja.ranks = L.R;
+        ja.inv = at<float>(ws, L.inv);
+        ja.out = at<float>(ws, L.pda);
+        ja.out_chunk = static_cast<int64_t>(L.R) * p.d;
+        ja.groups = L.groups[0];
+        ja.col_groups = static_cast<int>(p.d / (32 * L.cpl));
+        items += ja.groups;
+      }
+      for (int t = 0; t < 3 && p.dropout; ++t) {
+        // dropout: target t's ranks against its masked input, into the same partial-sum rows
+        if (!(p.targets & (1u << t))) continue;
+        LoraJob& ja = la.job[nj++];
+        ja.mat = p.drop_xm + static_cast<int64_t>(target_slot(p.targets, t)) * p.T * p.d;
+        ja.ldm = p.d;
+        ja.cols = static_cast<int>(p.d);
+        ja.pv = at<uint16_t>(ws, L.gcat) + p.N + L.off[t];
+        ja.ldp = L.K;
+        ja.ranks = p.r;
+        ja.inv = at<float>(ws, L.inv);
+        ja.out = at<float>(ws, L.pda) + static_cast<int64_t>(L.off[t]) * p.d;
+        ja.out_chunk = static_cast<int64_t>(L.R) * p.d;
+        ja.groups = L.groups_da_t;
+        ja.col_groups = static_cast<int>(p.d / (32 * L.cpl));
+        items += ja.groups;
+      }
       for (int t = 0; t < 3; ++t) {
         if (!(p.targets & (1u << t))) continue;
         LoraJob& jb = la.job[nj++];
@@ -845,6 +955,7 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
         jb.ranks = p.r;
         jb.inv = nullptr;
         jb.out = at<float>(ws, L.pdb[t]);
+        jb.out_chunk = static_cast<int64_t>(p.r) * nt[t];
         jb.groups = L.groups[t + 1];
         jb.col_groups = (nt[t] + 32 * L.cpl - 1) / (32 * L.cpl);
         items += jb.groups;

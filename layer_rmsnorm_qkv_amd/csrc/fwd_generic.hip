@@ -9,6 +9,8 @@
 //      touches in LDS; accumulate W h and U = A h in fp32;
 //   3. epilogue: + (alpha/r) B U (U rounded once to bf16 in the bf16 path), + bias,
 //      rotation of q and k pairs, one store.
+// With LoRA dropout, U_t sums only the features that target t's keep bits keep, and the
+// scale is alpha / r / (1 - p).
 // h and U live only in LDS and registers.  This family is the float32 path and the
 // fallback for shapes the MFMA kernels do not cover; it uses plain FMA arithmetic.
 #include "lrq_internal.h"
@@ -140,7 +142,20 @@ __global__ __launch_bounds__(kThreads) void fwd_generic_kernel(FwdParams p) {
       if (e < kRows * n_u) {
         const int rr = e / n_u, j = e % n_u;
         float s = u_acc[i];
-        for (int kk = 0; kk < kChunk; ++kk) s = fmaf(s_h[rr][kk], s_a[j][kk], s);
+        if (p.dropout) {
+          // the adapter's own keep bits of this row and chunk (kChunk = 32: one word)
+          int tj = 0;
+          for (int t = 0; t < 3; ++t)
+            if (u_off[t] >= 0 && j >= u_off[t] && j < u_off[t] + p.r) tj = t;
+          const int64_t row = row0 + rr;
+          const uint32_t keep =
+              row < p.T ? p.drop_bits_r[(static_cast<int64_t>(target_slot(p.targets, tj)) * p.T + row) *
+                                            ((d + 31) / 32) + k0 / kChunk]
+                        : 0u;
+          for (int kk = 0; kk < kChunk; ++kk) s = fmaf((keep >> kk) & 1u ? s_h[rr][kk] : 0.f, s_a[j][kk], s);
+        } else {
+          for (int kk = 0; kk < kChunk; ++kk) s = fmaf(s_h[rr][kk], s_a[j][kk], s);
+        }
         u_acc[i] = s;
       }
     }

@@ -24,6 +24,8 @@
 //     (K = r rounded up to 16) before the epilogue of every tile of that target.
 //   * Workgroup ids are remapped so that the runs of one token tile share an XCD (and its
 //     L2) when the grid is a multiple of the XCD count.
+//   * LoRA dropout: the U pass of target t reads x * keep_t (made with the keep bits before
+//     this kernel) instead of x; the scale s is then alpha / r / (1 - p).
 //   * Epilogue: row sums of squares -> inv, bias, RoPE on q and k heads (angle pos * omega_i
 //     reduced in double precision to a fraction of a turn, then the hardware sin / cos),
 //     bf16 store.
@@ -53,6 +55,7 @@ struct TiledArgs {
   const uint16_t* x;
   const uint16_t* wg;     // W' = bf16(W * gamma) [N][d] (workspace)
   const uint16_t* ag[3];  // A'_t = bf16(A_t * gamma) [r][d] (workspace)
+  const uint16_t* xm[3];  // LoRA dropout: x * keep_t [T][d], the adapter's input (DROP only)
   const uint16_t* bias;  // nullptr without bias
   const uint16_t* b[3];
   const int32_t* pos;
@@ -120,7 +123,7 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[4][4], const Ep
   }
 }
 
-template <int RB>
+template <int RB, bool DROP>
 __global__ __launch_bounds__(kThreads, 1) void fwd_tiled_kernel(TiledArgs p) {
   using L = Lay<RB>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[L::kBytes];
@@ -163,7 +166,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiled_kernel(TiledArgs p) {
       // U_t = x A'_t^T for the token tile; bf16(s U) kept for the rest of the run (ranks >= r
       // re-read A'_t row r - 1 and are stored as 0)
       floatx16 u[RB == 2 ? 4 : 2];
-      rankpass<RB>(smem, src, make_rank_src(p.ag[t], d, p.r, RB, wave, lane), nk, wave, lane, u);
+      if (DROP) {
+        // LoRA dropout: the adapter reads its masked copy of the x tile
+        const Src sm = make_src(p.xm[t], d, row0, T, p.wg, d, wave, lane);
+        rankpass<RB>(smem, sm, make_rank_src(p.ag[t], d, p.r, RB, wave, lane), nk, wave, lane, u);
+      } else {
+        rankpass<RB>(smem, src, make_rank_src(p.ag[t], d, p.r, RB, wave, lane), nk, wave, lane, u);
+      }
 #pragma unroll
       for (int i = 0; i < (RB == 2 ? 4 : 2); ++i) {
         const int rank = rank_col<RB>(wn, l32);
@@ -381,7 +390,9 @@ hipError_t launch_fwd_tiled(const FwdParams& p, hipStream_t s) {
     srcs[t] = static_cast<const uint16_t*>(p.a[t]);
     a.ag[t] = nullptr;
     a.b[t] = static_cast<const uint16_t*>(p.b[t]);
+    a.xm[t] = nullptr;
     if (p.targets & (1u << t)) {
+      if (p.dropout) a.xm[t] = p.drop_xm + static_cast<int64_t>(slots) * p.T * p.d;
       a.ag[t] = ws + (static_cast<int64_t>(w_rows) + static_cast<int64_t>(slots) * p.r) * p.d;
       slot_t[slots++] = t;
     }
@@ -419,10 +430,21 @@ hipError_t launch_fwd_tiled(const FwdParams& p, hipStream_t s) {
   const int rb = p.targets ? (p.r <= 32 ? 1 : 2) : 0;
   dim3 grid(a.items), block(kThreads);
   timing_begin(s);
+  const bool drop = p.dropout;
   switch (rb) {
-    case 0: hipLaunchKernelGGL(fwd_tiled_kernel<0>, grid, block, 0, s, a); break;
-    case 1: hipLaunchKernelGGL(fwd_tiled_kernel<1>, grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL(fwd_tiled_kernel<2>, grid, block, 0, s, a); break;
+    case 0: hipLaunchKernelGGL((fwd_tiled_kernel<0, false>), grid, block, 0, s, a); break;
+    case 1:
+      if (drop)
+        hipLaunchKernelGGL((fwd_tiled_kernel<1, true>), grid, block, 0, s, a);
+      else
+        hipLaunchKernelGGL((fwd_tiled_kernel<1, false>), grid, block, 0, s, a);
+      break;
+    default:
+      if (drop)
+        hipLaunchKernelGGL((fwd_tiled_kernel<2, true>), grid, block, 0, s, a);
+      else
+        hipLaunchKernelGGL((fwd_tiled_kernel<2, false>), grid, block, 0, s, a);
+      break;
   }
   timing_end(s);
   return hipGetLastError();

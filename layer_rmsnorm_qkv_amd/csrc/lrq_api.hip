@@ -146,6 +146,8 @@ lrq_status check_desc(const lrq_desc* d, lrq::FwdParams& p) {
   const int64_t N = static_cast<int64_t>(d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim;
   if (N > (1 << 24) || d->d_model > (1 << 24) || d->n_tokens > (int64_t{1} << 31) - 1)
     return fail(LRQ_ERR_UNSUPPORTED, "sizes beyond the supported range");
+  if (!std::isfinite(d->lora_dropout) || d->lora_dropout < 0.f || d->lora_dropout >= 1.f)
+    return fail(LRQ_ERR_INVALID_ARG, "lora_dropout must be finite and in [0, 1)");
   if (d->lora_targets && d->lora_rank > LRQ_MAX_LORA_RANK)
     return fail(LRQ_ERR_UNSUPPORTED, "lora_rank %d > %d", d->lora_rank, LRQ_MAX_LORA_RANK);
 
@@ -166,6 +168,15 @@ lrq_status check_desc(const lrq_desc* d, lrq::FwdParams& p) {
   p.scale = d->lora_targets ? d->lora_alpha / static_cast<float>(d->lora_rank) : 0.f;
   p.has_bias = d->has_bias;
   p.esize = d->dtype == LRQ_F32 ? 4 : 2;
+  p.dropout = d->lora_targets != 0 && d->lora_dropout > 0.f;
+  if (p.dropout) {
+    // inverted dropout: the kept features' 1 / (1 - p) joins the adapter scale
+    p.scale = d->lora_alpha / static_cast<float>(d->lora_rank) / (1.f - d->lora_dropout);
+    p.drop_nt = __builtin_popcount(d->lora_targets);
+    p.drop_thr = static_cast<uint32_t>(std::floor(static_cast<double>(d->lora_dropout) * 4294967296.0));
+    p.drop_offset = d->dropout_offset;
+    p.drop_seed = d->dropout_seed;
+  }
   return LRQ_OK;
 }
 
@@ -186,7 +197,7 @@ int select(const lrq_desc* d, const lrq::FwdParams& p, bool backward) {
   }
   const bool bf16 = d->dtype == LRQ_BF16;
   const bool tiled = bf16 && lrq::tiled_supports(p);
-  const bool decode = bf16 && lrq::decode_supports(p);
+  const bool decode = bf16 && !p.dropout && lrq::decode_supports(p);
   switch (d->variant) {
     case LRQ_VARIANT_AUTO:
       if (decode && p.T <= kDecodeMaxTokens) return LRQ_VARIANT_DECODE;
@@ -223,11 +234,29 @@ PrepLayout prep_layout(const lrq_desc* d, const lrq::FwdParams& p, bool for_back
   return L;
 }
 
-size_t workspace_for(int variant, const lrq::FwdParams& p, bool backward) {
+size_t family_workspace(int variant, const lrq::FwdParams& p, bool backward) {
   if (backward) return variant == LRQ_VARIANT_TILED ? lrq::bwd_tiled_workspace_bytes(p) : 0;
   if (variant == LRQ_VARIANT_TILED) return lrq::tiled_workspace_bytes(p);
   if (variant == LRQ_VARIANT_DECODE) return lrq::decode_workspace_bytes(p);
   return 0;
+}
+
+size_t al256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+// The family's own workspace, then (with LoRA dropout) the mask region: the tiled families
+// also take the masked adapter inputs, and the tiled backward the column-major bits.
+size_t workspace_for(int variant, const lrq::FwdParams& p, bool backward) {
+  const size_t base = family_workspace(variant, p, backward);
+  if (!p.dropout) return base;
+  const bool tiled = variant == LRQ_VARIANT_TILED;
+  return al256(base) + lrq::dropout_region_bytes(p, tiled && backward, tiled);
+}
+
+hipError_t launch_dropout(int variant, lrq::FwdParams& p, bool backward, hipStream_t s) {
+  if (!p.dropout) return hipSuccess;
+  const bool tiled = variant == LRQ_VARIANT_TILED;
+  void* region = static_cast<unsigned char*>(p.ws) + al256(family_workspace(variant, p, backward));
+  return lrq::launch_dropout_masks(p, region, tiled && backward, tiled, s);
 }
 
 lrq_status check_common_ptrs(const lrq_desc* d, lrq::FwdParams& p, const void* x, const void* gamma,
@@ -380,7 +409,8 @@ lrq_status lrq_forward_prepared(const lrq_desc* desc, const void* x, const void*
     p.kv_num_slots = kv->num_slots;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
+  hipError_t e = launch_dropout(v, p, false, s);
+  if (e != hipSuccess) return hip_status(e, "dropout masks");
   g_timing.kind = 0;
   switch (v) {
     case LRQ_VARIANT_TILED: e = lrq::launch_fwd_tiled(p, s); break;
@@ -484,7 +514,8 @@ lrq_status lrq_backward_prepared(const lrq_desc* desc, const void* x, const void
   bp.f.ws = workspace;
   bp.f.ws_bytes = workspace_bytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
+  hipError_t e = launch_dropout(v, bp.f, true, s);
+  if (e != hipSuccess) return hip_status(e, "dropout masks");
   g_timing.kind = 1;
   if (v == LRQ_VARIANT_TILED)
     e = lrq::launch_bwd_tiled(bp, s);

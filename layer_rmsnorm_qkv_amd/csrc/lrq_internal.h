@@ -42,6 +42,15 @@ struct FwdParams {
   void* kv_v;
   const int32_t* kv_slots;  // [T]; slots outside [0, kv_num_slots) are skipped
   int64_t kv_num_slots;
+  // LoRA dropout of the adapters' input (dropout.hip); scale above is then alpha / r / (1 - p)
+  bool dropout;             // p > 0 with targets
+  int drop_nt;              // mask slots = number of targets, in target order
+  uint32_t drop_thr;        // floor(p * 2^32): a generator word below it drops its feature
+  uint32_t drop_offset;
+  uint64_t drop_seed;
+  const uint32_t* drop_bits_r;  // [drop_nt][T][ceil(d / 32)] keep bits, row-major
+  const uint32_t* drop_bits_c;  // [drop_nt][d][ceil(T / 32)] keep bits, column-major, or nullptr
+  const uint16_t* drop_xm;      // [drop_nt][T][d] bf16 x * keep (tiled families), or nullptr
 };
 
 struct BwdParams {
@@ -72,6 +81,16 @@ struct MlpParams {
 bool mlp_supports(const MlpParams& p);
 size_t mlp_workspace_bytes(const MlpParams& p);
 hipError_t launch_mlp(const MlpParams& p, hipStream_t s);
+
+// LoRA dropout (dropout.hip): bytes of the mask region that follows a family's workspace
+// (row bits, then the column bits if `cols`, then the masked inputs if `xm`), and the launch
+// that fills it and points p.drop_* into it.  Slot s of the region belongs to the s-th target
+// in q, k, v order.
+size_t dropout_region_bytes(const FwdParams& p, bool cols, bool xm);
+hipError_t launch_dropout_masks(FwdParams& p, void* region, bool cols, bool xm, hipStream_t s);
+__host__ __device__ inline int target_slot(uint32_t targets, int t) {
+  return static_cast<int>((targets & 1u) * (t > 0) + ((targets >> 1) & 1u) * (t > 1));
+}
 
 // Column range [lo, hi) of target t.
 __host__ __device__ inline void target_cols(const FwdParams& p, int t, int& lo, int& hi) {

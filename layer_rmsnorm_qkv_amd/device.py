@@ -7,7 +7,7 @@ operator happens here.
 """
 from __future__ import annotations
 
-from typing import Dict, Optional
+from typing import Dict, Optional, Tuple
 
 import numpy as np
 
@@ -20,24 +20,29 @@ def torch_dtype(w: Workload):
     return torch.float32 if w.dtype == "f32" else torch.bfloat16
 
 
-def desc_for(w: Workload, n_tokens: Optional[int] = None, variant: int = B.LRQ_VARIANT_AUTO) -> B.LrqDesc:
+def desc_for(w: Workload, n_tokens: Optional[int] = None, variant: int = B.LRQ_VARIANT_AUTO,
+             dropout: Optional[Tuple[float, int, int]] = None) -> B.LrqDesc:
+    """Descriptor of workload ``w``; ``dropout`` = (rate, seed, offset) turns on LoRA dropout."""
+    p, seed, offset = dropout if dropout is not None else (0.0, 0, 0)
     return B.make_desc(w.n_tokens if n_tokens is None else n_tokens, w.d_model, w.n_q_heads, w.n_kv_heads,
                        w.head_dim, B.LRQ_F32 if w.dtype == "f32" else B.LRQ_BF16, w.eps, w.rope_theta,
                        w.lora_rank if w.lora_targets else 0, w.lora_alpha, w.lora_targets,
-                       1 if w.has_bias else 0, variant)
+                       1 if w.has_bias else 0, variant, lora_dropout=p, dropout_offset=offset,
+                       dropout_seed=seed)
 
 
 class DeviceProblem:
     """All device tensors of one forward (+ backward) call."""
 
     def __init__(self, w: Workload, inputs: Dict[str, object], device: str = "cuda",
-                 variant: int = B.LRQ_VARIANT_AUTO, backward: bool = False):
+                 variant: int = B.LRQ_VARIANT_AUTO, backward: bool = False,
+                 dropout: Optional[Tuple[float, int, int]] = None):
         import torch
         self.w = w
         dt = torch_dtype(w)
         T = inputs["x"].shape[0]
         self.T = T
-        self.desc = desc_for(w, T, variant)
+        self.desc = desc_for(w, T, variant, dropout)
 
         def up(a):
             return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dt)

@@ -37,15 +37,23 @@ def oracle_forward(w, inp, rows=None):
                           inp["positions"])
 
 
-# Per-element bound |g - o| <= C_REL |o| + C_ABS rms(reference row), per dtype.  For bf16 the unit
-# roundoff is u = 2^-9: the output rounding contributes at most u |o| (C_REL = 2u leaves room for
-# the fp32 accumulation), and one rounding of each operand of a length-d dot product (the
-# weights with gamma folded in, the LoRA intermediate) adds a random error of about
-# u / sqrt(3) times the RMS of the row's values when W ~ N(0, 1/d) -- so C_ABS = 12u is about
-# 20 standard deviations of that part (a CPU emulation of the kernels' rounding points reaches
-# 0.45 of the bound on 3 million elements), far from a false alarm and still ~40x below the
-# O(rms) error of one wrong element.  Float32 (u = 2^-24) takes the same form with room
-# for the library's sin / cos and accumulation order: C_ABS = 2e-5 (twice the Frobenius bar).
+# Per-element bound |g - o| <= C_REL |o| + C_ABS rms(reference row) [+ C_LORA e_lora], per
+# dtype.  For bf16 (8 significant bits) the unit roundoff is u = 2^-8: the output's own rounding
+# contributes at most u |o| (C_REL = u), and one rounding of each operand of a length-d dot
+# product (the weights with gamma folded in, h or x) adds a random error of about 0.8 u times
+# the RMS of the row's values when W ~ N(0, 1/d), so C_ABS = 6u is about 7 standard deviations
+# of that part (a CPU emulation of the kernels' rounding points reaches 0.45 of the bound on
+# 3 million elements), still ~40x below the O(rms) error of one wrong element.  Float32
+# (u = 2^-24) takes the same form with room for the library's sin / cos and accumulation
+# order: C_ABS = 2e-5 (twice the Frobenius bar).
+#
+# The rank-r LoRA intermediate (U = A h in the forward, V = s G B in the backward) is also
+# rounded once to bf16 before its r-term product, and with few ranks that error does not
+# average out: it is at most u |U_k| per rank, so an element gains at most
+# u * s * sum_k |B_nk| |U_k| (forward; summed over a rotation pair, since RoPE mixes the pair)
+# or u * inv * |gamma_j| * sum_k |V_k| |A_kj| (dx).  Tests whose adapters dominate the output
+# pass that term as e_lora (lora_bound_forward / lora_bound_dx), with C_LORA = 1.25 u (room for
+# U itself carrying fp32 accumulation error before its rounding).
 C_REL = {"bf16": 2.0 ** -8, "f32": 2.0 ** -23}
 C_ABS = {"bf16": 12 * 2.0 ** -9, "f32": 2e-5}
 ROW_FACTOR = 2.0  # per-row relative Frobenius error bar = ROW_FACTOR x the tensor bar
@@ -63,9 +71,13 @@ def row_rel_errors(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(rel))
 
 
-def elem_ratio(got: np.ndarray, ref: np.ndarray, dtype: str, scale: str = "row") -> float:
-    """max over elements of |g - o| / (C_REL |o| + C_ABS s), s = the RMS of the element's reference
-    row (scale="row") or of the whole tensor ("tensor"); <= 1 passes."""
+C_LORA = {"bf16": 1.25 * 2.0 ** -8, "f32": 1.25 * 2.0 ** -24}
+
+
+def elem_ratio(got: np.ndarray, ref: np.ndarray, dtype: str, scale: str = "row", lora=None) -> float:
+    """max over elements of |g - o| / (C_REL |o| + C_ABS s [+ C_LORA e_lora]), s = the RMS of the
+    element's reference row (scale="row") or of the whole tensor ("tensor"), e_lora = ``lora``
+    (an array of the same shape, see lora_bound_*); <= 1 passes."""
     if got.size == 0:
         return 0.0
     err = np.abs(got - ref)
@@ -74,8 +86,62 @@ def elem_ratio(got: np.ndarray, ref: np.ndarray, dtype: str, scale: str = "row")
     else:
         s = np.sqrt(np.mean(ref * ref))
     bound = C_REL[dtype] * np.abs(ref) + C_ABS[dtype] * s
+    if lora is not None:
+        bound = bound + C_LORA[dtype] * lora
     ratio = np.where(bound > 0.0, err / np.where(bound > 0.0, bound, 1.0), np.where(err == 0.0, 0.0, np.inf))
     return float(np.max(ratio))
+
+
+def _keep(w, t_index, dropout, n_rows, rows):
+    if dropout is None or dropout.p == 0.0:
+        return 1.0
+    return o.dropout_keep(n_rows, w.d_model, t_index, dropout.p, dropout.seed, dropout.offset, rows=rows)
+
+
+def lora_bound_forward(w, inp, dropout=None, rows=None) -> np.ndarray:
+    """e_lora of the forward output [rows, N]: s * |U_t| |B_t|^T in target t's columns, with U_t
+    the exact rank-r intermediate (of the dropped-out input), summed over each rotation pair on
+    q and k."""
+    x = np.asarray(inp["x"], np.float64)
+    rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
+    h = o.rms_normalise(x[rows], inp["gamma"], w.eps)
+    p = 0.0 if dropout is None else dropout.p
+    e = np.zeros((len(rows), w.n_out))
+    s = w.lora_alpha / w.lora_rank
+    cols = w.target_columns()
+    for i, t in enumerate((wl.TARGET_Q, wl.TARGET_K, wl.TARGET_V)):
+        if not (w.lora_targets & t):
+            continue
+        hin = h * _keep(w, i, dropout, x.shape[0], rows) / (1.0 - p)
+        u = hin @ np.asarray(inp["a"][t], np.float64).T
+        lo, hi = cols[t]
+        e[:, lo:hi] = s * (np.abs(u) @ np.abs(np.asarray(inp["b"][t], np.float64)).T)
+    cv, half = cols[wl.TARGET_V][0], w.head_dim // 2
+    rot = e[:, :cv].reshape(len(rows), -1, 2, half)
+    pair = rot[:, :, 0, :] + rot[:, :, 1, :]
+    e[:, :cv] = np.stack([pair, pair], axis=2).reshape(len(rows), cv)
+    return e
+
+
+def lora_bound_dx(w, inp, dropout=None, rows=None) -> np.ndarray:
+    """e_lora of dx [rows, d]: inv * |gamma_j| * sum_t keep_t * (|V_t| |A_t|)_j / (1 - p), with
+    V_t = s G_t B_t the exact rank-r intermediate of the backward."""
+    spec = spec_of(w)
+    x = np.asarray(inp["x"], np.float64)
+    rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
+    inv = o.rms_inverse(x, w.eps)[rows]
+    g = o.unrotate_grad(spec, inp["dy"], inp["positions"])[rows]
+    s = w.lora_alpha / w.lora_rank
+    p = 0.0 if dropout is None else dropout.p
+    e = np.zeros((len(rows), w.d_model))
+    cols = w.target_columns()
+    for i, t in enumerate((wl.TARGET_Q, wl.TARGET_K, wl.TARGET_V)):
+        if not (w.lora_targets & t):
+            continue
+        lo, hi = cols[t]
+        v = s / (1.0 - p) * (g[:, lo:hi] @ np.asarray(inp["b"][t], np.float64))
+        e += (np.abs(v) @ np.abs(np.asarray(inp["a"][t], np.float64))) * _keep(w, i, dropout, x.shape[0], rows)
+    return e * inv[:, None] * np.abs(np.asarray(inp["gamma"], np.float64))[None, :]
 
 
 def forward_errors(w, got: np.ndarray, ref: np.ndarray):

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol():
     assert set(syms) == set(B.EXPORTED), syms
     for s in syms:
         assert hasattr(lib, s), s
-    assert B.lrq_abi_version() == 3
+    assert B.lrq_abi_version() == 4
 
 
 def test_desc_layout_matches_header(tmp_path):
@@ -93,7 +93,8 @@ def expect(status, fn, *a, **k):
     ("n_tokens", -1), ("d_model", 0), ("n_q_heads", 0), ("n_kv_heads", 0), ("n_q_heads", 3),
     ("head_dim", 15), ("head_dim", 0), ("dtype", 7), ("eps", -1.0), ("eps", float("nan")),
     ("rope_theta", 0.0), ("rope_theta", float("inf")), ("lora_targets", 8), ("lora_rank", 0),
-    ("lora_alpha", float("nan")), ("has_bias", 2), ("variant", 9)])
+    ("lora_alpha", float("nan")), ("has_bias", 2), ("variant", 9), ("lora_dropout", -0.1),
+    ("lora_dropout", 1.0), ("lora_dropout", float("nan"))])
 def test_invalid_descriptor(field, value):
     expect(B.LRQ_ERR_INVALID_ARG, fwd, good_desc(**{field: value}))
     assert B.lrq_workspace_size(good_desc(**{field: value})) == 0
@@ -121,6 +122,32 @@ def test_forced_variant_that_cannot_run():
         expect(B.LRQ_ERR_UNSUPPORTED, fwd, good_desc(variant=v))
     assert B.lrq_select_variant(good_desc()) == B.LRQ_VARIANT_GENERIC
     assert B.lrq_select_variant(good_desc(), for_backward=True) == B.LRQ_VARIANT_GENERIC
+
+
+def test_dropout_workspace_and_family():
+    # LoRA dropout keeps its keep bits in the workspace: [targets][T][ceil(d / 32)] uint32 for
+    # the generic family (256-byte aligned); without targets the rate is ignored
+    d = good_desc(n_tokens=100, d_model=80, lora_dropout=0.25)
+    assert B.lrq_workspace_size(d) == (2 * 100 * 3 * 4 + 255) // 256 * 256
+    assert B.lrq_workspace_size(d, for_backward=True) == B.lrq_workspace_size(d)
+    assert B.lrq_workspace_size(good_desc(n_tokens=100, d_model=80, lora_dropout=0.25, lora_targets=0)) == 0
+    assert B.lrq_workspace_size(good_desc(n_tokens=100, d_model=80)) == 0
+    # bf16 decode-sized call: the decode family runs no dropout; AUTO picks another one and a
+    # forced decode call is refused
+    dec = dict(n_tokens=4, d_model=1024, n_q_heads=8, n_kv_heads=2, head_dim=128, dtype=B.LRQ_BF16)
+    assert B.lrq_select_variant(good_desc(**dec)) == B.LRQ_VARIANT_DECODE
+    assert B.lrq_select_variant(good_desc(**dec, lora_dropout=0.1)) == B.LRQ_VARIANT_TILED
+    assert B.lrq_select_variant(good_desc(**dec, lora_dropout=0.1, variant=B.LRQ_VARIANT_DECODE)) == -1
+    assert B.lrq_select_variant(good_desc(**dec, lora_dropout=0.1, lora_targets=0,
+                                          variant=B.LRQ_VARIANT_DECODE)) == B.LRQ_VARIANT_DECODE
+    # the tiled families add the masked adapter inputs (bf16 [targets][T][d]) and, in the
+    # backward, column-major bits ([targets][d][ceil(T / 32)] uint32)
+    base = good_desc(**dec, variant=B.LRQ_VARIANT_TILED)
+    drop = good_desc(**dec, variant=B.LRQ_VARIANT_TILED, lora_dropout=0.1)
+    a256 = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    rows, cols, xm = a256(2 * 4 * 32 * 4), a256(2 * 1024 * 1 * 4), a256(2 * 4 * 1024 * 2)
+    assert B.lrq_workspace_size(drop) == a256(B.lrq_workspace_size(base)) + rows + xm
+    assert B.lrq_workspace_size(drop, True) == a256(B.lrq_workspace_size(base, True)) + rows + cols + xm
 
 
 def test_zero_tokens_is_a_noop():
