@@ -183,7 +183,7 @@ def cpu_threads() -> int:
         return os.cpu_count() or 1
 
 
-def cpu_baseline(w, inp, budget_s: float, gpu_rows_fn=None):
+def cpu_baseline(w, inp, budget_s: float, gpu_rows_fn=None, dropout=None):
     """Time the float64 oracle on a bounded, seeded sample of rows of the same workload, with
     the BLAS pool pinned to this process's cores (the count used is reported)."""
     import numpy as np
@@ -202,13 +202,16 @@ def cpu_baseline(w, inp, budget_s: float, gpu_rows_fn=None):
     rng = np.random.default_rng(12345)
     order = rng.permutation(T)
 
+    drop = None if dropout is None else o.Dropout(float(np.float32(dropout[0])), dropout[1], dropout[2])
+
     def run(rows):
         t0 = time.perf_counter()
         out = o.forward_rows(spec, rows, inp["x"], inp["gamma"], inp["w"], inp["bias"], inp["a"], inp["b"],
-                             inp["positions"])
+                             inp["positions"], dropout=drop)
         if w.backward:
+            # the sample's rows as a call of their own (its masks are that call's: same cost)
             o.backward(spec, inp["x"][rows], inp["gamma"], inp["w"], inp["bias"], inp["a"], inp["b"],
-                       inp["positions"][rows], inp["dy"][rows])
+                       inp["positions"][rows], inp["dy"][rows], dropout=drop)
         return time.perf_counter() - t0, out
 
     try:
@@ -268,8 +271,9 @@ def working_set_copies(w, prob, n_copies: int):
     return sets
 
 
-def run_config(name, args, B, wl, DeviceProblem):
-    """Measure one workload: returns its result object (the shape of the top-level line)."""
+def run_config(name, args, B, wl, DeviceProblem, dropout=None):
+    """Measure one workload: returns its result object (the shape of the top-level line).
+    ``dropout`` = (rate, seed, offset) runs it with LoRA dropout."""
     import numpy as np
     import torch
 
@@ -277,7 +281,7 @@ def run_config(name, args, B, wl, DeviceProblem):
     variant = {"auto": B.LRQ_VARIANT_AUTO, "generic": B.LRQ_VARIANT_GENERIC, "tiled": B.LRQ_VARIANT_TILED,
                "decode": B.LRQ_VARIANT_DECODE}[args.variant]
     inp = wl.make_inputs(w, with_dy=w.backward)
-    prob = DeviceProblem(w, inp, variant=variant, backward=w.backward)
+    prob = DeviceProblem(w, inp, variant=variant, backward=w.backward, dropout=dropout)
     vname = B.VARIANT_NAMES[prob.variant]
     stream = torch.cuda.current_stream()
     # frozen weights are prepared once, before any step (untimed setup, as at model load), for
@@ -384,6 +388,7 @@ def run_config(name, args, B, wl, DeviceProblem):
                    "kernel_family": vname, "parallelism": "none (1 GPU)",
                    "pass": "forward+backward" if w.backward else "forward",
                    "kv_cache": bool(args.kv_cache),
+                   "lora_dropout": 0.0 if dropout is None else dropout[0],
                    "weights": "prepared once before the steps" if prob.prepared is not None else
                               "prepared inside every call",
                    "operand_copies": n_copies,
@@ -422,7 +427,8 @@ def run_config(name, args, B, wl, DeviceProblem):
         got = forward(stream)
         torch.cuda.synchronize()
         got = got.float().cpu().numpy().astype(np.float64)
-        res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, gpu_rows_fn=lambda rows: got[rows])
+        res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, gpu_rows_fn=lambda rows: got[rows],
+                                           dropout=dropout)
     del sets, prob, graph
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -535,13 +541,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30, help="untimed steps first (the clocks settle within about 20 steps of sustained MFMA load)")
-    ap.add_argument("--workload", default="all", choices=("all",) + ALL_WORKLOADS,
+    ap.add_argument("--workload", default="all", choices=("all",) + ALL_WORKLOADS + ("train_dropout",),
                     help="all: every workload, the headline (llama2, the largest) on the top level and all five "
                          "under 'configs'")
     ap.add_argument("--variant", default="auto", choices=["auto", "generic", "tiled", "decode"])
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for each cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mlp", action="store_true", help="leave the SwiGLU-MLP workload out of the default run")
+    ap.add_argument("--dropout", type=float, default=0.05,
+                    help="LoRA dropout rate of the extra train_dropout entry of the default run (0: leave it out)")
     ap.add_argument("--no-prepare", action="store_true",
                     help="let every call prepare the frozen weights itself (no lrq_prepare_weights)")
     ap.add_argument("--copies", type=int, default=0,
@@ -587,11 +595,22 @@ def main():
     names = ALL_WORKLOADS if args.workload == "all" else (args.workload,)
     results = {}
     for name in names:
+        if name == "train_dropout":
+            continue
         print(f"[bench] {name}: measuring", file=sys.stderr, flush=True)
         results[name] = run_config(name, args, B, wl, DeviceProblem)
         r = results[name]
         print(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step, {r['value']:.4g} tokens/s, roofline "
               f"{r['roofline']['frac']:.3f} of {r['roofline']['kernel']}", file=sys.stderr, flush=True)
+    if (args.workload == "all" and args.dropout > 0) or args.workload == "train_dropout":
+        # the training step again with LoRA dropout (default: the rate of the pages' SFT example)
+        print("[bench] train_dropout: measuring", file=sys.stderr, flush=True)
+        results["train_dropout"] = run_config("train", args, B, wl, DeviceProblem,
+                                              dropout=(args.dropout or 0.05, 0x5EED, 1))
+        r = results["train_dropout"]
+        print(f"[bench] train_dropout: {r['ms_per_step']:.4f} ms/step, roofline {r['roofline']['frac']:.3f}",
+              file=sys.stderr, flush=True)
+        names = tuple(n for n in names if n != "train_dropout") + ("train_dropout",)
     if args.workload == "all" and not args.no_mlp:
         print("[bench] mlp_llama3: measuring", file=sys.stderr, flush=True)
         results["mlp_llama3"] = run_mlp_config("mlp_llama3", args, B, wl)

@@ -25,11 +25,11 @@
 //   lora_reduce   dA_t, dB_t = sums over chunks (deterministic order), dB scaled by s
 // h and U are recomputed from x; G and V' live only in the workspace of this call.
 //
-// LoRA dropout (keep masks made before this family runs; s = alpha / r / (1 - p)): the
-// adapters' input is x * keep_t per target t, so U_t and dA_t come from per-target jobs over
-// those masked copies, and target t's dh term keep_t * (V'_t A_t) is no longer one K segment
-// shared by all targets -- the main kernel then runs K over N only and adds each target's
-// masked rank-r product in its epilogue (column-major keep bits: one word per 32 rows).
+// LoRA dropout (s = alpha / r / (1 - p)): the rows pass also makes every target's keep bits and
+// masked input x * keep_t for its row (Philox work overlapped with the pass's loads).  U_t and
+// dA_t then come from per-target jobs over the masked copies, and target t's dh term
+// keep_t * (V'_t A_t) is no longer one K segment shared by all targets: the main kernel starts
+// its accumulators at the sum of the targets' masked rank-r products and runs K over N only.
 #include <algorithm>
 
 #include "lrq_internal.h"
@@ -228,6 +228,12 @@ struct RowsArgs {
   int64_t K;
   float eps;
   double log2_theta;
+  // LoRA dropout (nt > 0): keep bits [nt][T][d / 8] bytes and x * keep [nt][T][d] per slot
+  int nt;
+  int target[3];
+  uint32_t thr, offset, seed_lo, seed_hi;
+  uint8_t* bits;
+  uint16_t* xm;
 };
 
 __global__ __launch_bounds__(256) void rows_kernel(RowsArgs a) {
@@ -243,6 +249,14 @@ __global__ __launch_bounds__(256) void rows_kernel(RowsArgs a) {
     for (int e = 0; e < 4; ++e) {
       const float lo = __uint_as_float(w4[e] << 16), hi = __uint_as_float(w4[e] & 0xffff0000u);
       ss = fmaf(lo, lo, fmaf(hi, hi, ss));
+    }
+    for (int sl = 0; sl < a.nt; ++sl) {
+      // dropout: this row's keep bits of features j .. j + 7 for slot sl, and its masked input
+      const uint32_t keep = dropout_byte(j, static_cast<uint32_t>(t), static_cast<uint32_t>(a.target[sl]),
+                                         a.offset, a.thr, a.seed_lo, a.seed_hi);
+      const int64_t srow = static_cast<int64_t>(sl) * a.T + t;
+      a.bits[srow * (a.d / 8) + j / 8] = static_cast<uint8_t>(keep);
+      *reinterpret_cast<uint4*>(a.xm + srow * a.d + j) = mask_bf16x8(v, keep);
     }
   }
 #pragma unroll
@@ -360,9 +374,8 @@ struct MainArgs {
   const uint16_t* wt;    // [d][N]
   const uint16_t* at;    // [d][Rp]
   int N, Rp;
-  // LoRA dropout (DROP): keep bits [slot][d][tw] and each slot's first LoRA column
-  const uint32_t* bits_c;
-  int64_t tw;
+  // LoRA dropout (DROP): keep bits [slot][T][d / 32] words and each slot's first LoRA column
+  const uint32_t* bits;
   int nslots, r;
   int loff[3];
   const uint16_t* x;
@@ -378,49 +391,62 @@ struct MainArgs {
   int remap;
 };
 
-// Dropout epilogue term of one slot: acc += keep * (V'_slot A_slot) on the wave's 64 x 128
-// part of the tile, one 32 x 32 block at a time (K = r rounded up to 16; ranks >= r read 0).
-__device__ __forceinline__ void drop_lora_term(const MainArgs& a, Acc8& ta, int sl, int64_t row0, int64_t col0,
-                                               int wm, int wn, int l32, int h32) {
-  const int off = a.N + a.loff[sl];  // V'_slot's first column in Gcat
-  const uint32_t* __restrict__ bc = a.bits_c + static_cast<int64_t>(sl) * a.d * a.tw;
+// Dropout: acc += keep_s * (V'_s A_s) for every slot s, on the wave's 64 x 128 part of the
+// tile before the K loop, one 32 x 32 block at a time and within it one slot at a time (K = r
+// rounded up to 16; ranks >= r read 0).  Lane l32's columns are bit l32 of the row's keep
+// words (col0 + 128 wn) / 32 + j.
+template <int NS>
+__device__ __forceinline__ void drop_lora_init(const MainArgs& a, Acc8& ta, int64_t row0, int64_t col0, int wm,
+                                               int wn, int l32, int h32) {
   const int ksteps = (a.r + 15) >> 4;
   const bool vec = (a.r & 7) == 0;
+  const int64_t dw = a.d / 32;
+  const int64_t wcol = (col0 + wn * 128) / 32;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int64_t rblk = row0 + wm * 64 + i * 32;  // a multiple of 32
+    const int64_t rblk = row0 + wm * 64 + i * 32;
     const int64_t vrow = min(rblk + l32, a.T - 1);
-    const uint16_t* vsrc = a.gcat + vrow * a.K + off;
+    const int64_t rbase = rblk + h32 * 4;  // the lane's 16 rows: rbase + 8 (v / 4) + v % 4
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t col = col0 + wn * 128 + j * 32 + l32;
-      const uint32_t keep = rblk / 32 < a.tw ? bc[col * a.tw + rblk / 32] : 0u;
-      const uint16_t* asrc = a.at + col * a.Rp + a.loff[sl];
-      floatx16 tmp = floatx16{};
-      for (int kq = 0; kq < ksteps; ++kq) {
-        const int k0 = kq * 16 + h32 * 8;
-        bf16x8 vf, af;
-        if (vec && k0 < a.r) {
-          vf = *reinterpret_cast<const bf16x8*>(vsrc + k0);
-          af = *reinterpret_cast<const bf16x8*>(asrc + k0);
-        } else {
+      asm volatile("" ::: "memory");
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const bool in = k0 + e < a.r;
-            vf[e] = __builtin_bit_cast(__bf16, in ? vsrc[k0 + e] : uint16_t{0});
-            af[e] = __builtin_bit_cast(__bf16, in ? asrc[k0 + e] : uint16_t{0});
+      for (int sl = 0; sl < NS; ++sl) {
+        const uint16_t* vsrc = a.gcat + vrow * a.K + a.N + a.loff[sl];
+        const uint16_t* asrc = a.at + col * a.Rp + a.loff[sl];
+        const uint32_t* __restrict__ bits = a.bits + static_cast<int64_t>(sl) * a.T * dw + wcol + j;
+        floatx16 tmp = floatx16{};
+        for (int kq = 0; kq < ksteps; ++kq) {
+          const int k0 = kq * 16 + h32 * 8;
+          bf16x8 vf, af;
+          if (vec && k0 < a.r) {
+            vf = *reinterpret_cast<const bf16x8*>(vsrc + k0);
+            af = *reinterpret_cast<const bf16x8*>(asrc + k0);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const bool in = k0 + e < a.r;
+              vf[e] = __builtin_bit_cast(__bf16, in ? vsrc[k0 + e] : uint16_t{0});
+              af[e] = __builtin_bit_cast(__bf16, in ? asrc[k0 + e] : uint16_t{0});
+            }
           }
+          tmp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, af, tmp, 0, 0, 0);
         }
-        tmp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, af, tmp, 0, 0, 0);
-      }
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        if ((keep >> ((v >> 2) * 8 + h32 * 4 + (v & 3))) & 1u) ta.acc[i][j][v] += tmp[v];
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t keep = bits[min(rbase + (v >> 2) * 8 + (v & 3), a.T - 1) * dw];
+          ta.acc[i][j][v] += ((keep >> l32) & 1u) ? tmp[v] : 0.f;
+        }
+        // the next slot's loads are not hoisted above this block's adds
+        asm volatile("" ::: "memory");
+      }
     }
   }
 }
 
-template <bool DROP>
+// NS: number of dropout slots (0: no dropout; the LoRA term is the K segment past N)
+template <int NS>
 __global__ __launch_bounds__(kThreads8, 1) void bwd_main_kernel(MainArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kRingBytes];
   const int tid = threadIdx.x;
@@ -440,13 +466,9 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_main_kernel(MainArgs a) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) ta.acc[i][j] = floatx16{};
+  if (NS > 0) drop_lora_init<NS>(a, ta, row0, col0, wm, wn, l32, h32);
   const Src8 src = make_src8(a.gcat, a.K, row0, a.T, a.wt, a.N, a.N / BK, a.at, a.Rp, wave, lane);
-  if (DROP) {
-    kloop8(smem, ta, src, col0, a.N / BK, wave, lane);
-    for (int sl = 0; sl < a.nslots; ++sl) drop_lora_term(a, ta, sl, row0, col0, wm, wn, l32, h32);
-  } else {
-    kloop8(smem, ta, src, col0, static_cast<int>(a.K / BK), wave, lane);
-  }
+  kloop8(smem, ta, src, col0, NS > 0 ? a.N / BK : static_cast<int>(a.K / BK), wave, lane);
 
   // epilogue: dx = inv * gamma * dh - m * x for the lane's rows and columns
   // (lane rows: 64 wm + 32 i + 8 (v / 4) + 4 h32 + v % 4; columns 128 wn + 32 j + l32)
@@ -809,6 +831,17 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
     ra.K = L.K;
     ra.eps = p.eps;
     ra.log2_theta = log2(p.theta);
+    if (p.dropout) {
+      ra.nt = p.drop_nt;
+      for (int t = 0, k = 0; t < 3; ++t)
+        if (p.targets & (1u << t)) ra.target[k++] = t;
+      ra.thr = p.drop_thr;
+      ra.offset = p.drop_offset;
+      ra.seed_lo = static_cast<uint32_t>(p.drop_seed);
+      ra.seed_hi = static_cast<uint32_t>(p.drop_seed >> 32);
+      ra.bits = reinterpret_cast<uint8_t*>(p.drop_bits_r);
+      ra.xm = p.drop_xm;
+    }
     hipLaunchKernelGGL(rows_kernel, dim3(static_cast<unsigned>((p.T + 3) / 4)), dim3(256), 0, s, ra);
 
     if (lora) {
@@ -895,17 +928,18 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
     ma.items = n_mt * ma.n_nt;
     ma.remap = ma.items % 8 == 0;
     if (p.dropout) {
-      ma.bits_c = p.drop_bits_c;
-      ma.tw = (p.T + 31) / 32;
+      ma.bits = p.drop_bits_r;
       ma.r = p.r;
       for (int t = 0; t < 3; ++t)
         if (p.targets & (1u << t)) ma.loff[ma.nslots++] = L.off[t];
     }
     timing_begin(s);
-    if (p.dropout)
-      hipLaunchKernelGGL(bwd_main_kernel<true>, dim3(ma.items), dim3(kThreads8), 0, s, ma);
-    else
-      hipLaunchKernelGGL(bwd_main_kernel<false>, dim3(ma.items), dim3(kThreads8), 0, s, ma);
+    switch (p.dropout ? ma.nslots : 0) {
+      case 0: hipLaunchKernelGGL(bwd_main_kernel<0>, dim3(ma.items), dim3(kThreads8), 0, s, ma); break;
+      case 1: hipLaunchKernelGGL(bwd_main_kernel<1>, dim3(ma.items), dim3(kThreads8), 0, s, ma); break;
+      case 2: hipLaunchKernelGGL(bwd_main_kernel<2>, dim3(ma.items), dim3(kThreads8), 0, s, ma); break;
+      default: hipLaunchKernelGGL(bwd_main_kernel<3>, dim3(ma.items), dim3(kThreads8), 0, s, ma); break;
+    }
     timing_end(s);
 
     if (lora) {

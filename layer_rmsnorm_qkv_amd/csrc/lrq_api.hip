@@ -243,20 +243,21 @@ size_t family_workspace(int variant, const lrq::FwdParams& p, bool backward) {
 
 size_t al256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
-// The family's own workspace, then (with LoRA dropout) the mask region: the tiled families
-// also take the masked adapter inputs, and the tiled backward the column-major bits.
+// The family's own workspace, then (with LoRA dropout) the mask region: keep bits, and for the
+// tiled families the masked adapter inputs too.
 size_t workspace_for(int variant, const lrq::FwdParams& p, bool backward) {
   const size_t base = family_workspace(variant, p, backward);
   if (!p.dropout) return base;
-  const bool tiled = variant == LRQ_VARIANT_TILED;
-  return al256(base) + lrq::dropout_region_bytes(p, tiled && backward, tiled);
+  return al256(base) + lrq::dropout_region_bytes(p, variant == LRQ_VARIANT_TILED);
 }
 
+// Points p's dropout fields into the region and fills it, except for the tiled backward, whose
+// rows pass makes the masks itself.
 hipError_t launch_dropout(int variant, lrq::FwdParams& p, bool backward, hipStream_t s) {
   if (!p.dropout) return hipSuccess;
   const bool tiled = variant == LRQ_VARIANT_TILED;
   void* region = static_cast<unsigned char*>(p.ws) + al256(family_workspace(variant, p, backward));
-  return lrq::launch_dropout_masks(p, region, tiled && backward, tiled, s);
+  return lrq::launch_dropout_masks(p, region, tiled, !(tiled && backward), s);
 }
 
 lrq_status check_common_ptrs(const lrq_desc* d, lrq::FwdParams& p, const void* x, const void* gamma,

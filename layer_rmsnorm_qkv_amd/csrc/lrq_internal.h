@@ -48,9 +48,8 @@ struct FwdParams {
   uint32_t drop_thr;        // floor(p * 2^32): a generator word below it drops its feature
   uint32_t drop_offset;
   uint64_t drop_seed;
-  const uint32_t* drop_bits_r;  // [drop_nt][T][ceil(d / 32)] keep bits, row-major
-  const uint32_t* drop_bits_c;  // [drop_nt][d][ceil(T / 32)] keep bits, column-major, or nullptr
-  const uint16_t* drop_xm;      // [drop_nt][T][d] bf16 x * keep (tiled families), or nullptr
+  uint32_t* drop_bits_r;        // [drop_nt][T][ceil(d / 32)] keep bits, row-major
+  uint16_t* drop_xm;            // [drop_nt][T][d] bf16 x * keep (tiled families), or nullptr
 };
 
 struct BwdParams {
@@ -83,11 +82,11 @@ size_t mlp_workspace_bytes(const MlpParams& p);
 hipError_t launch_mlp(const MlpParams& p, hipStream_t s);
 
 // LoRA dropout (dropout.hip): bytes of the mask region that follows a family's workspace
-// (row bits, then the column bits if `cols`, then the masked inputs if `xm`), and the launch
-// that fills it and points p.drop_* into it.  Slot s of the region belongs to the s-th target
-// in q, k, v order.
-size_t dropout_region_bytes(const FwdParams& p, bool cols, bool xm);
-hipError_t launch_dropout_masks(FwdParams& p, void* region, bool cols, bool xm, hipStream_t s);
+// (row bits, then the masked inputs if `xm`), and the launch that points p.drop_* into it and
+// fills it (unless `fill` is false: the tiled backward fills it from its own rows pass).
+// Slot s of the region belongs to the s-th target in q, k, v order.
+size_t dropout_region_bytes(const FwdParams& p, bool xm);
+hipError_t launch_dropout_masks(FwdParams& p, void* region, bool xm, bool fill, hipStream_t s);
 __host__ __device__ inline int target_slot(uint32_t targets, int t) {
   return static_cast<int>((targets & 1u) * (t > 0) + ((targets >> 1) & 1u) * (t > 1));
 }
@@ -124,6 +123,54 @@ __device__ __forceinline__ float load_elem(const float* p, int64_t i) { return p
 __device__ __forceinline__ float load_elem(const uint16_t* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
 __device__ __forceinline__ void store_elem(float* p, int64_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void store_elem(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16_bits(v); }
+
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2,
+// 3", SC 2011) on counter x with key (k0, k1): ten rounds, each multiplying words 0 and 2 by
+// the two multipliers and mixing the 64-bit products' halves with words 1 and 3 and the key;
+// the key is bumped by the two Weyl constants between rounds.  x is replaced by the output.
+__device__ __forceinline__ void philox4x32_10(uint32_t (&x)[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * x[0];
+    const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * x[2];
+    const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ x[1] ^ k0;
+    const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ x[3] ^ k1;
+    x[0] = n0;
+    x[1] = static_cast<uint32_t>(p1);
+    x[2] = n2;
+    x[3] = static_cast<uint32_t>(p0);
+  }
+}
+
+// LoRA dropout keep bits of features j .. j + 7 (j % 4 == 0) of one token row for target t:
+// bit e set iff word (j + e) % 4 of Philox4x32-10 on ((j + e) / 4, row, t, offset) >= thr.
+__device__ __forceinline__ uint32_t dropout_byte(int j, uint32_t row, uint32_t t, uint32_t offset, uint32_t thr,
+                                                 uint32_t k0, uint32_t k1) {
+  uint32_t bits = 0;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    uint32_t x[4] = {static_cast<uint32_t>(j / 4 + q), row, t, offset};
+    philox4x32_10(x, k0, k1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bits |= (x[e] >= thr ? 1u : 0u) << (4 * q + e);
+  }
+  return bits;
+}
+
+// x * keep for 8 bf16 values packed in a 16-byte vector (bit e of keep: element e).
+__device__ __forceinline__ uint4 mask_bf16x8(uint4 v, uint32_t keep) {
+  uint32_t o[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t b2 = keep >> (2 * q);
+    o[q] &= ((b2 & 1u) ? 0x0000ffffu : 0u) | ((b2 & 2u) ? 0xffff0000u : 0u);
+  }
+  return uint4{o[0], o[1], o[2], o[3]};
+}
 
 // RoPE frequency omega_i = theta^(-2i/D) in double precision.
 __device__ __forceinline__ double rope_omega(double theta, int i, int D) {

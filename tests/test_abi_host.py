@@ -140,14 +140,13 @@ def test_dropout_workspace_and_family():
     assert B.lrq_select_variant(good_desc(**dec, lora_dropout=0.1, variant=B.LRQ_VARIANT_DECODE)) == -1
     assert B.lrq_select_variant(good_desc(**dec, lora_dropout=0.1, lora_targets=0,
                                           variant=B.LRQ_VARIANT_DECODE)) == B.LRQ_VARIANT_DECODE
-    # the tiled families add the masked adapter inputs (bf16 [targets][T][d]) and, in the
-    # backward, column-major bits ([targets][d][ceil(T / 32)] uint32)
+    # the tiled families add the masked adapter inputs (bf16 [targets][T][d])
     base = good_desc(**dec, variant=B.LRQ_VARIANT_TILED)
     drop = good_desc(**dec, variant=B.LRQ_VARIANT_TILED, lora_dropout=0.1)
     a256 = lambda n: (n + 255) // 256 * 256  # noqa: E731
-    rows, cols, xm = a256(2 * 4 * 32 * 4), a256(2 * 1024 * 1 * 4), a256(2 * 4 * 1024 * 2)
+    rows, xm = a256(2 * 4 * 32 * 4), a256(2 * 4 * 1024 * 2)
     assert B.lrq_workspace_size(drop) == a256(B.lrq_workspace_size(base)) + rows + xm
-    assert B.lrq_workspace_size(drop, True) == a256(B.lrq_workspace_size(base, True)) + rows + cols + xm
+    assert B.lrq_workspace_size(drop, True) == a256(B.lrq_workspace_size(base, True)) + rows + xm
 
 
 def test_zero_tokens_is_a_noop():
