@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define LRQ_ABI_VERSION 4
+#define LRQ_ABI_VERSION 5
 #define LRQ_MAX_LORA_RANK 64
 
 typedef enum lrq_status {
@@ -86,6 +86,12 @@ typedef enum lrq_status {
 typedef enum lrq_dtype { LRQ_F32 = 0, LRQ_BF16 = 1 } lrq_dtype;
 
 enum { LRQ_TARGET_Q = 1, LRQ_TARGET_K = 2, LRQ_TARGET_V = 4 };
+
+/* Storage of the frozen W_qkv (lrq_desc.weight_format). */
+typedef enum lrq_weight_format {
+  LRQ_WEIGHT_DENSE = 0, /* [N, d] in the call's dtype */
+  LRQ_WEIGHT_NF4 = 1    /* QLoRA base: 4-bit NormalFloat blocks, see lrq_quantize_nf4 */
+} lrq_weight_format;
 
 /* Kernel families; LRQ_VARIANT_AUTO lets the library choose. */
 typedef enum lrq_variant {
@@ -125,6 +131,11 @@ typedef struct lrq_desc {
   float lora_dropout;      /* p, finite, 0 <= p < 1                                   */
   uint32_t dropout_offset; /* per-call counter word (e.g. the training step)         */
   uint64_t dropout_seed;   /* generator key                                           */
+  /* lrq_weight_format of w_qkv.  With LRQ_WEIGHT_NF4 every entry point takes w_qkv as the
+   * buffer that lrq_quantize_nf4 writes (lrq_nf4_weight_size bytes), d must be a multiple of
+   * 64, and the decode family is not used (AUTO picks another one; forcing it fails with
+   * UNSUPPORTED).  Everything else of the call is unchanged. */
+  int32_t weight_format;
 } lrq_desc;
 
 /* Forward: out = RoPE(W h + b + (alpha/r) B (A h)), h = x * inv_rms(x) * gamma.
@@ -134,7 +145,7 @@ typedef struct lrq_desc {
  * INVALID_ARG when: desc is NULL; T < 0; d < 1; Hq < 1; Hkv < 1; Hq % Hkv != 0; D < 2
  *   or odd; dtype unknown; eps < 0 or not finite; theta <= 0 or not finite; lora_targets
  *   has bits other than q|k|v; targets set with r < 1 or alpha not finite; has_bias not
- *   0/1; variant unknown; lora_dropout not finite or outside [0, 1); x, gamma, w_qkv, positions or out NULL (T > 0); bias NULL with
+ *   0/1; variant unknown; lora_dropout not finite or outside [0, 1); weight_format unknown; x, gamma, w_qkv, positions or out NULL (T > 0); bias NULL with
  *   has_bias; a target's lora_a / lora_b NULL; workspace_bytes below
  *   lrq_workspace_size(desc, 0) or workspace NULL when that size is > 0. */
 lrq_status lrq_forward(const lrq_desc* desc, const void* x, const void* gamma, const void* w_qkv,
@@ -272,6 +283,31 @@ const char* lrq_status_string(lrq_status status);
 
 /* Message describing the last error returned on the calling thread ("" if none). */
 const char* lrq_last_error(void);
+
+/* ---- QLoRA base: W_qkv as NF4 blocks.
+ * The pages name QLoRA among the fine-tuning settings these kernels serve ("Liger-Kernel内核级
+ * 优化：GPU利用率飙升至90%以上", opening section; "Swift-All一文详解：如何用Liger-Kernel提升训练
+ * 效率", section 2.3, the QLoRA row of the table; "Liger-Kernel底层优化：新一代内核级推理加速引擎
+ * 深度解析", system-integration section) without defining a stored format.  The library's
+ * format is the QLoRA paper's 4-bit NormalFloat (Dettmers et al., NeurIPS 2023): its published
+ * 16-value code book L, blocks of 64 consecutive weights of a row of W [N, d], one float32
+ * scale per block (the block's largest magnitude), no second-level quantisation.  A weight is
+ * L[code] * scale.  Buffer: codes [N][d / 2] bytes (weight k of a row in the low nibble of byte
+ * k / 2 for even k, the high nibble for odd k), then the scales [N][d / 64] float32 at the
+ * codes' size rounded up to 256 bytes.  Buffers made elsewhere in this layout are accepted. */
+
+/* Bytes of the NF4 buffer of desc's W_qkv (0 for an invalid desc or d % 64 != 0). */
+size_t lrq_nf4_weight_size(const lrq_desc* desc);
+
+/* Quantise W_qkv [N, d] (desc's dtype, dense) into the NF4 buffer w_nf4 (16-byte aligned,
+ * nf4_bytes >= lrq_nf4_weight_size(desc)), on the device.  Per block: y = w / absmax in
+ * float32 (correctly rounded); the code is the number of midpoints (L_i + L_{i+1}) / 2
+ * (float32) that y exceeds, so exact ties take the lower level; an all-zero block gets code 7
+ * (L[7] = 0) and scale 0.  desc->weight_format is ignored here.
+ * INVALID_ARG: invalid desc, NULL pointers, buffer too small; UNSUPPORTED: d % 64 != 0 or
+ * misaligned pointers. */
+lrq_status lrq_quantize_nf4(const lrq_desc* desc, const void* w_qkv, void* w_nf4, size_t nf4_bytes,
+                            void* stream);
 
 /* LRQ_ABI_VERSION of the loaded library. */
 int lrq_abi_version(void);

@@ -19,13 +19,14 @@ LRQ_F32, LRQ_BF16 = 0, 1
 LRQ_TARGET_Q, LRQ_TARGET_K, LRQ_TARGET_V = 1, 2, 4
 LRQ_VARIANT_AUTO, LRQ_VARIANT_GENERIC, LRQ_VARIANT_TILED, LRQ_VARIANT_DECODE = 0, 1, 2, 3
 VARIANT_NAMES = {LRQ_VARIANT_GENERIC: "generic", LRQ_VARIANT_TILED: "tiled", LRQ_VARIANT_DECODE: "decode"}
+LRQ_WEIGHT_DENSE, LRQ_WEIGHT_NF4 = 0, 1
 
 # every symbol include/lrq.h declares
 EXPORTED = ("lrq_forward", "lrq_forward_kv", "lrq_backward", "lrq_workspace_size", "lrq_select_variant",
             "lrq_status_string", "lrq_last_error", "lrq_abi_version", "lrq_kernel_timing",
             "lrq_kernel_time_ms", "lrq_prepared_size", "lrq_prepare_weights", "lrq_forward_prepared",
             "lrq_backward_prepared", "lrq_workspace_size_prepared", "lrq_forward_noalloc",
-            "lrq_mlp_workspace_size", "lrq_mlp_forward")
+            "lrq_mlp_workspace_size", "lrq_mlp_forward", "lrq_nf4_weight_size", "lrq_quantize_nf4")
 LRQ_MLP_GATE, LRQ_MLP_UP, LRQ_MLP_DOWN = 1, 2, 4
 
 
@@ -37,7 +38,8 @@ class LrqDesc(ctypes.Structure):
                 ("lora_rank", ctypes.c_int32), ("lora_alpha", ctypes.c_float),
                 ("lora_targets", ctypes.c_uint32), ("has_bias", ctypes.c_int32),
                 ("variant", ctypes.c_int32), ("lora_dropout", ctypes.c_float),
-                ("dropout_offset", ctypes.c_uint32), ("dropout_seed", ctypes.c_uint64)]
+                ("dropout_offset", ctypes.c_uint32), ("dropout_seed", ctypes.c_uint64),
+                ("weight_format", ctypes.c_int32)]
 
 
 class LrqMlpDesc(ctypes.Structure):
@@ -88,6 +90,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.lrq_workspace_size.restype = ctypes.c_size_t
         lib.lrq_workspace_size_prepared.argtypes = [ctypes.POINTER(LrqDesc), ctypes.c_int]
         lib.lrq_workspace_size_prepared.restype = ctypes.c_size_t
+        lib.lrq_nf4_weight_size.argtypes = [ctypes.POINTER(LrqDesc)]
+        lib.lrq_nf4_weight_size.restype = ctypes.c_size_t
+        lib.lrq_quantize_nf4.argtypes = [ctypes.POINTER(LrqDesc), P, P, S, P]
+        lib.lrq_quantize_nf4.restype = ctypes.c_int
         lib.lrq_prepared_size.argtypes = [ctypes.POINTER(LrqDesc), ctypes.c_int]
         lib.lrq_prepared_size.restype = ctypes.c_size_t
         lib.lrq_prepare_weights.argtypes = [ctypes.POINTER(LrqDesc), ctypes.c_int, P, P, P, S, P]
@@ -124,11 +130,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
 
 def make_desc(n_tokens, d_model, n_q_heads, n_kv_heads, head_dim, dtype, eps=1e-6, rope_theta=10000.0,
               lora_rank=0, lora_alpha=0.0, lora_targets=0, has_bias=0, variant=LRQ_VARIANT_AUTO,
-              lora_dropout=0.0, dropout_offset=0, dropout_seed=0) -> LrqDesc:
+              lora_dropout=0.0, dropout_offset=0, dropout_seed=0, weight_format=LRQ_WEIGHT_DENSE) -> LrqDesc:
     return LrqDesc(int(n_tokens), int(d_model), int(n_q_heads), int(n_kv_heads), int(head_dim), int(dtype),
                    float(eps), float(rope_theta), int(lora_rank), float(lora_alpha), int(lora_targets),
                    int(has_bias), int(variant), float(lora_dropout), int(dropout_offset) & 0xFFFFFFFF,
-                   int(dropout_seed) & 0xFFFFFFFFFFFFFFFF)
+                   int(dropout_seed) & 0xFFFFFFFFFFFFFFFF, int(weight_format))
 
 
 def _ptr(t) -> Optional[int]:
@@ -209,6 +215,17 @@ def lrq_prepared_size(desc: LrqDesc, for_backward: bool = False) -> int:
 
 def lrq_workspace_size_prepared(desc: LrqDesc, for_backward: bool = False) -> int:
     return int(load().lrq_workspace_size_prepared(ctypes.byref(desc), int(bool(for_backward))))
+
+
+def lrq_nf4_weight_size(desc: LrqDesc) -> int:
+    return int(load().lrq_nf4_weight_size(ctypes.byref(desc)))
+
+
+def lrq_quantize_nf4(desc: LrqDesc, w_qkv, w_nf4, nf4_bytes: Optional[int] = None, stream=None) -> None:
+    lib = load()
+    nbytes = _ws_bytes(w_nf4, nf4_bytes)
+    _check(lib.lrq_quantize_nf4(ctypes.byref(desc), _ptr(w_qkv), _ptr(w_nf4), int(nbytes),
+                                _stream(stream, (w_qkv,))))
 
 
 def lrq_prepare_weights(desc: LrqDesc, for_backward: bool, gamma, w_qkv, prepared,

@@ -12,7 +12,8 @@
 // products) and everything else stays in fp32.  dA / dB are zeroed by a fill kernel first,
 // so they are overwritten.  The atomics make the summation order of dA / dB vary between
 // runs (within rounding).  With LoRA dropout, U_t, dA_t and target t's dh term see only the
-// features that t's keep bits keep, and s = alpha / r / (1 - p).
+// features that t's keep bits keep, and s = alpha / r / (1 - p).  With an NF4 base (QLoRA), W
+// is dequantised as it is read.
 #include <algorithm>
 
 #include "lrq_internal.h"
@@ -44,6 +45,7 @@ __global__ __launch_bounds__(kThreads) void bwd_generic_kernel(BwdParams bp) {
   const TIn* __restrict__ x = static_cast<const TIn*>(p.x);
   const TIn* __restrict__ gamma = static_cast<const TIn*>(p.gamma);
   const TIn* __restrict__ w = static_cast<const TIn*>(p.w);
+  const Nf4View wq = nf4_view(p.w, p.N, p.d);  // used when p.nf4 (the QLoRA base)
   const TIn* __restrict__ dy = static_cast<const TIn*>(bp.dy);
   TIn* __restrict__ dx = static_cast<TIn*>(bp.dx);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void bwd_generic_kernel(BwdParams bp) {
       for (int m = 0; m < kMaxCols; ++m) {
         const int64_t j = tid + static_cast<int64_t>(m) * kThreads;
         if (j < d) {
-          const float wv = load_elem(w, wrow + j);
+          const float wv = p.nf4 ? nf4_at(wq, c0 + i, j) : load_elem(w, wrow + j);
 #pragma unroll
           for (int rr = 0; rr < kRows; ++rr) acc[rr][m] = fmaf(s_g[rr][i], wv, acc[rr][m]);
         }

@@ -14,7 +14,8 @@
 // the rotated W_eff h), so the RMSNorm backward needs no second pass over dh.
 //
 // Kernels, in launch order (all on the caller's stream):
-//   prep_weights  WT = W^T [d][N] (unless the call brings it prepared), AT = [A_q^T | A_k^T |
+//   prep_weights  WT = W^T [d][N] (unless the call brings it prepared; an NF4 W, the QLoRA
+//                 base, is dequantised on the way), AT = [A_q^T | A_k^T |
 //                 A_v^T | 0] [d][Rp] with Rp = sum r rounded up to 64, B_t^T [r][N_t] and
 //                 A'_t = bf16(A_t * gamma) [r][d]
 //   rows          per token: inv, m, G (bf16) into Gcat[:, 0:N)
@@ -132,6 +133,7 @@ T* at(void* base, size_t off) {
 // transpose grid.
 struct PrepArgs {
   const uint16_t* w;
+  Nf4View wq;    // W as NF4 blocks instead (QLoRA base) when wq.codes != nullptr
   const uint16_t* a[3];
   const uint16_t* b[3];
   const uint16_t* gamma;
@@ -151,8 +153,11 @@ __global__ __launch_bounds__(256) void prep_weights_kernel(PrepArgs a) {
   // writes of a row and the column reads (8 rows q = 8 k + const, one chunk per wave) both
   // hit distinct banks (a padded row pitch cannot do both and stay 16-byte aligned)
   __shared__ uint16_t tile_s[64][64];
+  __shared__ float levels[16];
   auto ts = [&](int q, int j) -> uint16_t& { return tile_s[q][(((j >> 3) ^ (q >> 3)) & 7) * 8 + (j & 7)]; };
   const int tid = threadIdx.x;
+  if (tid < 16) levels[tid] = kNf4Levels[tid];
+  __syncthreads();
   if (static_cast<int>(blockIdx.x) < a.wt_blocks) {
     // transpose a 64 x 64 block: source rows q (LoRA-extended K index) x columns j, moved as
     // 16-byte vectors (8 columns of a source row in, 8 rows of a destination row out)
@@ -166,14 +171,23 @@ __global__ __launch_bounds__(256) void prep_weights_kernel(PrepArgs a) {
       const int q = q0 + qi;
       const uint16_t* src = nullptr;
       if (q < a.N) {
-        src = a.w + static_cast<int64_t>(q) * a.d;
+        src = a.wq.codes ? nullptr : a.w + static_cast<int64_t>(q) * a.d;
       } else if (q - a.N < a.R) {
         const int cq = q - a.N;
         for (int t = 0; t < 3; ++t)
           if (((a.targets >> t) & 1u) && cq >= a.off[t] && cq < a.off[t] + a.r)
             src = a.a[t] + static_cast<int64_t>(cq - a.off[t]) * a.d;
       }
-      const uint4 v = src ? *reinterpret_cast<const uint4*>(src + j0 + jc) : uint4{0u, 0u, 0u, 0u};
+      uint4 v = src ? *reinterpret_cast<const uint4*>(src + j0 + jc) : uint4{0u, 0u, 0u, 0u};
+      if (q < a.N && a.wq.codes) {
+        // NF4 base: 8 dequantised weights, rounded once to bf16
+        float wv[8];
+        nf4_at8(a.wq, q, j0 + jc, levels, wv);
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16_bits(wv[2 * e]) | (f32_to_bf16_bits(wv[2 * e + 1]) << 16);
+        v = uint4{o[0], o[1], o[2], o[3]};
+      }
       *reinterpret_cast<uint4*>(&ts(qi, jc)) = v;
     }
     __syncthreads();
@@ -763,6 +777,7 @@ size_t bwd_tiled_prepared_bytes(const FwdParams& p) { return al256(static_cast<s
 hipError_t prepare_bwd_tiled(const FwdParams& p, void* dst, hipStream_t s) {
   PrepArgs pa{};
   pa.w = static_cast<const uint16_t*>(p.w);
+  if (p.nf4) pa.wq = nf4_view(p.w, p.N, p.d);
   pa.wt = static_cast<uint16_t*>(dst);
   pa.N = p.N;
   pa.d = static_cast<int>(p.d);
@@ -790,6 +805,7 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
     // ---- weights
     PrepArgs pa{};
     pa.w = static_cast<const uint16_t*>(p.w);
+    if (p.nf4) pa.wq = nf4_view(p.w, p.N, p.d);
     pa.gamma = static_cast<const uint16_t*>(p.gamma);
     pa.wt = at<uint16_t>(ws, L.wt);
     pa.at = at<uint16_t>(ws, L.at);

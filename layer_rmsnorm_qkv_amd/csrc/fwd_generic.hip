@@ -10,7 +10,7 @@
 //   3. epilogue: + (alpha/r) B U (U rounded once to bf16 in the bf16 path), + bias,
 //      rotation of q and k pairs, one store.
 // With LoRA dropout, U_t sums only the features that target t's keep bits keep, and the
-// scale is alpha / r / (1 - p).
+// scale is alpha / r / (1 - p).  With an NF4 base (QLoRA), W is dequantised as it is staged.
 // h and U live only in LDS and registers.  This family is the float32 path and the
 // fallback for shapes the MFMA kernels do not cover; it uses plain FMA arithmetic.
 #include "lrq_internal.h"
@@ -36,6 +36,7 @@ __global__ __launch_bounds__(kThreads) void fwd_generic_kernel(FwdParams p) {
   const TIn* __restrict__ x = static_cast<const TIn*>(p.x);
   const TIn* __restrict__ gamma = static_cast<const TIn*>(p.gamma);
   const TIn* __restrict__ w = static_cast<const TIn*>(p.w);
+  const Nf4View wq = nf4_view(p.w, p.N, p.d);  // used when p.nf4 (the QLoRA base)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void fwd_generic_kernel(FwdParams p) {
       float v = 0.f;
       if (pr < n_pairs && k < d) {
         const int col = (pr / half) * p.D + (pr % half) + (c >= kPairs ? half : 0);
-        v = load_elem(w, static_cast<int64_t>(col) * d + k);
+        v = p.nf4 ? nf4_at(wq, col, k) : load_elem(w, static_cast<int64_t>(col) * d + k);
       }
       s_w[c][kk] = v;
     }

@@ -272,11 +272,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiled_kernel(TiledArgs p) {
   }
 }
 
-// W' = bf16(W * gamma) and A'_t = bf16(A_t * gamma): rows [0, N) of the destination
+// W' = bf16(W * gamma) and A'_t = bf16(A_t * gamma) (W dequantised first when it is stored as
+// NF4 blocks, the QLoRA base): rows [0, N) of the destination
 // come from W (N = 0: W is not folded), then r rows per target from A_q, A_k, A_v (targets
 // only).  Each thread scales 8 consecutive elements of one row (d % 8 == 0).
 struct FoldArgs {
   const uint16_t* w;
+  Nf4View wq;       // W as NF4 blocks instead (QLoRA base) when wq.codes != nullptr
   const uint16_t* a[3];
   const uint16_t* gamma;
   uint16_t* dst;
@@ -286,12 +288,31 @@ struct FoldArgs {
 };
 
 __global__ __launch_bounds__(256) void fold_gamma_kernel(FoldArgs f) {
+  __shared__ float levels[16];
+  if (threadIdx.x < 16) levels[threadIdx.x] = kNf4Levels[threadIdx.x];
+  __syncthreads();
   const int64_t chunks_per_row = f.d / 8;
   const int64_t total = f.rows * chunks_per_row;
   for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < total;
        c += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int64_t row = c / chunks_per_row;
     const int k = static_cast<int>(c - row * chunks_per_row) * 8;
+    if (row < f.N && f.wq.codes) {
+      // NF4 base: dequantise 8 weights, times gamma, one rounding to bf16
+      float wv[8];
+      nf4_at8(f.wq, row, k, levels, wv);
+      const uint4 g = *reinterpret_cast<const uint4*>(f.gamma + k);
+      const uint32_t gs[4] = {g.x, g.y, g.z, g.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = f32_to_bf16_bits(wv[2 * e] * lo_bf16(gs[e]));
+        const uint32_t hi = f32_to_bf16_bits(wv[2 * e + 1] * hi_bf16(gs[e]));
+        o[e] = lo | (hi << 16);
+      }
+      *reinterpret_cast<uint4*>(f.dst + row * f.d + k) = uint4{o[0], o[1], o[2], o[3]};
+      continue;
+    }
     const uint16_t* src;
     if (row < f.N) {
       src = f.w + row * f.d;
@@ -334,6 +355,8 @@ bool tiled_supports(const FwdParams& p) {
 }
 
 namespace {
+// The NF4 view of W for the fold (QLoRA base), or an empty one for dense weights.
+Nf4View weight_view(const FwdParams& p) { return p.nf4 ? nf4_view(p.w, p.N, p.d) : Nf4View{nullptr, nullptr, 0}; }
 int n_targets(const FwdParams& p) { return (p.targets & 1u) + ((p.targets >> 1) & 1u) + ((p.targets >> 2) & 1u); }
 size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 }  // namespace
@@ -349,10 +372,11 @@ size_t tiled_workspace_bytes(const FwdParams& p) {
 size_t tiled_prepared_bytes(const FwdParams& p) { return align256(static_cast<size_t>(p.N) * p.d * 2); }
 
 namespace {
-void launch_fold(const uint16_t* w, int w_rows, const uint16_t* const a[3], int na, const int slot_t[3], int r,
-                 const uint16_t* gamma, uint16_t* dst, int64_t d, hipStream_t s) {
+void launch_fold(const uint16_t* w, const Nf4View& wq, int w_rows, const uint16_t* const a[3], int na,
+                 const int slot_t[3], int r, const uint16_t* gamma, uint16_t* dst, int64_t d, hipStream_t s) {
   FoldArgs f;
   f.w = w;
+  f.wq = wq;
   f.gamma = gamma;
   f.dst = dst;
   f.N = w_rows;
@@ -373,8 +397,8 @@ void launch_fold(const uint16_t* w, int w_rows, const uint16_t* const a[3], int 
 hipError_t prepare_fwd_tiled(const FwdParams& p, void* prepared, hipStream_t s) {
   const uint16_t* none[3] = {nullptr, nullptr, nullptr};
   const int slot_t[3] = {0, 0, 0};
-  launch_fold(static_cast<const uint16_t*>(p.w), p.N, none, 0, slot_t, 0, static_cast<const uint16_t*>(p.gamma),
-              static_cast<uint16_t*>(prepared), p.d, s);
+  launch_fold(static_cast<const uint16_t*>(p.w), weight_view(p), p.N, none, 0, slot_t, 0,
+              static_cast<const uint16_t*>(p.gamma), static_cast<uint16_t*>(prepared), p.d, s);
   return hipGetLastError();
 }
 
@@ -397,7 +421,7 @@ hipError_t launch_fwd_tiled(const FwdParams& p, hipStream_t s) {
       slot_t[slots++] = t;
     }
   }
-  launch_fold(static_cast<const uint16_t*>(p.w), w_rows, srcs, slots, slot_t, p.r,
+  launch_fold(static_cast<const uint16_t*>(p.w), weight_view(p), w_rows, srcs, slots, slot_t, p.r,
               static_cast<const uint16_t*>(p.gamma), ws, p.d, s);
 
   a.x = static_cast<const uint16_t*>(p.x);

@@ -148,6 +148,10 @@ lrq_status check_desc(const lrq_desc* d, lrq::FwdParams& p) {
     return fail(LRQ_ERR_UNSUPPORTED, "sizes beyond the supported range");
   if (!std::isfinite(d->lora_dropout) || d->lora_dropout < 0.f || d->lora_dropout >= 1.f)
     return fail(LRQ_ERR_INVALID_ARG, "lora_dropout must be finite and in [0, 1)");
+  if (d->weight_format != LRQ_WEIGHT_DENSE && d->weight_format != LRQ_WEIGHT_NF4)
+    return fail(LRQ_ERR_INVALID_ARG, "unknown weight_format %d", d->weight_format);
+  if (d->weight_format == LRQ_WEIGHT_NF4 && d->d_model % lrq::kNf4Block != 0)
+    return fail(LRQ_ERR_UNSUPPORTED, "NF4 weights need d_model %% 64 == 0");
   if (d->lora_targets && d->lora_rank > LRQ_MAX_LORA_RANK)
     return fail(LRQ_ERR_UNSUPPORTED, "lora_rank %d > %d", d->lora_rank, LRQ_MAX_LORA_RANK);
 
@@ -168,6 +172,7 @@ lrq_status check_desc(const lrq_desc* d, lrq::FwdParams& p) {
   p.scale = d->lora_targets ? d->lora_alpha / static_cast<float>(d->lora_rank) : 0.f;
   p.has_bias = d->has_bias;
   p.esize = d->dtype == LRQ_F32 ? 4 : 2;
+  p.nf4 = d->weight_format == LRQ_WEIGHT_NF4;
   p.dropout = d->lora_targets != 0 && d->lora_dropout > 0.f;
   if (p.dropout) {
     // inverted dropout: the kept features' 1 / (1 - p) joins the adapter scale
@@ -197,7 +202,7 @@ int select(const lrq_desc* d, const lrq::FwdParams& p, bool backward) {
   }
   const bool bf16 = d->dtype == LRQ_BF16;
   const bool tiled = bf16 && lrq::tiled_supports(p);
-  const bool decode = bf16 && !p.dropout && lrq::decode_supports(p);
+  const bool decode = bf16 && !p.dropout && !p.nf4 && lrq::decode_supports(p);
   switch (d->variant) {
     case LRQ_VARIANT_AUTO:
       if (decode && p.T <= kDecodeMaxTokens) return LRQ_VARIANT_DECODE;
@@ -296,6 +301,26 @@ lrq_status hip_status(hipError_t e, const char* what) {
 extern "C" {
 
 int lrq_abi_version(void) { return LRQ_ABI_VERSION; }
+
+size_t lrq_nf4_weight_size(const lrq_desc* desc) {
+  lrq::FwdParams p;
+  if (check_desc(desc, p) != LRQ_OK || p.d % lrq::kNf4Block != 0) return 0;
+  return lrq::nf4_buffer_bytes(p.N, p.d);
+}
+
+lrq_status lrq_quantize_nf4(const lrq_desc* desc, const void* w_qkv, void* w_nf4, size_t nf4_bytes, void* stream) {
+  lrq::FwdParams p;
+  lrq_status st = check_desc(desc, p);
+  if (st != LRQ_OK) return st;
+  if (p.d % lrq::kNf4Block != 0) return fail(LRQ_ERR_UNSUPPORTED, "NF4 weights need d_model %% 64 == 0");
+  if (!w_qkv || !w_nf4) return fail(LRQ_ERR_INVALID_ARG, "w_qkv and w_nf4 are required");
+  const size_t need = lrq::nf4_buffer_bytes(p.N, p.d);
+  if (nf4_bytes < need) return fail(LRQ_ERR_INVALID_ARG, "NF4 buffer too small: %zu < %zu", nf4_bytes, need);
+  if (!aligned16(w_qkv) || !aligned16(w_nf4)) return fail(LRQ_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  return hip_status(lrq::launch_quantize_nf4(w_qkv, desc->dtype == LRQ_F32, p.N, p.d, w_nf4,
+                                             static_cast<hipStream_t>(stream)),
+                    "NF4 quantisation");
+}
 
 const char* lrq_status_string(lrq_status s) {
   switch (s) {

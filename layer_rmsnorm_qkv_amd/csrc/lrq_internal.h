@@ -50,6 +50,8 @@ struct FwdParams {
   uint64_t drop_seed;
   uint32_t* drop_bits_r;        // [drop_nt][T][ceil(d / 32)] keep bits, row-major
   uint16_t* drop_xm;            // [drop_nt][T][d] bf16 x * keep (tiled families), or nullptr
+  // QLoRA base: w is an NF4 buffer (codes [N][d / 2], then float32 scales [N][d / 64])
+  int nf4;
 };
 
 struct BwdParams {
@@ -90,6 +92,49 @@ hipError_t launch_dropout_masks(FwdParams& p, void* region, bool xm, bool fill, 
 __host__ __device__ inline int target_slot(uint32_t targets, int t) {
   return static_cast<int>((targets & 1u) * (t > 0) + ((targets >> 1) & 1u) * (t > 1));
 }
+
+// ---- NF4 weights (QLoRA base): the QLoRA paper's published 4-bit NormalFloat code book,
+// blocks of 64 weights along d with a float32 scale each (nf4.hip quantises).
+constexpr int kNf4Block = 64;
+__host__ __device__ inline size_t nf4_codes_bytes(int64_t n, int64_t d) {
+  return (static_cast<size_t>(n) * static_cast<size_t>(d) / 2 + 255) & ~static_cast<size_t>(255);
+}
+__host__ __device__ inline size_t nf4_buffer_bytes(int64_t n, int64_t d) {
+  return nf4_codes_bytes(n, d) + static_cast<size_t>(n) * static_cast<size_t>(d / kNf4Block) * 4;
+}
+static __device__ __constant__ const float kNf4Levels[16] = {
+    -1.0f, -0.6961928009986877f, -0.5250730514526367f, -0.39491748809814453f,
+    -0.28444138169288635f, -0.18477343022823334f, -0.09105003625154495f, 0.0f,
+    0.07958029955625534f, 0.16093020141124725f, 0.24611230194568634f, 0.33791524171829224f,
+    0.44070982933044434f, 0.5626170039176941f, 0.7229568362236023f, 1.0f};
+
+// Read-only view of an NF4 buffer of an [n, d] weight.
+struct Nf4View {
+  const uint8_t* codes;
+  const float* scales;
+  int64_t d;
+};
+__host__ __device__ inline Nf4View nf4_view(const void* buf, int64_t n, int64_t d) {
+  const uint8_t* c = static_cast<const uint8_t*>(buf);
+  return Nf4View{c, reinterpret_cast<const float*>(c + nf4_codes_bytes(n, d)), d};
+}
+// Weight (row, k) of the buffer.
+__device__ __forceinline__ float nf4_at(const Nf4View& v, int64_t row, int64_t k) {
+  const uint32_t byte = v.codes[(row * v.d + k) >> 1];
+  const uint32_t code = (k & 1) ? (byte >> 4) : (byte & 15u);
+  return kNf4Levels[code] * v.scales[row * (v.d / kNf4Block) + k / kNf4Block];
+}
+// Weights (row, k .. k + 7) (k % 8 == 0) as float, from 4 code bytes and the block scale;
+// `levels` is the code book (in LDS or constant memory).
+__device__ __forceinline__ void nf4_at8(const Nf4View& v, int64_t row, int64_t k, const float* levels,
+                                        float (&out)[8]) {
+  const uint32_t c4 = *reinterpret_cast<const uint32_t*>(v.codes + ((row * v.d + k) >> 1));
+  const float sc = v.scales[row * (v.d / kNf4Block) + k / kNf4Block];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = levels[(c4 >> (4 * e)) & 15u] * sc;
+}
+
+hipError_t launch_quantize_nf4(const void* w, bool f32, int64_t n, int64_t d, void* dst, hipStream_t s);
 
 // Column range [lo, hi) of target t.
 __host__ __device__ inline void target_cols(const FwdParams& p, int t, int& lo, int& hi) {

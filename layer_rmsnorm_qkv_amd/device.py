@@ -21,14 +21,15 @@ def torch_dtype(w: Workload):
 
 
 def desc_for(w: Workload, n_tokens: Optional[int] = None, variant: int = B.LRQ_VARIANT_AUTO,
-             dropout: Optional[Tuple[float, int, int]] = None) -> B.LrqDesc:
-    """Descriptor of workload ``w``; ``dropout`` = (rate, seed, offset) turns on LoRA dropout."""
+             dropout: Optional[Tuple[float, int, int]] = None, nf4: bool = False) -> B.LrqDesc:
+    """Descriptor of workload ``w``; ``dropout`` = (rate, seed, offset) turns on LoRA dropout,
+    ``nf4`` stores W_qkv as NF4 blocks (the QLoRA base)."""
     p, seed, offset = dropout if dropout is not None else (0.0, 0, 0)
     return B.make_desc(w.n_tokens if n_tokens is None else n_tokens, w.d_model, w.n_q_heads, w.n_kv_heads,
                        w.head_dim, B.LRQ_F32 if w.dtype == "f32" else B.LRQ_BF16, w.eps, w.rope_theta,
                        w.lora_rank if w.lora_targets else 0, w.lora_alpha, w.lora_targets,
                        1 if w.has_bias else 0, variant, lora_dropout=p, dropout_offset=offset,
-                       dropout_seed=seed)
+                       dropout_seed=seed, weight_format=B.LRQ_WEIGHT_NF4 if nf4 else B.LRQ_WEIGHT_DENSE)
 
 
 class DeviceProblem:
@@ -36,13 +37,13 @@ class DeviceProblem:
 
     def __init__(self, w: Workload, inputs: Dict[str, object], device: str = "cuda",
                  variant: int = B.LRQ_VARIANT_AUTO, backward: bool = False,
-                 dropout: Optional[Tuple[float, int, int]] = None):
+                 dropout: Optional[Tuple[float, int, int]] = None, nf4: bool = False):
         import torch
         self.w = w
         dt = torch_dtype(w)
         T = inputs["x"].shape[0]
         self.T = T
-        self.desc = desc_for(w, T, variant, dropout)
+        self.desc = desc_for(w, T, variant, dropout, nf4)
 
         def up(a):
             return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dt)
@@ -50,6 +51,11 @@ class DeviceProblem:
         self.x = up(inputs["x"])
         self.gamma = up(inputs["gamma"])
         self.w_qkv = up(inputs["w"])
+        self.w_dense = self.w_qkv
+        if nf4:
+            # the QLoRA base: W quantised to NF4 blocks on the device; every call takes the buffer
+            self.w_qkv = torch.empty(B.lrq_nf4_weight_size(self.desc), dtype=torch.uint8, device=device)
+            B.lrq_quantize_nf4(self.desc, self.w_dense, self.w_qkv)
         self.bias = up(inputs["bias"])
         self.a = [up(inputs["a"].get(t)) for t in (TARGET_Q, TARGET_K, TARGET_V)]
         self.b = [up(inputs["b"].get(t)) for t in (TARGET_Q, TARGET_K, TARGET_V)]

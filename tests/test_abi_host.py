@@ -33,7 +33,7 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails va
 def declared_symbols():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lrq_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(lrq_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol():
@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol():
     assert set(syms) == set(B.EXPORTED), syms
     for s in syms:
         assert hasattr(lib, s), s
-    assert B.lrq_abi_version() == 4
+    assert B.lrq_abi_version() == 5
 
 
 def test_desc_layout_matches_header(tmp_path):
@@ -94,7 +94,7 @@ def expect(status, fn, *a, **k):
     ("head_dim", 15), ("head_dim", 0), ("dtype", 7), ("eps", -1.0), ("eps", float("nan")),
     ("rope_theta", 0.0), ("rope_theta", float("inf")), ("lora_targets", 8), ("lora_rank", 0),
     ("lora_alpha", float("nan")), ("has_bias", 2), ("variant", 9), ("lora_dropout", -0.1),
-    ("lora_dropout", 1.0), ("lora_dropout", float("nan"))])
+    ("lora_dropout", 1.0), ("lora_dropout", float("nan")), ("weight_format", 2), ("weight_format", -1)])
 def test_invalid_descriptor(field, value):
     expect(B.LRQ_ERR_INVALID_ARG, fwd, good_desc(**{field: value}))
     assert B.lrq_workspace_size(good_desc(**{field: value})) == 0
@@ -147,6 +147,27 @@ def test_dropout_workspace_and_family():
     rows, xm = a256(2 * 4 * 32 * 4), a256(2 * 4 * 1024 * 2)
     assert B.lrq_workspace_size(drop) == a256(B.lrq_workspace_size(base)) + rows + xm
     assert B.lrq_workspace_size(drop, True) == a256(B.lrq_workspace_size(base, True)) + rows + xm
+
+
+def test_nf4_sizes_and_checks():
+    # NF4 buffer: codes N * d / 2 bytes rounded up to 256, then N * d / 64 float32 scales
+    d = good_desc(d_model=128)                      # N = (4 + 2 * 2) * 16 = 128
+    assert B.lrq_nf4_weight_size(d) == (128 * 128 // 2 + 255) // 256 * 256 + 128 * 2 * 4
+    assert B.lrq_nf4_weight_size(good_desc(d_model=96)) == 0
+    assert B.lrq_nf4_weight_size(good_desc(n_q_heads=0)) == 0
+    expect(B.LRQ_ERR_UNSUPPORTED, fwd, good_desc(d_model=96, weight_format=B.LRQ_WEIGHT_NF4))
+    expect(B.LRQ_ERR_UNSUPPORTED, B.lrq_quantize_nf4, good_desc(d_model=96), FAKE, FAKE, 1 << 20)
+    expect(B.LRQ_ERR_INVALID_ARG, B.lrq_quantize_nf4, d, FAKE, FAKE, 100)
+    expect(B.LRQ_ERR_INVALID_ARG, B.lrq_quantize_nf4, d, None, FAKE, 1 << 20)
+    expect(B.LRQ_ERR_UNSUPPORTED, B.lrq_quantize_nf4, d, FAKE + 4, FAKE, 1 << 20)
+    # the decode family does not take NF4 weights
+    dec = dict(n_tokens=4, d_model=1024, n_q_heads=8, n_kv_heads=2, head_dim=128, dtype=B.LRQ_BF16)
+    assert B.lrq_select_variant(good_desc(**dec, weight_format=B.LRQ_WEIGHT_NF4)) == B.LRQ_VARIANT_TILED
+    assert B.lrq_select_variant(good_desc(**dec, weight_format=B.LRQ_WEIGHT_NF4,
+                                          variant=B.LRQ_VARIANT_DECODE)) == -1
+    # T == 0 with NF4 is still a no-op
+    B.lrq_forward(good_desc(d_model=128, n_tokens=0, weight_format=B.LRQ_WEIGHT_NF4), None, None, None, None,
+                  [FAKE, None, FAKE], [FAKE, None, FAKE], None, None)
 
 
 def test_zero_tokens_is_a_noop():
