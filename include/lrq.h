@@ -309,6 +309,42 @@ size_t lrq_nf4_weight_size(const lrq_desc* desc);
 lrq_status lrq_quantize_nf4(const lrq_desc* desc, const void* w_qkv, void* w_nf4, size_t nf4_bytes,
                             void* stream);
 
+/* ---- Attention over the key/value cache: the step after the projection.
+ * "Liger-Kernel底层优化：新一代内核级推理加速引擎深度解析" lists a fused attention kernel with
+ * KV-cache handling next to the fused norm/QKV/RoPE kernel; its decoder-layer op sequence
+ * computes scaled_dot_product_attention(q, k, v) from the rotated q, k and v.  The library's
+ * readings: softmax(q.k * scale) v per query head, scale = 1/sqrt(D) unless given; query head h
+ * reads kv head h / (Hq / Hkv); causal with the queries as the last q_len tokens of their
+ * sequence (query i, 0-based among the sequence's queries, sees keys 0 .. kv_len - q_len + i),
+ * or non-causal (every key).  Keys and values are rows of the caches lrq_forward_kv writes,
+ * named per sequence by a slot list in token order (a contiguous cache, or a paged one
+ * flattened to rows); queries are rows of the projection's output (its first Hq * D columns).
+ * Sequence b: query rows q_indptr[b] .. q_indptr[b+1] of q and out, keys
+ * kv_slots[kv_indptr[b] .. kv_indptr[b+1]].  Device arrays; the library reads them as given:
+ * slots outside [0, num_slots) read as zero vectors, rows past max_q_len of a sequence are not
+ * computed, and a query with no visible key (kv_len < q_len) gets a zero row. */
+typedef struct lrq_attn_desc {
+  int32_t n_seqs;      /* sequences, >= 0 (0: no-op)                                    */
+  int32_t n_q_heads;   /* Hq >= 1                                                       */
+  int32_t n_kv_heads;  /* Hkv >= 1, Hq % Hkv == 0                                       */
+  int32_t head_dim;    /* D; 128 is supported                                           */
+  int32_t dtype;       /* LRQ_BF16 (q, caches, out); scores and softmax in float32      */
+  int32_t max_q_len;   /* >= every sequence's query count; (max_q_len * Hq/Hkv + 127) / 128 <= 65535 */
+  int64_t ld_q;        /* elements between rows of q, >= Hq * D, multiple of 8          */
+  int64_t num_slots;   /* rows of each cache, >= 0                                      */
+  float scale;         /* softmax scale, finite and >= 0; 0 means 1/sqrt(D)             */
+  int32_t causal;      /* 1 causal, 0 not                                               */
+} lrq_attn_desc;
+
+/* out [T_q, Hq * D] bf16 = attention of the queries over their cached keys and values.
+ * q, k_cache, v_cache, out 16-byte aligned; the index arrays int32.  No workspace.
+ * INVALID_ARG: NULL desc, negative counts, heads invalid, ld_q < Hq * D, scale invalid, causal
+ * not 0/1, NULL pointers (n_seqs > 0 and max_q_len > 0); UNSUPPORTED: head_dim != 128, dtype
+ * not bf16, ld_q % 8 != 0, misaligned pointers, too many query rows per sequence. */
+lrq_status lrq_attention(const lrq_attn_desc* desc, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* q_indptr, const int32_t* kv_indptr, const int32_t* kv_slots, void* out,
+                         void* stream);
+
 /* LRQ_ABI_VERSION of the loaded library. */
 int lrq_abi_version(void);
 
@@ -353,8 +389,8 @@ lrq_status lrq_mlp_forward(const lrq_mlp_desc* desc, const void* h, const void* 
  * lrq_backward call records a pair of HIP events on the caller's stream around the call's
  * dominant kernel: the fused tile kernel of the tiled forward, the streaming kernel of the
  * decode forward, the dh/dx product of the tiled backward, the single kernel of the
- * generic family, the fused gate/up/SwiGLU kernel of lrq_mlp_forward (as a forward).
- * Enabling (or disabling) discards what was recorded.  Events are created
+ * generic family, the fused gate/up/SwiGLU kernel of lrq_mlp_forward and the attention
+ * kernel of lrq_attention (both as forwards).  Enabling (or disabling) discards what was recorded.  Events are created
  * on demand (at most 4096 pairs per direction) and kept until the process ends.  Not
  * thread-safe: meant for one benchmarking thread.  Always LRQ_OK. */
 lrq_status lrq_kernel_timing(int enable);

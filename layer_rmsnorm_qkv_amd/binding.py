@@ -26,7 +26,8 @@ EXPORTED = ("lrq_forward", "lrq_forward_kv", "lrq_backward", "lrq_workspace_size
             "lrq_status_string", "lrq_last_error", "lrq_abi_version", "lrq_kernel_timing",
             "lrq_kernel_time_ms", "lrq_prepared_size", "lrq_prepare_weights", "lrq_forward_prepared",
             "lrq_backward_prepared", "lrq_workspace_size_prepared", "lrq_forward_noalloc",
-            "lrq_mlp_workspace_size", "lrq_mlp_forward", "lrq_nf4_weight_size", "lrq_quantize_nf4")
+            "lrq_mlp_workspace_size", "lrq_mlp_forward", "lrq_nf4_weight_size", "lrq_quantize_nf4",
+            "lrq_attention")
 LRQ_MLP_GATE, LRQ_MLP_UP, LRQ_MLP_DOWN = 1, 2, 4
 
 
@@ -46,6 +47,13 @@ class LrqMlpDesc(ctypes.Structure):
     _fields_ = [("n_tokens", ctypes.c_int64), ("d_model", ctypes.c_int64), ("d_ff", ctypes.c_int64),
                 ("dtype", ctypes.c_int32), ("lora_rank", ctypes.c_int32), ("lora_alpha", ctypes.c_float),
                 ("lora_targets", ctypes.c_uint32)]
+
+
+class LrqAttnDesc(ctypes.Structure):
+    _fields_ = [("n_seqs", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("max_q_len", ctypes.c_int32),
+                ("ld_q", ctypes.c_int64), ("num_slots", ctypes.c_int64), ("scale", ctypes.c_float),
+                ("causal", ctypes.c_int32)]
 
 
 class LrqKvCache(ctypes.Structure):
@@ -90,6 +98,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.lrq_workspace_size.restype = ctypes.c_size_t
         lib.lrq_workspace_size_prepared.argtypes = [ctypes.POINTER(LrqDesc), ctypes.c_int]
         lib.lrq_workspace_size_prepared.restype = ctypes.c_size_t
+        lib.lrq_attention.argtypes = [ctypes.POINTER(LrqAttnDesc), P, P, P, P, P, P, P, P]
+        lib.lrq_attention.restype = ctypes.c_int
         lib.lrq_nf4_weight_size.argtypes = [ctypes.POINTER(LrqDesc)]
         lib.lrq_nf4_weight_size.restype = ctypes.c_size_t
         lib.lrq_quantize_nf4.argtypes = [ctypes.POINTER(LrqDesc), P, P, S, P]
@@ -215,6 +225,19 @@ def lrq_prepared_size(desc: LrqDesc, for_backward: bool = False) -> int:
 
 def lrq_workspace_size_prepared(desc: LrqDesc, for_backward: bool = False) -> int:
     return int(load().lrq_workspace_size_prepared(ctypes.byref(desc), int(bool(for_backward))))
+
+
+def make_attn_desc(n_seqs, n_q_heads, n_kv_heads, head_dim, max_q_len, ld_q, num_slots, dtype=LRQ_BF16,
+                   scale=0.0, causal=1) -> LrqAttnDesc:
+    return LrqAttnDesc(int(n_seqs), int(n_q_heads), int(n_kv_heads), int(head_dim), int(dtype), int(max_q_len),
+                       int(ld_q), int(num_slots), float(scale), int(causal))
+
+
+def lrq_attention(desc: LrqAttnDesc, q, k_cache, v_cache, q_indptr, kv_indptr, kv_slots, out,
+                  stream=None) -> None:
+    lib = load()
+    _check(lib.lrq_attention(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(q_indptr),
+                             _ptr(kv_indptr), _ptr(kv_slots), _ptr(out), _stream(stream, (q, out))))
 
 
 def lrq_nf4_weight_size(desc: LrqDesc) -> int:

@@ -302,6 +302,53 @@ extern "C" {
 
 int lrq_abi_version(void) { return LRQ_ABI_VERSION; }
 
+lrq_status lrq_attention(const lrq_attn_desc* d, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* q_indptr, const int32_t* kv_indptr, const int32_t* kv_slots, void* out,
+                         void* stream) {
+  if (!d) return fail(LRQ_ERR_INVALID_ARG, "desc is NULL");
+  if (d->n_seqs < 0 || d->max_q_len < 0 || d->num_slots < 0)
+    return fail(LRQ_ERR_INVALID_ARG, "n_seqs, max_q_len and num_slots must be >= 0");
+  if (d->n_q_heads < 1 || d->n_kv_heads < 1 || d->n_q_heads % d->n_kv_heads != 0)
+    return fail(LRQ_ERR_INVALID_ARG, "head counts must be >= 1 with n_q_heads %% n_kv_heads == 0");
+  if (d->head_dim < 1) return fail(LRQ_ERR_INVALID_ARG, "head_dim < 1");
+  if (d->ld_q < static_cast<int64_t>(d->n_q_heads) * d->head_dim)
+    return fail(LRQ_ERR_INVALID_ARG, "ld_q < n_q_heads * head_dim");
+  if (!std::isfinite(d->scale) || d->scale < 0.f) return fail(LRQ_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if (d->causal != 0 && d->causal != 1) return fail(LRQ_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (d->dtype != LRQ_BF16) return fail(LRQ_ERR_UNSUPPORTED, "attention runs in bf16 only");
+  if (!lrq::attn_supports(d->head_dim)) return fail(LRQ_ERR_UNSUPPORTED, "head_dim %d not supported", d->head_dim);
+  if (d->ld_q % 8 != 0) return fail(LRQ_ERR_UNSUPPORTED, "ld_q must be a multiple of 8");
+  const int64_t group = d->n_q_heads / d->n_kv_heads;
+  if ((static_cast<int64_t>(d->max_q_len) * group + 127) / 128 > 65535)
+    return fail(LRQ_ERR_UNSUPPORTED, "too many query rows per sequence");
+  if (d->n_seqs == 0 || d->max_q_len == 0) return ok();
+  if (!q || !k_cache || !v_cache || !q_indptr || !kv_indptr || !kv_slots || !out)
+    return fail(LRQ_ERR_INVALID_ARG, "q, caches, index arrays and out are required");
+  for (const void* p : {q, k_cache, v_cache, static_cast<const void*>(out)})
+    if (!aligned16(p)) return fail(LRQ_ERR_UNSUPPORTED, "q, caches and out must be 16-byte aligned");
+  for (const void* p : {static_cast<const void*>(q_indptr), static_cast<const void*>(kv_indptr),
+                        static_cast<const void*>(kv_slots)})
+    if (reinterpret_cast<uintptr_t>(p) & 3u) return fail(LRQ_ERR_UNSUPPORTED, "index arrays must be 4-byte aligned");
+  lrq::AttnParams p{};
+  p.q = q;
+  p.ld_q = d->ld_q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.num_slots = d->num_slots;
+  p.q_indptr = q_indptr;
+  p.kv_indptr = kv_indptr;
+  p.kv_slots = kv_slots;
+  p.out = out;
+  p.n_seqs = d->n_seqs;
+  p.max_q_len = d->max_q_len;
+  p.Hq = d->n_q_heads;
+  p.Hkv = d->n_kv_heads;
+  p.scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt(static_cast<float>(d->head_dim));
+  p.causal = d->causal;
+  g_timing.kind = 0;  // timed with the forward-direction calls
+  return hip_status(lrq::launch_attention(p, static_cast<hipStream_t>(stream)), "attention launch");
+}
+
 size_t lrq_nf4_weight_size(const lrq_desc* desc) {
   lrq::FwdParams p;
   if (check_desc(desc, p) != LRQ_OK || p.d % lrq::kNf4Block != 0) return 0;

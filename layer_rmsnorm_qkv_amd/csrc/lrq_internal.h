@@ -136,6 +136,24 @@ __device__ __forceinline__ void nf4_at8(const Nf4View& v, int64_t row, int64_t k
 
 hipError_t launch_quantize_nf4(const void* w, bool f32, int64_t n, int64_t d, void* dst, hipStream_t s);
 
+// Attention over the key/value cache (attn.hip).
+struct AttnParams {
+  const void* q;          // [T_q][ld_q] bf16, q heads in the first Hq * D columns
+  int64_t ld_q;
+  const void* k_cache;    // [num_slots][Hkv * D] bf16
+  const void* v_cache;
+  int64_t num_slots;
+  const int32_t* q_indptr;   // [n_seqs + 1]
+  const int32_t* kv_indptr;  // [n_seqs + 1]
+  const int32_t* kv_slots;   // cache rows of each sequence's keys, in token order
+  void* out;              // [T_q][Hq * D] bf16
+  int n_seqs, max_q_len, Hq, Hkv;
+  float scale;
+  int causal;
+};
+bool attn_supports(int head_dim);
+hipError_t launch_attention(const AttnParams& p, hipStream_t s);
+
 // Column range [lo, hi) of target t.
 __host__ __device__ inline void target_cols(const FwdParams& p, int t, int& lo, int& hi) {
   lo = t == 0 ? 0 : (t == 1 ? p.col_k : p.col_v);

@@ -15,7 +15,9 @@ sequence computes the attention output from the rotated q, k and v
          0 .. kv_len - q_len + i; with causal off every query sees all kv_len keys;
   (R-A4) the keys and values of a sequence are cache rows named by a slot list (one row of
          Hkv * D values per token, the layout the projection's cache write uses), in token
-         order; q rows come from the projection's output (q heads first in each row).
+         order; q rows come from the projection's output (q heads first in each row);
+  (R-A5) degenerate cases: a sequence without queries contributes nothing, and a query that
+         sees no key (kv_len < q_len puts early queries before the first key) gets a zero row.
 """
 from __future__ import annotations
 
@@ -41,6 +43,10 @@ def attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, q_indptr:
         q0, q1 = int(q_indptr[b]), int(q_indptr[b + 1])
         slots = np.asarray(kv_slots[int(kv_indptr[b]):int(kv_indptr[b + 1])], dtype=np.int64)
         q_len, kv_len = q1 - q0, len(slots)
+        if q_len == 0:
+            continue
+        n_vis = np.minimum(kv_len, kv_len - q_len + np.arange(q_len) + 1) if causal else np.full(q_len, kv_len)
+        seen = n_vis > 0                                             # rows with at least one key (R-A5)
         for h in range(Hq):
             g = h // group
             keys = kc[slots, g * D:(g + 1) * D]                     # [kv_len, D]
@@ -49,9 +55,12 @@ def attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, q_indptr:
             if causal:
                 visible = np.arange(kv_len)[None, :] <= (kv_len - q_len + np.arange(q_len))[:, None]
                 scores = np.where(visible, scores, -np.inf)
-            m = np.max(scores, axis=1, keepdims=True)
-            w = np.exp(scores - m)
-            out[q0:q1, h * D:(h + 1) * D] = (w @ vals) / np.sum(w, axis=1, keepdims=True)
+            if not np.any(seen):
+                continue
+            sc = scores[seen]
+            m = np.max(sc, axis=1, keepdims=True)
+            w = np.exp(sc - m)
+            out[q0 + np.flatnonzero(seen), h * D:(h + 1) * D] = (w @ vals) / np.sum(w, axis=1, keepdims=True)
     return out
 
 
@@ -66,6 +75,8 @@ def attention_rows(rows: Sequence[int], q, k_cache, v_cache, q_indptr, kv_indptr
         b = int(np.searchsorted(q_indptr, r, side="right") - 1)
         kv_len = int(kv_indptr[b + 1] - kv_indptr[b])
         last = kv_len - int(q_indptr[b + 1] - q_indptr[b]) + (r - int(q_indptr[b])) if causal else kv_len - 1
+        if last < 0:
+            continue  # no visible key: a zero row (R-A5)
         mine = slots[int(kv_indptr[b]):int(kv_indptr[b]) + last + 1]
         res[n] = attention(np.asarray(q)[r:r + 1], k_cache, v_cache, [0, 1], [0, len(mine)], mine, n_q_heads,
                            n_kv_heads, head_dim, scale, causal=False)[0]

@@ -134,4 +134,19 @@ def check_rows_helper(a):
         _close(a.attention_rows(rows, **c, causal=causal), full[rows], 1e-13, f"rows causal={causal}")
 
 
-ALL_CHECKS = [check_closed_forms, check_torch_sdpa, check_brute_force, check_causality_and_slots, check_rows_helper]
+def check_degenerate_sequences(a):
+    """A sequence without queries (with or without keys) writes nothing and leaves the other
+    sequences' rows as they are alone; with kv_len < q_len the queries before the first key get
+    zero rows and the others see their windows (checked by scalar loops)."""
+    c = paged_case(seed=8, lens=((0, 0), (2, 3), (0, 4)))
+    alone = paged_case(seed=8, lens=((0, 0), (2, 3), (0, 4)))
+    alone.update(q_indptr=[0, 2], kv_indptr=[0, 3], kv_slots=c["kv_slots"][0:3])
+    _close(a.attention(**c), a.attention(**alone), 1e-15, "sequences without queries")
+    c = paged_case(seed=9, lens=((4, 2),))
+    out = a.attention(**c)
+    assert not np.any(out[:2])
+    _close(out[2:], brute(dict(c, q=c["q"][2:], q_indptr=[0, 2]))[:, :out.shape[1]], 1e-12, "late queries")
+
+
+ALL_CHECKS = [check_closed_forms, check_torch_sdpa, check_brute_force, check_causality_and_slots, check_rows_helper,
+              check_degenerate_sequences]

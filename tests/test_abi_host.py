@@ -170,6 +170,55 @@ def test_nf4_sizes_and_checks():
                   [FAKE, None, FAKE], [FAKE, None, FAKE], None, None)
 
 
+def test_attn_desc_layout_matches_header(tmp_path):
+    fields = [f for f, _ in B.LrqAttnDesc._fields_]
+    src = tmp_path / "attn_layout.c"
+    body = "\n".join(f'  printf("{f} %zu\\n", offsetof(lrq_attn_desc, {f}));' for f in fields)
+    src.write_text(f'#include <stdio.h>\n#include <stddef.h>\n#include "lrq.h"\n'
+                   f'int main(void) {{\n{body}\n  printf("size %zu\\n", sizeof(lrq_attn_desc));\n  return 0;\n}}\n')
+    exe = tmp_path / "attn_layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src),
+                    "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                       check=True).stdout.splitlines())
+    for f in fields:
+        assert int(got[f]) == getattr(B.LrqAttnDesc, f).offset, f
+    assert int(got["size"]) == ctypes.sizeof(B.LrqAttnDesc)
+
+
+def attn_desc(**kw):
+    base = dict(n_seqs=2, n_q_heads=8, n_kv_heads=2, head_dim=128, max_q_len=4, ld_q=1536, num_slots=64)
+    base.update(kw)
+    return B.make_attn_desc(**base)
+
+
+def attn(desc, **over):
+    args = dict(q=FAKE, k_cache=FAKE, v_cache=FAKE, q_indptr=FAKE, kv_indptr=FAKE, kv_slots=FAKE, out=FAKE)
+    args.update(over)
+    B.lrq_attention(desc, **args)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(n_seqs=-1), B.LRQ_ERR_INVALID_ARG), (dict(n_q_heads=0), B.LRQ_ERR_INVALID_ARG),
+    (dict(n_q_heads=6, n_kv_heads=4), B.LRQ_ERR_INVALID_ARG), (dict(ld_q=1000), B.LRQ_ERR_INVALID_ARG),
+    (dict(scale=-1.0), B.LRQ_ERR_INVALID_ARG), (dict(scale=float("inf")), B.LRQ_ERR_INVALID_ARG),
+    (dict(causal=2), B.LRQ_ERR_INVALID_ARG), (dict(max_q_len=-1), B.LRQ_ERR_INVALID_ARG),
+    (dict(head_dim=64), B.LRQ_ERR_UNSUPPORTED), (dict(dtype=B.LRQ_F32), B.LRQ_ERR_UNSUPPORTED),
+    (dict(ld_q=1540), B.LRQ_ERR_UNSUPPORTED), (dict(max_q_len=1 << 30), B.LRQ_ERR_UNSUPPORTED)])
+def test_attention_checks(over, status):
+    expect(status, attn, attn_desc(**over))
+
+
+def test_attention_pointer_checks_and_noop():
+    expect(B.LRQ_ERR_INVALID_ARG, attn, attn_desc(), kv_slots=None)
+    expect(B.LRQ_ERR_INVALID_ARG, attn, attn_desc(), out=None)
+    expect(B.LRQ_ERR_UNSUPPORTED, attn, attn_desc(), q=FAKE + 8)
+    expect(B.LRQ_ERR_UNSUPPORTED, attn, attn_desc(), kv_slots=FAKE + 2)
+    # nothing to do: NULL pointers are fine
+    B.lrq_attention(attn_desc(n_seqs=0), None, None, None, None, None, None, None)
+    B.lrq_attention(attn_desc(max_q_len=0), None, None, None, None, None, None, None)
+
+
 def test_zero_tokens_is_a_noop():
     # T == 0: valid, nothing is launched, pointers may be NULL
     B.lrq_forward(good_desc(n_tokens=0), None, None, None, None, [FAKE, None, FAKE], [FAKE, None, FAKE],

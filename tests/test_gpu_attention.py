@@ -1,0 +1,176 @@
+"""GPU parity of the attention over the key/value cache, through the C ABI, against the
+attention oracle: batches of sequences with decode, chunk and prefill shapes over a paged
+(shuffled) cache, grouped-query heads, causal on and off, an explicit scale, empty sequences,
+slots outside the cache, q rows read out of a wider projection output; full-size prefill and
+decode samples; and the projection -> cache -> attention chain end to end."""
+import numpy as np
+import pytest
+
+import oracle.attn_oracle as at
+import oracle.lrq_oracle as o
+from helpers import TOL, assert_parity, elem_ratio, log, row_rel_errors, spec_of, to_np
+from layer_rmsnorm_qkv_amd import binding as B
+from layer_rmsnorm_qkv_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+def bf16(a):
+    return wl.to_dtype(np.asarray(a, np.float64), "bf16")
+
+
+def make_case(seed, lens, hq, hkv, ld_extra=0, extra_slots=7, bad_slots=0):
+    rng = np.random.default_rng(seed)
+    q_ind, kv_ind = [0], [0]
+    for ql, kl in lens:
+        q_ind.append(q_ind[-1] + ql)
+        kv_ind.append(kv_ind[-1] + kl)
+    n_slots = kv_ind[-1] + extra_slots
+    slots = rng.permutation(n_slots)[:kv_ind[-1]].astype(np.int32)
+    if bad_slots:
+        idx = rng.choice(len(slots), size=bad_slots, replace=False)
+        slots[idx[: bad_slots // 2]] = -3
+        slots[idx[bad_slots // 2:]] = n_slots + 11
+    ld_q = hq * D + ld_extra
+    return dict(q=bf16(rng.standard_normal((q_ind[-1], ld_q))), k_cache=bf16(rng.standard_normal((n_slots, hkv * D))),
+                v_cache=bf16(rng.standard_normal((n_slots, hkv * D))), q_indptr=np.array(q_ind, np.int32),
+                kv_indptr=np.array(kv_ind, np.int32), kv_slots=slots, hq=hq, hkv=hkv, ld_q=ld_q,
+                max_q_len=max([ql for ql, _ in lens] + [0]))
+
+
+def oracle_of(c, scale=None, causal=True, rows=None):
+    """The oracle with slots outside the cache reading a zero row (the library's rule)."""
+    n = c["k_cache"].shape[0]
+    kc = np.vstack([c["k_cache"], np.zeros((1, c["k_cache"].shape[1]))])
+    vc = np.vstack([c["v_cache"], np.zeros((1, c["v_cache"].shape[1]))])
+    slots = np.where((c["kv_slots"] < 0) | (c["kv_slots"] >= n), n, c["kv_slots"])
+    args = (c["q"], kc, vc, c["q_indptr"], c["kv_indptr"], slots, c["hq"], c["hkv"], D)
+    if rows is None:
+        return at.attention(*args, scale=scale, causal=causal)
+    return at.attention_rows(rows, *args, scale=scale, causal=causal)
+
+
+def run_gpu(c, scale=0.0, causal=1, max_q_len=None):
+    import torch
+    dev = "cuda"
+    t = lambda a, dt=torch.bfloat16: torch.from_numpy(np.ascontiguousarray(a)).to(device=dev, dtype=dt)  # noqa: E731
+    q, kc, vc = t(c["q"]), t(c["k_cache"]), t(c["v_cache"])
+    qi, ki, sl = (t(c[k], torch.int32) for k in ("q_indptr", "kv_indptr", "kv_slots"))
+    out = torch.full((c["q"].shape[0], c["hq"] * D), float("nan"), dtype=torch.bfloat16, device=dev)
+    desc = B.make_attn_desc(len(c["q_indptr"]) - 1, c["hq"], c["hkv"], D,
+                            c["max_q_len"] if max_q_len is None else max_q_len, c["ld_q"], c["k_cache"].shape[0],
+                            scale=scale, causal=causal)
+    B.lrq_attention(desc, q, kc, vc, qi, ki, sl, out)
+    torch.cuda.synchronize()
+    return to_np(out)
+
+
+def errors(got, ref):
+    return {"out": o.rel_frobenius(got, ref), "out_row": row_rel_errors(got, ref),
+            "out_elem": elem_ratio(got, ref, "bf16")}
+
+
+CASES = {
+    # (q_len, kv_len) per sequence
+    "decode_gqa4": dict(lens=((1, 1), (1, 37), (1, 64), (1, 65), (1, 300)), hq=8, hkv=2),
+    "prefill_gqa4": dict(lens=((100, 100), (64, 64), (7, 7), (130, 130)), hq=8, hkv=2),
+    "chunks_mha": dict(lens=((5, 77), (64, 200), (33, 33), (1, 129)), hq=4, hkv=4),
+    "gqa8_wide_q_rows": dict(lens=((40, 90), (17, 17)), hq=8, hkv=1, ld_extra=2 * 128),
+    "empty_sequences": dict(lens=((0, 0), (3, 5), (0, 9), (2, 2)), hq=4, hkv=2),
+    "slots_outside_cache": dict(lens=((4, 50), (1, 70)), hq=4, hkv=2, bad_slots=6),
+}
+
+
+@pytest.mark.parametrize("causal", [1, 0])
+@pytest.mark.parametrize("name", list(CASES))
+def test_attention_small(name, causal):
+    spec = dict(CASES[name])
+    c = make_case(seed=len(name) + causal, **spec)
+    log(f"[gpu] attention {name} causal={causal}")
+    got = run_gpu(c, causal=causal)
+    ref = oracle_of(c, causal=bool(causal))
+    errs = errors(got, ref)
+    log(f"  errors {errs}")
+    assert_parity(errs, "bf16")
+
+
+def test_attention_explicit_scale_and_long_max_q_len():
+    c = make_case(seed=3, lens=((9, 40), (1, 8)), hq=4, hkv=2)
+    got = run_gpu(c, scale=0.05, max_q_len=1000)
+    errs = errors(got, oracle_of(c, scale=0.05))
+    log(f"  errors {errs}")
+    assert_parity(errs, "bf16")
+
+
+def test_attention_rows_past_max_q_len_untouched():
+    """Rows of a sequence past max_q_len are not computed (the caller's bound)."""
+    c = make_case(seed=4, lens=((6, 6),), hq=4, hkv=4)
+    got = run_gpu(c, max_q_len=4)
+    ref = oracle_of(c)
+    assert_parity(errors(got[:4], ref[:4]), "bf16")
+    assert np.all(np.isnan(got[4:]))
+
+
+def test_attention_llama3_prefill_sampled():
+    """16 sequences of 512 tokens with the Llama-3-8B heads (32 q, 8 kv), sampled rows."""
+    lens = tuple((512, 512) for _ in range(16))
+    c = make_case(seed=5, lens=lens, hq=32, hkv=8, extra_slots=0)
+    got = run_gpu(c)
+    rows = np.sort(np.random.default_rng(6).choice(c["q"].shape[0], 96, replace=False))
+    rows = np.unique(np.concatenate([rows, [0, 511, 512, c["q"].shape[0] - 1]]))
+    ref = oracle_of(c, rows=rows)
+    errs = errors(got[rows], ref)
+    log(f"  errors {errs}")
+    assert_parity(errs, "bf16")
+
+
+def test_attention_decode_batch_sampled():
+    """64 decoding sequences with 1..2048 cached tokens each (Llama-3-8B heads: 32 q, 8 kv)."""
+    rng = np.random.default_rng(7)
+    kv = rng.integers(1, 2049, size=64)
+    kv[0], kv[1] = 2048, 1
+    c = make_case(seed=8, lens=tuple((1, int(k)) for k in kv), hq=32, hkv=8, extra_slots=0)
+    got = run_gpu(c)
+    rows = np.arange(0, 64, 5)
+    ref = oracle_of(c, rows=rows)
+    errs = errors(got[rows], ref)
+    log(f"  errors {errs}")
+    assert_parity(errs, "bf16")
+
+
+def test_projection_cache_attention_chain():
+    """x -> lrq_forward_kv (q, k, v with RoPE, k and v into a paged cache) -> lrq_attention over
+    the cache, against the oracles chained the same way on the GPU's projection output."""
+    import torch
+    from layer_rmsnorm_qkv_amd.device import DeviceProblem
+    w = wl.get("llama3").replace(n_tokens=3 * 96, d_model=1024, n_q_heads=8, n_kv_heads=2, seq_len=96)
+    inp = wl.make_inputs(w)
+    prob = DeviceProblem(w, inp)
+    T, kvw = w.n_tokens, w.n_kv_heads * D
+    n_slots = T + 13
+    slots = np.random.default_rng(9).permutation(n_slots)[:T].astype(np.int32)
+    kc = torch.zeros((n_slots, kvw), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    sl = torch.from_numpy(slots).cuda()
+    ws = prob.workspace
+    B.lrq_forward_kv(prob.desc, prob.x, prob.gamma, prob.w_qkv, prob.bias, prob.a, prob.b, prob.positions,
+                     prob.out, kc, vc, sl, n_slots, ws)
+    # three sequences of 96 tokens, each attending over its own cached tokens (prefill)
+    q_ind = torch.tensor([0, 96, 192, 288], dtype=torch.int32, device="cuda")
+    attn = torch.empty((T, w.n_q_heads * D), dtype=torch.bfloat16, device="cuda")
+    desc = B.make_attn_desc(3, w.n_q_heads, w.n_kv_heads, D, 96, w.n_out, n_slots)
+    B.lrq_attention(desc, prob.out, kc, vc, q_ind, q_ind, sl, attn)
+    torch.cuda.synchronize()
+    y = to_np(prob.out)
+    ref_y = o.forward(spec_of(w), inp["x"], inp["gamma"], inp["w"], inp["bias"], inp["a"], inp["b"],
+                      inp["positions"])
+    assert_parity({"proj": o.rel_frobenius(y, ref_y)}, "bf16")
+    kref, vref = o.kv_cache_write(spec_of(w), y, slots, np.zeros((n_slots, kvw)), np.zeros((n_slots, kvw)))
+    ref = at.attention(y, kref, vref, [0, 96, 192, 288], [0, 96, 192, 288], slots, w.n_q_heads, w.n_kv_heads, D)
+    got = to_np(attn)
+    errs = errors(got, ref)
+    log(f"  errors {errs}")
+    assert_parity(errs, "bf16")
+    assert TOL["bf16"] > 0
