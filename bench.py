@@ -536,12 +536,124 @@ def run_mlp_config(name, args, B, wl):
     return res
 
 
+def attn_work(w):
+    """Matmul FLOPs (Q K^T and P V over the visible keys) and bytes (q, the sequences' cached
+    keys and values, out) of one attention call."""
+    D, hq, hkv = w.head_dim, w.n_q_heads, w.n_kv_heads
+    vis = 0
+    for i in range(w.q_len):
+        vis += min(w.kv_len, w.kv_len - w.q_len + i + 1) if w.causal else w.kv_len
+    flop = 4.0 * D * hq * vis * w.n_seqs
+    byts = 2.0 * (2 * w.n_seqs * w.q_len * hq * D + 2 * w.n_seqs * w.kv_len * hkv * D)
+    return flop, byts
+
+
+def run_attn_config(name, args, B, wl):
+    """Attention over the key/value cache (the step after the projection): timed like the
+    projection's workloads; MFMA roofline for prefill, HBM for decode."""
+    import numpy as np
+    import torch
+
+    w = wl.get_attn(name)
+    inp = wl.make_attn_inputs_device(w)
+    D = w.head_dim
+    out = torch.empty((w.n_seqs * w.q_len, w.n_q_heads * D), dtype=torch.bfloat16, device="cuda")
+    desc = B.make_attn_desc(w.n_seqs, w.n_q_heads, w.n_kv_heads, D, w.q_len, w.n_q_heads * D,
+                            w.n_seqs * w.kv_len, causal=1 if w.causal else 0)
+    stream = torch.cuda.current_stream()
+
+    def step(i, s):
+        B.lrq_attention(desc, inp["q"], inp["k_cache"], inp["v_cache"], inp["q_indptr"], inp["kv_indptr"],
+                        inp["kv_slots"], out, stream=s)
+
+    for i in range(args.warmup):
+        step(i, stream)
+    torch.cuda.synchronize()
+    graph = None
+    if args.graph == "on":
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(0, side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream()
+            for i in range(args.steps):
+                step(i, cap)
+        graph.replay()
+        torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i, stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    B.lrq_kernel_timing(True)
+    for i in range(args.steps):
+        step(i, stream)
+    torch.cuda.synchronize()
+    k_ms, n = B.lrq_kernel_time_ms(False)
+    B.lrq_kernel_timing(False)
+    assert n == args.steps
+    dom = min(k_ms, ms_per_step)
+    flop, byts = attn_work(w)
+    tokens = w.n_seqs * w.q_len
+    res = {"value": tokens / (ms_per_step * 1e-3), "unit": "tokens/s", "ms_per_step": ms_per_step, "dtype": "bf16",
+           "config": {"workload": w.name, "description": w.description, "sequences": w.n_seqs, "q_len": w.q_len,
+                      "kv_len": w.kv_len, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": D,
+                      "causal": w.causal, "kernel_family": "attention (flash, MFMA)",
+                      "launch": "one HIP graph replay of the K steps" if graph is not None else "eager calls"},
+           "tflops_step": flop / (ms_per_step * 1e-3) / 1e12}
+    common = {"traffic": None, "kernel": "attn_kernel", "launch_ms": dom, "launch_ms_eager_events": k_ms}
+    if w.q_len == 1:
+        ach = byts / (dom * 1e-3) / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": ach / PEAK_HBM_GBS, "algorithmic_bytes": byts, **common}
+    else:
+        ach = flop / (dom * 1e-3) / 1e12
+        res["roofline"] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": ach / PEAK_BF16_TFLOPS, "algorithmic_flop": flop, **common}
+    if not args.no_cpu_baseline:
+        import oracle.attn_oracle as at
+        from oracle.lrq_oracle import rel_frobenius
+        # a bounded sample: whole sequences (their q rows and cached rows copied to the host)
+        n_seq_s = 2 if w.q_len > 1 else 8
+        seqs = list(range(0, w.n_seqs, max(1, w.n_seqs // n_seq_s)))[:n_seq_s]
+        q_rows = np.concatenate([np.arange(s * w.q_len, (s + 1) * w.q_len) for s in seqs])
+        kv_rows = np.concatenate([np.arange(s * w.kv_len, (s + 1) * w.kv_len) for s in seqs])
+        f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+        qh = f64(inp["q"][torch.from_numpy(q_rows).cuda()])
+        kh = f64(inp["k_cache"][torch.from_numpy(kv_rows).cuda()])
+        vh = f64(inp["v_cache"][torch.from_numpy(kv_rows).cuda()])
+        got = f64(out[torch.from_numpy(q_rows).cuda()])
+        qi = np.arange(0, len(seqs) * w.q_len + 1, w.q_len)
+        ki = np.arange(0, len(seqs) * w.kv_len + 1, w.kv_len)
+        n_threads = cpu_threads()
+        t0 = time.perf_counter()
+        ref = at.attention(qh, kh, vh, qi, ki, np.arange(len(kv_rows)), w.n_q_heads, w.n_kv_heads, D,
+                           causal=w.causal)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": len(q_rows) / dt, "unit": "tokens/s", "cores": n_threads, "kind": "oracle",
+                               "sample": f"{len(seqs)} of {w.n_seqs} sequences ({len(q_rows)} query rows), float64 "
+                                         f"numpy, {dt:.2f} s",
+                               "gpu_parity_rel_fro": rel_frobenius(got, ref)}
+    del graph, inp, out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30, help="untimed steps first (the clocks settle within about 20 steps of sustained MFMA load)")
-    ap.add_argument("--workload", default="all", choices=("all",) + ALL_WORKLOADS + ("train_dropout",),
+    ap.add_argument("--workload", default="all",
+                    choices=("all",) + ALL_WORKLOADS + ("train_dropout", "attn_prefill", "attn_decode"),
                     help="all: every workload, the headline (llama2, the largest) on the top level and all five "
                          "under 'configs'")
     ap.add_argument("--variant", default="auto", choices=["auto", "generic", "tiled", "decode"])
@@ -595,7 +707,7 @@ def main():
     names = ALL_WORKLOADS if args.workload == "all" else (args.workload,)
     results = {}
     for name in names:
-        if name == "train_dropout":
+        if name == "train_dropout" or name.startswith("attn_"):
             continue
         print(f"[bench] {name}: measuring", file=sys.stderr, flush=True)
         results[name] = run_config(name, args, B, wl, DeviceProblem)
@@ -611,6 +723,14 @@ def main():
         print(f"[bench] train_dropout: {r['ms_per_step']:.4f} ms/step, roofline {r['roofline']['frac']:.3f}",
               file=sys.stderr, flush=True)
         names = tuple(n for n in names if n != "train_dropout") + ("train_dropout",)
+    if args.workload == "all" or args.workload.startswith("attn_"):
+        for an in (wl.ATTN_BY_NAME if args.workload == "all" else (args.workload,)):
+            print(f"[bench] {an}: measuring", file=sys.stderr, flush=True)
+            results[an] = run_attn_config(an, args, B, wl)
+            r = results[an]
+            print(f"[bench] {an}: {r['ms_per_step']:.4f} ms/step, roofline {r['roofline']['frac']:.3f}",
+                  file=sys.stderr, flush=True)
+            names = tuple(n for n in names if n != an) + (an,)
     if args.workload == "all" and not args.no_mlp:
         print("[bench] mlp_llama3: measuring", file=sys.stderr, flush=True)
         results["mlp_llama3"] = run_mlp_config("mlp_llama3", args, B, wl)

@@ -100,24 +100,33 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   // ---- tile loads: K rows (tid / 16) + 16 c, chunk tid % 16; V key pairs (tid / 16) + 16 c
   const int chunk = tid & 15, rsub = tid >> 4;
   const int64_t koff = static_cast<int64_t>(g) * kD + chunk * 8;
+  // slot numbers are loaded two tiles ahead of their rows, so a tile's row loads never wait for
+  // a slot-list load
   uint4 kreg[4], vreg[2][2];
-  auto load_tile = [&](int t) {
+  int32_t kslot[4], vslot[4];
+  auto load_slots = [&](int t) {
     const int64_t base = static_cast<int64_t>(t) * kKT;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int64_t key = base + rsub + 16 * c;
-      const int64_t slot = key < kv_end ? a.kv_slots[kv0 + key] : -1;
-      kreg[c] = load_row16(a.kc, a.ld_kv, slot, a.num_slots, static_cast<int>(koff));
+      kslot[c] = key < kv_end ? a.kv_slots[kv0 + key] : -1;
     }
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int64_t key = base + 2 * (rsub + 16 * c) + e;
-        const int64_t slot = key < kv_end ? a.kv_slots[kv0 + key] : -1;
-        vreg[c][e] = load_row16(a.vc, a.ld_kv, slot, a.num_slots, static_cast<int>(koff));
+        vslot[2 * c + e] = key < kv_end ? a.kv_slots[kv0 + key] : -1;
       }
-    }
+  };
+  auto load_tile = [&]() {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kreg[c] = load_row16(a.kc, a.ld_kv, kslot[c], a.num_slots, static_cast<int>(koff));
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        vreg[c][e] = load_row16(a.vc, a.ld_kv, vslot[2 * c + e], a.num_slots, static_cast<int>(koff));
   };
   auto store_tile = [&](int buf) {
     unsigned char* kb = smem + buf * kBufBytes;
@@ -144,12 +153,17 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
 
   if (n_tiles > 0) {
-    load_tile(0);
+    load_slots(0);
+    load_tile();
+    if (n_tiles > 1) load_slots(1);
     store_tile(0);
   }
   __syncthreads();
   for (int t = 0; t < n_tiles; ++t) {
-    if (t + 1 < n_tiles) load_tile(t + 1);
+    if (t + 1 < n_tiles) {
+      load_tile();  // rows of tile t + 1 (their slots were loaded an iteration ago)
+      if (t + 2 < n_tiles) load_slots(t + 2);
+    }
     if (wave_active) {
       const unsigned char* kb = smem + (t & 1) * kBufBytes;
       const unsigned char* vb = kb + kKBytes;

@@ -273,3 +273,61 @@ def make_mlp_inputs(w: MlpWorkload, n_tokens: Optional[int] = None, seed: Option
             b[t] = to_dtype(_normal(rng(bn), (dout, r), w.b_var), dt)
     out["a"], out["b"] = a, b
     return out
+
+
+# --------------------------------------------------------------------------- attention workloads
+#
+# The attention step over the key/value cache, with the Llama-3-8B heads (32 q, 8 kv, D 128) of
+# the llama3 projection workload: a prefill batch of 16 sequences of 512 tokens (the projection
+# workload's 8192 tokens) and a decode batch of 64 sequences with 4096 cached tokens each.  The
+# cache is one row per token (a contiguous cache per sequence: slot = sequence * kv_len + t);
+# q, k and v are N(0, 1) bf16 (values of a rotated projection output have that scale when the
+# layer's weights are N(0, 1/d)).
+
+@dataclasses.dataclass(frozen=True)
+class AttnWorkload:
+    name: str
+    index: int
+    n_seqs: int
+    q_len: int            # queries per sequence
+    kv_len: int           # cached keys per sequence (>= q_len)
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    causal: bool
+    description: str = ""
+
+    @property
+    def seed(self) -> int:
+        return BASE_SEED + self.index
+
+
+ATTN_WORKLOADS = [
+    AttnWorkload("attn_prefill", 20, 16, 512, 512, 32, 8, 128, True,
+                 description="causal attention, 16 sequences x 512 tokens, Llama-3-8B heads (32 q / 8 kv, D 128)"),
+    AttnWorkload("attn_decode", 21, 64, 1, 4096, 32, 8, 128, True,
+                 description="decode attention, 64 sequences x 1 query over 4096 cached tokens, Llama-3-8B heads"),
+]
+ATTN_BY_NAME = {w.name: w for w in ATTN_WORKLOADS}
+
+
+def get_attn(name: str) -> AttnWorkload:
+    return ATTN_BY_NAME[name]
+
+
+def make_attn_inputs_device(w: AttnWorkload, device: str = "cuda") -> Dict[str, object]:
+    """Seeded device tensors of one attention call: q [S*q_len, Hq*D], k_cache / v_cache
+    [S*kv_len, Hkv*D] bf16 N(0, 1) (drawn on the device with torch's seeded generator: the cache
+    of the decode workload is 0.5 GB per tensor), q_indptr, kv_indptr and the slot list (int32)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed)
+    D = w.head_dim
+    nq, nk = w.n_seqs * w.q_len, w.n_seqs * w.kv_len
+    q = torch.randn((nq, w.n_q_heads * D), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn((nk, w.n_kv_heads * D), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((nk, w.n_kv_heads * D), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    q_ind = torch.arange(0, nq + 1, w.q_len, dtype=torch.int32, device=device)
+    kv_ind = torch.arange(0, nk + 1, w.kv_len, dtype=torch.int32, device=device)
+    slots = torch.arange(nk, dtype=torch.int32, device=device)
+    return dict(q=q, k_cache=k, v_cache=v, q_indptr=q_ind, kv_indptr=kv_ind, kv_slots=slots)
