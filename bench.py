@@ -75,7 +75,7 @@ def algorithmic_work(w, T=None):
     return f_fwd, f_bwd, bytes_fwd
 
 
-def dominant_kernel_work(w, family: str, backward: bool):
+def dominant_kernel_work(w, family: str, backward: bool, nf4: bool = False):
     """Algorithmic work of one launch of a call's dominant kernel: (amount, unit kind).
 
     Forward, tiled or generic: every matmul FLOP of the forward.  Forward, decode: the bytes
@@ -93,6 +93,8 @@ def dominant_kernel_work(w, family: str, backward: bool):
         eb = 2
         unadapted = sum(hi - lo for t, (lo, hi) in cols.items() if not (w.lora_targets & t))
         nbytes = eb * (T * d + d + N * d + (N if w.has_bias else 0) + ranks * d + T * unadapted) + 4 * T
+        if nf4:  # the QLoRA base: 4-bit codes plus a float32 scale per 64 weights instead of bf16
+            nbytes -= eb * N * d - (N * d // 2 + N * (d // 64) * 4)
         return nbytes, "bytes"
     return f_fwd, "flop"
 
@@ -271,9 +273,10 @@ def working_set_copies(w, prob, n_copies: int):
     return sets
 
 
-def run_config(name, args, B, wl, DeviceProblem, dropout=None):
+def run_config(name, args, B, wl, DeviceProblem, dropout=None, nf4=False):
     """Measure one workload: returns its result object (the shape of the top-level line).
-    ``dropout`` = (rate, seed, offset) runs it with LoRA dropout."""
+    ``dropout`` = (rate, seed, offset) runs it with LoRA dropout; ``nf4`` stores the base as NF4
+    blocks (the QLoRA base, quantised on the device before the steps)."""
     import numpy as np
     import torch
 
@@ -281,7 +284,7 @@ def run_config(name, args, B, wl, DeviceProblem, dropout=None):
     variant = {"auto": B.LRQ_VARIANT_AUTO, "generic": B.LRQ_VARIANT_GENERIC, "tiled": B.LRQ_VARIANT_TILED,
                "decode": B.LRQ_VARIANT_DECODE}[args.variant]
     inp = wl.make_inputs(w, with_dy=w.backward)
-    prob = DeviceProblem(w, inp, variant=variant, backward=w.backward, dropout=dropout)
+    prob = DeviceProblem(w, inp, variant=variant, backward=w.backward, dropout=dropout, nf4=nf4)
     vname = B.VARIANT_NAMES[prob.variant]
     stream = torch.cuda.current_stream()
     # frozen weights are prepared once, before any step (untimed setup, as at model load), for
@@ -389,6 +392,7 @@ def run_config(name, args, B, wl, DeviceProblem, dropout=None):
                    "pass": "forward+backward" if w.backward else "forward",
                    "kv_cache": bool(args.kv_cache),
                    "lora_dropout": 0.0 if dropout is None else dropout[0],
+                   "weight_format": "nf4" if nf4 else "dense",
                    "weights": "prepared once before the steps" if prob.prepared is not None else
                               "prepared inside every call",
                    "operand_copies": n_copies,
@@ -408,7 +412,7 @@ def run_config(name, args, B, wl, DeviceProblem, dropout=None):
     dom_eager = kbwd_ms if backward_dominant else kfwd_ms
     dom_ms = min(dom_eager, ms_per_step)
     assert dom_ms <= ms_per_step
-    work, kind = dominant_kernel_work(w, family, backward_dominant)
+    work, kind = dominant_kernel_work(w, family, backward_dominant, nf4)
     kname = KERNEL_NAMES[(family, backward_dominant)]
     traffic = stored_traffic(w.name, ("bwd_" if backward_dominant else "") + family)
     common = {"traffic": traffic, "kernel": kname, "launch_ms": dom_ms, "launch_ms_eager_events": dom_eager,
@@ -427,7 +431,11 @@ def run_config(name, args, B, wl, DeviceProblem, dropout=None):
         got = forward(stream)
         torch.cuda.synchronize()
         got = got.float().cpu().numpy().astype(np.float64)
-        res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, gpu_rows_fn=lambda rows: got[rows],
+        base_inp = inp
+        if nf4:  # the oracle on the same NF4 base: the dequantised W
+            import oracle.qlora_oracle as qo
+            base_inp = dict(inp, w=qo.dequantize(*qo.quantize(np.asarray(inp["w"], np.float32))))
+        res["cpu_baseline"] = cpu_baseline(w, base_inp, args.cpu_budget, gpu_rows_fn=lambda rows: got[rows],
                                            dropout=dropout)
     del sets, prob, graph
     torch.cuda.synchronize()
@@ -653,7 +661,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30, help="untimed steps first (the clocks settle within about 20 steps of sustained MFMA load)")
     ap.add_argument("--workload", default="all",
-                    choices=("all",) + ALL_WORKLOADS + ("train_dropout", "attn_prefill", "attn_decode"),
+                    choices=("all",) + ALL_WORKLOADS + ("train_dropout", "decode_nf4", "attn_prefill", "attn_decode"),
                     help="all: every workload, the headline (llama2, the largest) on the top level and all five "
                          "under 'configs'")
     ap.add_argument("--variant", default="auto", choices=["auto", "generic", "tiled", "decode"])
@@ -707,13 +715,21 @@ def main():
     names = ALL_WORKLOADS if args.workload == "all" else (args.workload,)
     results = {}
     for name in names:
-        if name == "train_dropout" or name.startswith("attn_"):
+        if name in ("train_dropout", "decode_nf4") or name.startswith("attn_"):
             continue
         print(f"[bench] {name}: measuring", file=sys.stderr, flush=True)
         results[name] = run_config(name, args, B, wl, DeviceProblem)
         r = results[name]
         print(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step, {r['value']:.4g} tokens/s, roofline "
               f"{r['roofline']['frac']:.3f} of {r['roofline']['kernel']}", file=sys.stderr, flush=True)
+    if args.workload in ("all", "decode_nf4"):
+        # the decode step with the QLoRA base (NF4 blocks)
+        print("[bench] decode_nf4: measuring", file=sys.stderr, flush=True)
+        results["decode_nf4"] = run_config("decode", args, B, wl, DeviceProblem, nf4=True)
+        r = results["decode_nf4"]
+        print(f"[bench] decode_nf4: {r['ms_per_step']:.4f} ms/step, roofline {r['roofline']['frac']:.3f}",
+              file=sys.stderr, flush=True)
+        names = tuple(n for n in names if n != "decode_nf4") + ("decode_nf4",)
     if (args.workload == "all" and args.dropout > 0) or args.workload == "train_dropout":
         # the training step again with LoRA dropout (default: the rate of the pages' SFT example)
         print("[bench] train_dropout: measuring", file=sys.stderr, flush=True)

@@ -15,6 +15,11 @@
 //           where RoPE is applied to the LoRA term on its own (the rotation is linear).
 // With a key/value cache, the stores of the k and v columns into out (main for columns
 // without an adapter, finish for the others) also go to the token's cache row.
+// With an NF4 W (the QLoRA base) a W block streams the rows' 4-bit codes instead (a quarter of
+// the bytes) and dequantises them into the MFMA operand: code book value times the block
+// scale, rounded once to bf16; its scales are staged once per block.  Those blocks stream
+// x_g = bf16(x * gamma) and read inv, made once by a prep pass, so that their VALU time goes
+// to the dequantisation (A blocks and dense W blocks form x * gamma per stage as above).
 //
 // The operator is RoPE(W h + b + s B (A h)) with h = x * inv * gamma; inv, a per-row scalar,
 // is applied after the products and gamma before them.  Every sum runs in a fixed order, so
@@ -46,7 +51,7 @@ struct DecodeLayout {
   int Tp;      // rows rounded up to the row group
   int nt;      // number of LoRA targets
   int tgt[3];  // target of A block i
-  size_t y, u, total;
+  size_t y, u, xg, inv, total;
 };
 
 DecodeLayout decode_layout(const FwdParams& p) {
@@ -59,6 +64,10 @@ DecodeLayout decode_layout(const FwdParams& p) {
   o += al256(L.nt ? static_cast<size_t>(L.Tp) * p.N * 4 : 0);
   L.u = o;  // bf16 [Tp][nt * 64]: s * inv * U_t, ranks padded to 64
   o += al256(static_cast<size_t>(L.Tp) * L.nt * 64 * 2);
+  L.xg = o;  // NF4 weights: bf16 [T][d] x * gamma from the prep pass
+  o += al256(p.nf4 ? static_cast<size_t>(p.T) * p.d * 2 : 0);
+  L.inv = o;  // NF4 weights: float [T] 1 / rms(x) from the prep pass
+  o += al256(p.nf4 ? static_cast<size_t>(p.T) * 4 : 0);
   L.total = o;
   return L;
 }
@@ -75,8 +84,12 @@ __device__ __forceinline__ uint16_t* cache_row(uint16_t* kv_k, uint16_t* kv_v, i
 // ---------------------------------------------------------------- main
 struct MainArgs {
   const uint16_t* x;
+  const uint16_t* xg;      // NF4 W blocks: x * gamma (bf16) from the prep pass
+  const float* inv;        // NF4 W blocks: 1 / rms(x) per token row from the prep pass
   const uint16_t* gamma;
   const uint16_t* w;
+  Nf4View wq;            // W as NF4 blocks (QLoRA base) when nf4
+  int nf4;
   const uint16_t* bias;
   const uint16_t* a[3];  // A of the targets in A-block order
   const int32_t* pos;
@@ -99,15 +112,27 @@ struct MainArgs {
 // chunk land in 16 distinct 16-byte bank groups (ds_read_b128 serves 16 lanes per cycle).
 __device__ __forceinline__ int sw(int row, int chunk) { return row * (kBK * 2) + ((chunk ^ (row & 15)) << 4); }
 
-// Waits for the last kStages - 1 stages (all issued) and computes them.
-template <int I, typename F>
+// Waits for the last kStages - 1 stages (all issued) and computes them; L loads per stage.
+template <int L, int I, typename F>
 __device__ __forceinline__ void drain(F& compute, int st) {
   if constexpr (I < kStages - 1) {
-    tile::wait_barrier<(kStages - 2 - I) * kLoads>();
+    tile::wait_barrier<(kStages - 2 - I) * L>();
     compute(st + I);
-    drain<I + 1>(compute, st);
+    drain<L, I + 1>(compute, st);
   }
 }
+
+// NF4 W blocks (QLoRA base): a stage holds the x part and the block's codes, 64 rows x 64
+// bytes (16-byte chunk j of row r stored at j ^ ((r / 4) % 4), so the 4-byte reads of 32 rows
+// hit at most two rows per bank); the block scales sit transposed, [d / 64][64 rows] float32,
+// after the ring, then a 256-entry table: code byte -> its two code-book values (float32
+// pair), so one 8-byte LDS read dequantises two weights (value times scale in float32, one
+// rounding to bf16, as in the other families).
+constexpr int kCodeBytes = kRows * kBK / 2;             // 4 KB
+constexpr int kStageNf4 = kPartBytes + kCodeBytes;      // 20 KB
+constexpr int kScalesOff = kStages * kStageNf4;         // 80 KB
+constexpr int kLevelsOff = kScalesOff + kRows * (kMaxD / 64) * 4;  // 112 KB
+static_assert(kLevelsOff + 256 * 8 <= kRingBytes, "NF4 staging fits under gamma");
 
 // bf16(x * g) of 8 values, and ss += sum of x^2 (products exact, fp32 sums)
 __device__ __forceinline__ bf16x8 scale8(const bf16x8& x, const bf16x8& g, float& ss) {
@@ -122,11 +147,45 @@ __device__ __forceinline__ bf16x8 scale8(const bf16x8& x, const bf16x8& g, float
   return o;
 }
 
+// ---------------------------------------------------------------- prep (NF4 weights)
+// One wavefront per token row: inv = 1 / rms(x) (fp32 sum of the exact squares) and
+// x_g = bf16(x * gamma), once for all NF4 W blocks: their dequantisation takes the VALU time
+// that forming x * gamma inside every block would otherwise need.
+struct PrepArgs {
+  const uint16_t* x;
+  const uint16_t* gamma;
+  uint16_t* xg;
+  float* inv;
+  int64_t T;
+  int d;
+  float eps;
+};
+
+__global__ __launch_bounds__(256) void decode_prep_kernel(PrepArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= a.T) return;
+  const uint16_t* xr = a.x + row * a.d;
+  uint16_t* gr = a.xg + row * a.d;
+  float ss = 0.f;
+  for (int j = lane * 8; j < a.d; j += 512) {
+    const bf16x8 x = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xr + j));
+    const bf16x8 g = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(a.gamma + j));
+    *reinterpret_cast<uint4*>(gr + j) = __builtin_bit_cast(uint4, scale8(x, g, ss));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  if (lane == 0) a.inv[row] = 1.0f / sqrtf(ss / static_cast<float>(a.d) + a.eps);
+}
+
 // Tiles: rt = token-row tile (32 rows), ct = weight-row tile (32 rows).  In a W block the
 // weight rows of ct 0 and ct 1 are the two members of rotate-half pairs, so a pair sits in
 // the same lane and register of the two tiles.
-__global__ __launch_bounds__(256, 1) void decode_main_kernel(MainArgs a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kRingBytes + 2 * kMaxD];
+template <bool NF4>
+__device__ __forceinline__ void decode_main_body(const MainArgs& a, unsigned char* smem) {
+  constexpr int kPer = kLoads / 2;                   // x loads (and dense weight loads) per stage
+  constexpr int kLoadsT = NF4 ? kPer + 1 : kLoads;   // loads per thread and stage
+  constexpr int kStageT = NF4 ? kStageNf4 : kStageBytes;
   unsigned char* gs = smem + kRingBytes;  // gamma, [d] bf16
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -140,16 +199,34 @@ __global__ __launch_bounds__(256, 1) void decode_main_kernel(MainArgs a) {
   const int ab = nb - a.n_wblocks;         // A blocks
   const int64_t ld = a.d;
 
-  // gamma into LDS: 1 KB per load instruction, wave w takes chunks w, w + 4, ...
-  const uint32_t lds_g = tile::lds_addr(gs);
-  const int gchunks = a.d * 2 / 1024;
-  for (int c = wave; c < gchunks; c += 4)
-    tile::dma16(reinterpret_cast<const unsigned char*>(a.gamma) + c * 1024 + lane * 16, lds_g + c * 1024);
+  // gamma into LDS (x * gamma is formed per stage; NF4 W blocks stream x_g instead): 1 KB per
+  // load instruction, wave w takes chunks w, w + 4, ...
+  if constexpr (!NF4) {
+    const uint32_t lds_g = tile::lds_addr(gs);
+    const int gchunks = a.d * 2 / 1024;
+    for (int c = wave; c < gchunks; c += 4)
+      tile::dma16(reinterpret_cast<const unsigned char*>(a.gamma) + c * 1024 + lane * 16, lds_g + c * 1024);
+  }
+
+  // NF4: block scales transposed into LDS (plain loads, overlapped with the ring prologue
+  // below), and the code book
+  float* sc_t = reinterpret_cast<float*>(smem + kScalesOff);
+  float2* pairs = reinterpret_cast<float2*>(smem + kLevelsOff);
+  const int nblk = a.d / 64;
+  float scv[NF4 ? kRows * (kMaxD / 64) / 256 : 1];
+  if constexpr (NF4) {
+#pragma unroll
+    for (int i = 0; i < kRows * (kMaxD / 64) / 256; ++i) {
+      const int e = tid + 256 * i;  // (row, block) = (e / nblk, e % nblk)
+      const int row = e / nblk, blk = e - (e / nblk) * nblk;
+      const int64_t wrow = col0 + (row >> 5) * half + (row & 31);
+      scv[i] = row < kRows ? a.wq.scales[wrow * nblk + blk] : 0.f;
+    }
+  }
 
   // direct-to-LDS sources: this thread fills slots p = (kLoads/2 * wave + j) * 64 + lane of
   // each part; slot p is (staged row p / kChunks, physical chunk p % kChunks).  Token rows
   // past T re-read row T - 1 and padded A rows re-read row r - 1 (never stored).
-  constexpr int kPer = kLoads / 2;
   const uint16_t* xsrc[kPer];
   const uint16_t* wsrc[kPer];
   const uint16_t* arows = a.a[0];
@@ -161,22 +238,44 @@ __global__ __launch_bounds__(256, 1) void decode_main_kernel(MainArgs a) {
     const int p = (wave * kPer + j) * 64 + lane;
     const int row = p / kChunks, chunk = (p % kChunks) ^ (row & 15);
     const int64_t trow = min(static_cast<int64_t>(rg * kRows + row), a.T - 1);
-    xsrc[j] = a.x + trow * ld + chunk * 8;
+    xsrc[j] = (NF4 ? a.xg : a.x) + trow * ld + chunk * 8;
     const int64_t wrow = wblock ? col0 + (row >> 5) * half + (row & 31) : min(row, a.r - 1);
     wsrc[j] = (wblock ? a.w : arows) + wrow * ld + chunk * 8;
   }
+  // NF4 codes: slot p = wave * 64 + lane is (row p / 4, physical chunk p % 4)
+  const uint8_t* csrc = nullptr;
+  if constexpr (NF4) {
+    const int p = wave * 64 + lane, row = p >> 2, lc = (p & 3) ^ ((row >> 2) & 3);
+    const int64_t wrow = col0 + (row >> 5) * half + (row & 31);
+    csrc = a.wq.codes + wrow * (ld / 2) + lc * 16;
+  }
   const uint32_t lds0 = tile::lds_addr(smem) + wave * kPer * 1024;
+  const uint32_t ldsc = tile::lds_addr(smem) + kPartBytes + wave * 1024;
   auto issue = [&](int st) {
-    const uint32_t base = lds0 + (st % kStages) * kStageBytes;
+    const uint32_t base = lds0 + (st % kStages) * kStageT;
     const int k = st * kBK;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) tile::dma16(xsrc[j] + k, base + j * 1024);
+    if constexpr (NF4) {
+      tile::dma16(csrc + k / 2, ldsc + (st % kStages) * kStageT);
+    } else {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) tile::dma16(wsrc[j] + k, base + kPartBytes + j * 1024);
+      for (int j = 0; j < kPer; ++j) tile::dma16(wsrc[j] + k, base + kPartBytes + j * 1024);
+    }
   };
   const int nst = a.d / kBK;  // >= kStages - 1
 #pragma unroll
   for (int st = 0; st < kStages - 1; ++st) issue(st);
+  if constexpr (NF4) {
+    // the scales' loads are older than the ring's: they have landed by now or soon
+#pragma unroll
+    for (int i = 0; i < kRows * (kMaxD / 64) / 256; ++i) {
+      const int e = tid + 256 * i;
+      const int row = e / nblk, blk = e - (e / nblk) * nblk;
+      if (row < kRows) sc_t[blk * kRows + row] = scv[i];
+    }
+    pairs[tid] = make_float2(kNf4Levels[tid & 15], kNf4Levels[tid >> 4]);  // 256 threads, 256 bytes
+  }
 
   floatx16 acc[2][2];
 #pragma unroll
@@ -184,17 +283,43 @@ __global__ __launch_bounds__(256, 1) void decode_main_kernel(MainArgs a) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
   float ss[2] = {0.f, 0.f};  // token rows l32 and 32 + l32, this lane's columns
+  // 8 dequantised weights (row, columns 8 c .. 8 c + 7 of the stage) as a bf16 operand
+  auto nf4_frag = [&](const unsigned char* cs, int row, int c, int st) -> bf16x8 {
+    const uint32_t code = *reinterpret_cast<const uint32_t*>(
+        cs + (row * 4 + ((c >> 2) ^ ((row >> 2) & 3))) * 16 + (c & 3) * 4);
+    const float sc = sc_t[(2 * st + (c >> 3)) * kRows + row];
+    bf16x8 f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float2 v = pairs[(code >> (8 * e)) & 255u];
+      f[2 * e] = static_cast<__bf16>(v.x * sc);
+      f[2 * e + 1] = static_cast<__bf16>(v.y * sc);
+    }
+    return f;
+  };
   auto compute = [&](int st) {
-    const unsigned char* xs = smem + (st % kStages) * kStageBytes;
+    const unsigned char* xs = smem + (st % kStages) * kStageT;
     const unsigned char* ws = xs + kPartBytes;
 #pragma unroll
     for (int i = 0; i < kBK / 64; ++i) {
       const int c = (kBK / 64 * wave + i) * 2 + h32;
-      const bf16x8 g = *reinterpret_cast<const bf16x8*>(gs + (st * kChunks + c) * 16);
-      const bf16x8 a0 = scale8(*reinterpret_cast<const bf16x8*>(xs + sw(l32, c)), g, ss[0]);
-      const bf16x8 a1 = scale8(*reinterpret_cast<const bf16x8*>(xs + sw(32 + l32, c)), g, ss[1]);
-      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(ws + sw(l32, c));
-      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(ws + sw(32 + l32, c));
+      bf16x8 a0, a1;
+      if constexpr (NF4) {
+        a0 = *reinterpret_cast<const bf16x8*>(xs + sw(l32, c));
+        a1 = *reinterpret_cast<const bf16x8*>(xs + sw(32 + l32, c));
+      } else {
+        const bf16x8 g = *reinterpret_cast<const bf16x8*>(gs + (st * kChunks + c) * 16);
+        a0 = scale8(*reinterpret_cast<const bf16x8*>(xs + sw(l32, c)), g, ss[0]);
+        a1 = scale8(*reinterpret_cast<const bf16x8*>(xs + sw(32 + l32, c)), g, ss[1]);
+      }
+      bf16x8 b0, b1;
+      if constexpr (NF4) {
+        b0 = nf4_frag(ws, l32, c, st);
+        b1 = nf4_frag(ws, 32 + l32, c, st);
+      } else {
+        b0 = *reinterpret_cast<const bf16x8*>(ws + sw(l32, c));
+        b1 = *reinterpret_cast<const bf16x8*>(ws + sw(32 + l32, c));
+      }
       acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
       acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
       acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
@@ -207,11 +332,11 @@ __global__ __launch_bounds__(256, 1) void decode_main_kernel(MainArgs a) {
   // whose slot is refilled next.
   int st = 0;
   for (; st + kStages - 1 < nst; ++st) {
-    tile::wait_barrier<(kStages - 2) * kLoads>();
+    tile::wait_barrier<(kStages - 2) * kLoadsT>();
     issue(st + kStages - 1);
     compute(st);
   }
-  drain<0>(compute, st);
+  drain<kLoadsT, 0>(compute, st);
   tile::barrier_lds();  // the ring is reused below
 
   // ---- sums of the four waves' column subsets, in wave order: products, then x^2
@@ -248,11 +373,17 @@ __global__ __launch_bounds__(256, 1) void decode_main_kernel(MainArgs a) {
       y[ct][4 * q + 2] = sum.z;
       y[ct][4 * q + 3] = sum.w;
     }
-  // row statistics of token row rt * 32 + l32 (lanes l32 and 32 + l32 held its two halves)
-  float ssum = 0.f;
+  // row statistics of token row rt * 32 + l32 (lanes l32 and 32 + l32 held its two halves;
+  // NF4 W blocks: from the prep pass)
+  float inv_l;
+  if constexpr (NF4) {
+    inv_l = a.inv[min(static_cast<int64_t>(rg * kRows + rt * 32 + l32), a.T - 1)];
+  } else {
+    float ssum = 0.f;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) ssum += rss[w][rt][l32] + rss[w][rt][32 + l32];
-  const float inv_l = 1.0f / sqrtf(ssum / static_cast<float>(a.d) + a.eps);
+    for (int w = 0; w < 4; ++w) ssum += rss[w][rt][l32] + rss[w][rt][32 + l32];
+    inv_l = 1.0f / sqrtf(ssum / static_cast<float>(a.d) + a.eps);
+  }
 
   if (!wblock) {
     // U_t: lane holds rank ct * 32 + l32 of token rows (v / 4) * 8 + h32 * 4 + v % 4
@@ -316,6 +447,14 @@ __global__ __launch_bounds__(256, 1) void decode_main_kernel(MainArgs a) {
       }
     }
   }
+}
+
+__global__ __launch_bounds__(256, 1) void decode_main_kernel(MainArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kRingBytes + 2 * kMaxD];
+  if (a.nf4 && static_cast<int>(blockIdx.x) < a.n_wblocks)
+    decode_main_body<true>(a, smem);
+  else
+    decode_main_body<false>(a, smem);
 }
 
 // ---------------------------------------------------------------- finish
@@ -455,7 +594,22 @@ hipError_t launch_fwd_decode(const FwdParams& p, hipStream_t s) {
   MainArgs ma{};
   ma.x = static_cast<const uint16_t*>(p.x);
   ma.gamma = static_cast<const uint16_t*>(p.gamma);
+  if (p.nf4) {
+    PrepArgs pa{};
+    pa.x = ma.x;
+    pa.gamma = ma.gamma;
+    pa.xg = reinterpret_cast<uint16_t*>(ws + L.xg);
+    pa.inv = reinterpret_cast<float*>(ws + L.inv);
+    pa.T = p.T;
+    pa.d = static_cast<int>(p.d);
+    pa.eps = p.eps;
+    hipLaunchKernelGGL(decode_prep_kernel, dim3(static_cast<unsigned>((p.T + 3) / 4)), dim3(256), 0, s, pa);
+    ma.xg = pa.xg;
+    ma.inv = pa.inv;
+  }
   ma.w = static_cast<const uint16_t*>(p.w);
+  ma.nf4 = p.nf4;
+  if (p.nf4) ma.wq = nf4_view(p.w, p.N, p.d);
   ma.bias = p.has_bias ? static_cast<const uint16_t*>(p.bias) : nullptr;
   for (int i = 0; i < 3; ++i) ma.a[i] = static_cast<const uint16_t*>(p.a[L.tgt[i]]);
   ma.pos = p.pos;

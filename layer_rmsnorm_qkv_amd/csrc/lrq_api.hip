@@ -202,7 +202,7 @@ int select(const lrq_desc* d, const lrq::FwdParams& p, bool backward) {
   }
   const bool bf16 = d->dtype == LRQ_BF16;
   const bool tiled = bf16 && lrq::tiled_supports(p);
-  const bool decode = bf16 && !p.dropout && !p.nf4 && lrq::decode_supports(p);
+  const bool decode = bf16 && !p.dropout && lrq::decode_supports(p);
   switch (d->variant) {
     case LRQ_VARIANT_AUTO:
       if (decode && p.T <= kDecodeMaxTokens) return LRQ_VARIANT_DECODE;

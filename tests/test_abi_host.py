@@ -160,11 +160,11 @@ def test_nf4_sizes_and_checks():
     expect(B.LRQ_ERR_INVALID_ARG, B.lrq_quantize_nf4, d, FAKE, FAKE, 100)
     expect(B.LRQ_ERR_INVALID_ARG, B.lrq_quantize_nf4, d, None, FAKE, 1 << 20)
     expect(B.LRQ_ERR_UNSUPPORTED, B.lrq_quantize_nf4, d, FAKE + 4, FAKE, 1 << 20)
-    # the decode family does not take NF4 weights
+    # every bf16 family takes NF4 weights (decode included)
     dec = dict(n_tokens=4, d_model=1024, n_q_heads=8, n_kv_heads=2, head_dim=128, dtype=B.LRQ_BF16)
-    assert B.lrq_select_variant(good_desc(**dec, weight_format=B.LRQ_WEIGHT_NF4)) == B.LRQ_VARIANT_TILED
+    assert B.lrq_select_variant(good_desc(**dec, weight_format=B.LRQ_WEIGHT_NF4)) == B.LRQ_VARIANT_DECODE
     assert B.lrq_select_variant(good_desc(**dec, weight_format=B.LRQ_WEIGHT_NF4,
-                                          variant=B.LRQ_VARIANT_DECODE)) == -1
+                                          variant=B.LRQ_VARIANT_TILED)) == B.LRQ_VARIANT_TILED
     # T == 0 with NF4 is still a no-op
     B.lrq_forward(good_desc(d_model=128, n_tokens=0, weight_format=B.LRQ_WEIGHT_NF4), None, None, None, None,
                   [FAKE, None, FAKE], [FAKE, None, FAKE], None, None)

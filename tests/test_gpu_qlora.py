@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 TQ, TK, TV = wl.TARGET_Q, wl.TARGET_K, wl.TARGET_V
 TRAIN = wl.get("train")
-VARIANTS = {"generic": B.LRQ_VARIANT_GENERIC, "tiled": B.LRQ_VARIANT_TILED}
+VARIANTS = {"generic": B.LRQ_VARIANT_GENERIC, "tiled": B.LRQ_VARIANT_TILED, "decode": B.LRQ_VARIANT_DECODE}
 
 CASES = {
     "f32_t37_allt_bias": wl.get("tiny").replace(n_tokens=37, d_model=128, lora_targets=TQ | TK | TV,
@@ -81,13 +81,17 @@ def test_qlora_forward_backward(name, variant):
     w = CASES[name]
     inp = wl.make_inputs(w, with_dy=True)
     log(f"[gpu] qlora {name} variant={variant}")
-    prob, res = run_case(w, inp, VARIANTS[variant], backward=True)
+    prob, res = run_case(w, inp, VARIANTS[variant], backward=variant != "decode")
     codes, scales = oracle_nf4(inp)
     spec = spec_of(w)
     ref = q.forward(spec, inp["x"], inp["gamma"], codes, scales, inp["bias"], inp["a"], inp["b"], inp["positions"])
     got = to_np(res["out"])
     errs = {"out": o.rel_frobenius(got, ref), "out_row": row_rel_errors(got, ref),
             "out_elem": elem_ratio(got, ref, w.dtype)}
+    if variant == "decode":  # a forward family
+        log(f"  errors {errs}")
+        assert_parity(errs, w.dtype)
+        return
     rdx, rda, rdb = q.backward(spec, inp["x"], inp["gamma"], codes, scales, inp["bias"], inp["a"], inp["b"],
                                inp["positions"], inp["dy"])
     gdx = to_np(res["dx"])
@@ -133,6 +137,37 @@ def test_qlora_with_dropout():
             "dx": o.rel_frobenius(gdx, rdx), "dx_elem": elem_ratio(gdx, rdx, "bf16")}
     log(f"  errors {errs}")
     assert_parity(errs, "bf16")
+
+
+def test_qlora_decode_full_size_with_cache():
+    """The decode workload (64 rows, Llama-2-7B layer, rank 64 on q, k, v, bias) with its base
+    in NF4, through the decode family with a key/value cache: every output row, and the cache
+    rows equal to the output's k and v blocks bit for bit."""
+    import torch
+    w = wl.get("decode")
+    inp = wl.make_inputs(w)
+    desc = desc_for(w, nf4=True)
+    assert B.lrq_select_variant(desc) == B.LRQ_VARIANT_DECODE
+    prob = DeviceProblem(w, inp, nf4=True)
+    kvw = w.n_kv_heads * w.head_dim
+    n_slots = 100
+    slots = np.random.default_rng(3).permutation(n_slots)[:w.n_tokens].astype(np.int32)
+    kc = torch.zeros((n_slots, kvw), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    B.lrq_forward_kv(prob.desc, prob.x, prob.gamma, prob.w_qkv, prob.bias, prob.a, prob.b, prob.positions,
+                     prob.out, kc, vc, torch.from_numpy(slots).cuda(), n_slots, prob.workspace)
+    torch.cuda.synchronize()
+    codes, scales = oracle_nf4(inp)
+    ref = q.forward(spec_of(w), inp["x"], inp["gamma"], codes, scales, inp["bias"], inp["a"], inp["b"],
+                    inp["positions"])
+    got = to_np(prob.out)
+    errs = {"out": o.rel_frobenius(got, ref), "out_row": row_rel_errors(got, ref),
+            "out_elem": elem_ratio(got, ref, "bf16")}
+    log(f"  errors {errs}")
+    assert_parity(errs, "bf16")
+    k0 = w.target_columns()[wl.TARGET_K][0]
+    assert torch.equal(kc[torch.from_numpy(slots).long().cuda()], prob.out[:, k0:k0 + kvw])
+    assert torch.equal(vc[torch.from_numpy(slots).long().cuda()], prob.out[:, k0 + kvw:k0 + 2 * kvw])
 
 
 def test_qlora_llama3_full_size():
