@@ -4,39 +4,60 @@
 //
 // Work: one workgroup per (sequence, kv head g, block of 128 query rows), a query row being a
 // (token, q head of g's group) pair, row = token * G + head (G = Hq / Hkv), so the group's
-// heads share every K/V tile.  Four wavefronts, 32 rows each.
+// heads share every K/V tile.  Four wavefronts, 32 rows each.  The blocks of one (sequence,
+// kv head) pair all land on one XCD (they read the same keys and values through its L2), and
+// with a causal mask the blocks with the longest key windows are dispatched first.
 // Per tile of 64 keys (gathered through the slot list):
-//   load     K rows and V rows into registers (the next tile's, while this one is computed),
-//            then into LDS: K row-major [key][d], V transposed [d][key] (pairs of keys packed
-//            into one 32-bit LDS word), both padded against bank conflicts; double-buffered.
+//   load     K and V rows go from global memory straight into LDS (16 bytes per lane,
+//            global_load_lds_dwordx4; no registers, no LDS store instructions), through a
+//            ring of two stages; each row is 256 bytes with its 16-byte chunks XOR-swizzled
+//            by key.  A key past the sequence or a slot outside the cache loads a zero row.
+//            Slot numbers are read two tiles ahead of their rows.
 //   scores   S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (Q stays in registers for the whole
 //            kernel): lane (l32, h) then holds the scores of query row l32 for keys
 //            8 (v / 4) + 4 h + v % 4, v = 0..15, of each 32-key half.
-//   softmax  online, in base 2 (scores pre-multiplied by scale * log2 e): running row max
-//            from the two lanes of a row, rescale of the running sum and of the output.
-//   P V      the score registers are already the A operand of O = P V for a permuted key order
-//            (16-key step s: keys 16 s + 4 h + 0..3 and 16 s + 8 + 4 h + 0..3); the B operand
-//            reads the same keys of V^T as two 8-byte LDS reads.
-// Causal windows are per query row; keys past a row's window score -inf.  Slots outside the
-// cache read as zero vectors (never out of bounds).  Rows with no visible key are written 0.
+//   softmax  online, in base 2: running row max of the raw scores over the row's two lanes
+//            (v_permlane32_swap), probabilities exp2(s * scale * log2 e - max * scale * log2 e)
+//            (one fma each), rescale of the running sum and (when a row's max moved) of O.
+//   P V      computed transposed, O^T += V^T P^T: the score registers are already the B
+//            operand for a permuted key order (16-key step s: keys 16 s + 4 h + 0..3 and
+//            16 s + 8 + 4 h + 0..3), and the A operand V^T is read from the row-major V tile
+//            with the LDS transpose read (ds_read_b64_tr_b16).  Each lane's accumulators then
+//            belong to its own query row (head-dim columns 32 dt + 8 j + 4 h + 0..3), so the
+//            rescale and the final normalisation need no cross-lane traffic, and each lane
+//            stores 8-byte runs of its row.
+// Causal windows are per query row; keys past a row's window score -inf.  Rows with no
+// visible key are written 0.
 #include <algorithm>
 
 #include "lrq_internal.h"
+#include "tile_common.h"
 
 namespace lrq {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
-constexpr int kD = 128;                 // head size
-constexpr int kKT = 64;                 // keys per tile
-constexpr int kRowsWG = 128;            // query rows per workgroup
-constexpr int kKPitch = kD * 2 + 16;    // bytes per K row in LDS (272)
-constexpr int kVPitch = kKT * 2 + 8;    // bytes per V^T row in LDS (136)
-constexpr int kKBytes = kKT * kKPitch;  // 17408
-constexpr int kVBytes = kD * kVPitch;   // 17408
-constexpr int kBufBytes = kKBytes + kVBytes;
+constexpr int kD = 128;                      // head size
+constexpr int kKT = 64;                      // keys per tile
+constexpr int kRowsWG = 128;                 // query rows per workgroup
+constexpr int kRowBytes = kD * 2;            // one K or V row in LDS: 256 bytes, unpadded
+constexpr int kTileBytes = kKT * kRowBytes;  // 16 KB
+constexpr int kStageBytes = 2 * kTileBytes;  // K tile, then V tile
+constexpr int kPairsPerXcd = 8;              // XCDs: consecutive workgroups go to consecutive XCDs
+
+// The DMA source of keys past the sequence and of slots outside the cache.
+__device__ __attribute__((aligned(256))) uint16_t g_zero_row[kD] = {};
+
+// XOR of the 16-byte chunk index of V row `key` (by key % 4: 0, 10, 4, 14).  A transpose read
+// takes four consecutive keys at two adjacent chunks in each 16-lane group and four keys at four
+// adjacent chunks in each 32 lanes: these masks send both sets to distinct bank groups of a
+// 128-byte and of a 256-byte window.  K rows use key % 16 (16 consecutive keys at one chunk).
+__device__ __forceinline__ int v_xor(int key) { return ((key & 1) ? 10 : 0) ^ ((key & 2) ? 4 : 0); }
 
 struct AttnArgs {
   const uint16_t* q;
@@ -50,43 +71,58 @@ struct AttnArgs {
   const int32_t* kv_slots;
   uint16_t* out;
   int64_t ld_o;
-  int Hq, Hkv, G;
-  int max_q_len;  // rows of a sequence past this bound are not computed
+  int Hkv, G;
+  int pairs, pairs8;  // (sequence, kv head) pairs, rounded up to a multiple of 8
+  int mblocks;        // 128-row blocks per sequence
+  int max_q_len;      // rows of a sequence past this bound are not computed
   float scale_log2e;
   int causal;
 };
 
-__device__ __forceinline__ uint4 load_row16(const uint16_t* base, int64_t ld, int64_t slot, int64_t num_slots,
-                                            int off) {
-  if (slot < 0 || slot >= num_slots) return uint4{0u, 0u, 0u, 0u};
-  return *reinterpret_cast<const uint4*>(base + slot * ld + off);
+__device__ __forceinline__ float pair_max(float x) {
+  // max of x over lanes l and l ^ 32
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kBufBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStageBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h32 = lane >> 5;
-  const int b = blockIdx.x, g = blockIdx.z;
-  const int64_t q0 = a.q_indptr[b], q_len = a.q_indptr[b + 1] - q0;
-  const int64_t kv0 = a.kv_indptr[b], kv_len = a.kv_indptr[b + 1] - kv0;
-  const int64_t n_rows = min(q_len, static_cast<int64_t>(a.max_q_len)) * a.G;
-  const int64_t rho0 = static_cast<int64_t>(blockIdx.y) * kRowsWG;
+  // block -> (pair, row block): ids m * pairs8 + pair, so a pair's blocks share id % 8 (one XCD)
+  const int m_ord = static_cast<int>(blockIdx.x) / a.pairs8;
+  const int pair = static_cast<int>(blockIdx.x) - m_ord * a.pairs8;
+  if (pair >= a.pairs) return;
+  const int b = pair / a.Hkv, g = pair - b * a.Hkv;
+  const int mblk = a.causal ? a.mblocks - 1 - m_ord : m_ord;  // longest windows first
+  const int64_t q0 = a.q_indptr[b];
+  const int q_len = a.q_indptr[b + 1] - static_cast<int>(q0);
+  const int64_t kv0 = a.kv_indptr[b];
+  const int kv_len = a.kv_indptr[b + 1] - static_cast<int>(kv0);
+  const int n_rows = min(q_len, a.max_q_len) * a.G;
+  const int rho0 = mblk * kRowsWG;
   if (rho0 >= n_rows) return;  // uniform over the workgroup
 
   // keys the workgroup needs: up to the last row's window
-  const int64_t last_row = min(n_rows, rho0 + kRowsWG) - 1;
-  const int64_t kv_end = a.causal ? min(kv_len, kv_len - q_len + last_row / a.G + 1) : kv_len;
-  const int n_tiles = kv_end > 0 ? static_cast<int>((kv_end + kKT - 1) / kKT) : 0;
+  const int last_row = min(n_rows, rho0 + kRowsWG) - 1;
+  const int kv_end = a.causal ? min(kv_len, kv_len - q_len + last_row / a.G + 1) : kv_len;
+  const int n_tiles = kv_end > 0 ? (kv_end + kKT - 1) / kKT : 0;
 
-  // this lane's query row (as the B operand of S^T and the softmax row)
-  const int64_t rw0 = rho0 + wave * 32;  // first row of the wave
+  // this lane's query row (the B operand of S^T, the softmax row and the output row)
+  const int rw0 = rho0 + wave * 32;  // first row of the wave
   const bool wave_active = rw0 < n_rows;
-  const int64_t my_row = rw0 + l32;
+  const int my_row = rw0 + l32;
   const bool row_ok = my_row < n_rows;
-  const int64_t my_tok = row_ok ? my_row / a.G : 0;
-  const int my_head = g * a.G + static_cast<int>(row_ok ? my_row % a.G : 0);
-  const int64_t my_lim = !row_ok ? -1 : (a.causal ? kv_len - q_len + my_tok : kv_len - 1);
+  const int my_tok = row_ok ? my_row / a.G : 0;
+  const int my_head = g * a.G + (row_ok ? my_row - my_tok * a.G : 0);
+  const int my_lim = !row_ok ? -1 : (a.causal ? kv_len - q_len + my_tok : kv_len - 1);
+  // smallest window end of the wave's rows (-1 when some row is past the sequence)
+  const int wave_min_lim = rw0 + 31 < n_rows ? (a.causal ? kv_len - q_len + rw0 / a.G : kv_len - 1) : -1;
   bf16x8 qf[kD / 16];
   {
     const uint16_t* qr = a.q + (q0 + my_tok) * a.ld_q + static_cast<int64_t>(my_head) * kD + 8 * h32;
@@ -97,55 +133,57 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     }
   }
 
-  // ---- tile loads: K rows (tid / 16) + 16 c, chunk tid % 16; V key pairs (tid / 16) + 16 c
-  const int chunk = tid & 15, rsub = tid >> 4;
-  const int64_t koff = static_cast<int64_t>(g) * kD + chunk * 8;
-  // slot numbers are loaded two tiles ahead of their rows, so a tile's row loads never wait for
-  // a slot-list load
-  uint4 kreg[4], vreg[2][2];
-  int32_t kslot[4], vslot[4];
+  // ---- DMA: instruction c of wave w fills keys 16 w + 4 c .. + 3 of the tile (1 KB); lane
+  // `lane` takes LDS chunk position lane % 16 of key 16 w + 4 c + lane / 16, whose source is
+  // the logical chunk position ^ (key % 16) of K and position ^ v_xor(key) of V.
+  const int kq = lane >> 4, pos = lane & 15;
+  int kchunk[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) kchunk[c] = pos ^ (4 * c + kq);
+  const int vchunk = pos ^ v_xor(kq);
+  const uint16_t* kc_g = a.kc + static_cast<int64_t>(g) * kD;
+  const uint16_t* vc_g = a.vc + static_cast<int64_t>(g) * kD;
+  const uint32_t lds0 = tile::lds_addr(smem) + static_cast<uint32_t>(wave) * 4096u;
+  int32_t sl[4];  // slots of the next tile to load (-1: zero row)
   auto load_slots = [&](int t) {
-    const int64_t base = static_cast<int64_t>(t) * kKT;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int64_t key = base + rsub + 16 * c;
-      kslot[c] = key < kv_end ? a.kv_slots[kv0 + key] : -1;
-    }
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int64_t key = base + 2 * (rsub + 16 * c) + e;
-        vslot[2 * c + e] = key < kv_end ? a.kv_slots[kv0 + key] : -1;
-      }
-  };
-  auto load_tile = [&]() {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) kreg[c] = load_row16(a.kc, a.ld_kv, kslot[c], a.num_slots, static_cast<int>(koff));
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        vreg[c][e] = load_row16(a.vc, a.ld_kv, vslot[2 * c + e], a.num_slots, static_cast<int>(koff));
-  };
-  auto store_tile = [&](int buf) {
-    unsigned char* kb = smem + buf * kBufBytes;
-    unsigned char* vb = kb + kKBytes;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4*>(kb + (rsub + 16 * c) * kKPitch + chunk * 16) = kreg[c];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const uint32_t w0[4] = {vreg[c][0].x, vreg[c][0].y, vreg[c][0].z, vreg[c][0].w};
-      const uint32_t w1[4] = {vreg[c][1].x, vreg[c][1].y, vreg[c][1].z, vreg[c][1].w};
-      const int pair = rsub + 16 * c;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t lo = (e & 1) ? (w0[e >> 1] >> 16) : (w0[e >> 1] & 0xffffu);
-        const uint32_t hi = (e & 1) ? (w1[e >> 1] >> 16) : (w1[e >> 1] & 0xffffu);
-        *reinterpret_cast<uint32_t*>(vb + (chunk * 8 + e) * kVPitch + pair * 4) = lo | (hi << 16);
-      }
+      const int key = t * kKT + 16 * wave + 4 * c + kq;
+      const int32_t s = a.kv_slots[kv0 + min(key, kv_end - 1)];
+      sl[c] = key < kv_end && s >= 0 && s < a.num_slots ? s : -1;
     }
   };
+  auto issue_dma = [&](int buf) {
+    const uint32_t dst = lds0 + static_cast<uint32_t>(buf * kStageBytes);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      // sl[c] >= 0 wherever the row is used: one 32 x 32 -> 64-bit multiply
+      const uint64_t row = static_cast<uint64_t>(static_cast<uint32_t>(sl[c])) * static_cast<uint32_t>(a.ld_kv);
+      const uint16_t* ks = sl[c] >= 0 ? kc_g + row + 8 * kchunk[c] : g_zero_row + 8 * kchunk[c];
+      const uint16_t* vs = sl[c] >= 0 ? vc_g + row + 8 * vchunk : g_zero_row + 8 * vchunk;
+      tile::dma16(ks, dst + c * 1024);
+      tile::dma16(vs, dst + kTileBytes + c * 1024);
+    }
+  };
+
+  // ---- LDS read offsets of this lane
+  // K (A operand of S^T): key 32 st + l32, logical chunk 2 ks + h32 at position ^ (l32 % 16)
+  const int k_row_off = l32 * kRowBytes;
+  const int k_xor = (l32 & 15) ^ h32;  // (2 ks + h32) ^ (l32 % 16) = 2 ks ^ k_xor
+  // V (A operand of O^T, transpose read): in 16-lane group q = lane / 16, lane j reads the
+  // 8 bytes of key 4 (q / 2) + j / 4 (+ 16 s + 8 half) at head-dim columns 32 dt + 16 (q % 2)
+  // + 4 (j % 4) .. + 3; the read hands lane j of the group that key's column 32 dt + 16 (q % 2)
+  // + j for each of the four keys.
+  int v_off[kD / 32];
+  {
+    const int q = lane >> 4, j = lane & 15;
+    const int key = 4 * (q >> 1) + (j >> 2);
+#pragma unroll
+    for (int dt = 0; dt < kD / 32; ++dt) {
+      const int chunk = 4 * dt + 2 * (q & 1) + ((j & 3) >> 1);
+      v_off[dt] = key * kRowBytes + ((chunk ^ v_xor(key)) << 4) + 8 * (j & 1);
+    }
+  }
 
   floatx16 o[kD / 32];
 #pragma unroll
@@ -154,103 +192,98 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 
   if (n_tiles > 0) {
     load_slots(0);
-    load_tile();
+    issue_dma(0);
     if (n_tiles > 1) load_slots(1);
-    store_tile(0);
   }
-  __syncthreads();
   for (int t = 0; t < n_tiles; ++t) {
+    // tile t is in LDS (every wave's loads), and every wave is done with tile t - 1
+    tile::wait_barrier<0>();
     if (t + 1 < n_tiles) {
-      load_tile();  // rows of tile t + 1 (their slots were loaded an iteration ago)
+      issue_dma((t + 1) & 1);  // slots of tile t + 1 were read an iteration ago
       if (t + 2 < n_tiles) load_slots(t + 2);
     }
-    if (wave_active) {
-      const unsigned char* kb = smem + (t & 1) * kBufBytes;
-      const unsigned char* vb = kb + kKBytes;
-      // ---- S^T = K Q^T for the two 32-key halves
-      floatx16 s[2];
+    if (!wave_active) continue;
+    const unsigned char* kb = smem + (t & 1) * kStageBytes;
+    const unsigned char* vb = kb + kTileBytes;
+    // ---- S^T = K Q^T for the two 32-key halves
+    floatx16 s[2];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        s[st] = floatx16{};
-        const unsigned char* krow = kb + (st * 32 + l32) * kKPitch + h32 * 16;
+    for (int st = 0; st < 2; ++st) {
+      s[st] = floatx16{};
+      const unsigned char* krow = kb + st * 32 * kRowBytes + k_row_off;
 #pragma unroll
-        for (int ks = 0; ks < kD / 16; ++ks) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + ks * 32);
-          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[st], 0, 0, 0);
-        }
-      }
-      // ---- scale, mask, running max
-      const int64_t kbase = static_cast<int64_t>(t) * kKT + 4 * h32;
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t key = kbase + st * 32 + (v >> 2) * 8 + (v & 3);
-          const float x = key <= my_lim ? s[st][v] * a.scale_log2e : -INFINITY;
-          s[st][v] = x;
-          mloc = fmaxf(mloc, x);
-        }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float m_new = fmaxf(m_run, mloc);
-      // rows that have seen no key yet keep m = -inf: scale 1, probabilities 0
-      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      float lsum = 0.f;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = __builtin_amdgcn_exp2f(s[st][v] - m_use);
-          s[st][v] = p;
-          lsum += p;
-        }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-      // ---- rescale O: its rows are 8 (v / 4) + 4 h + v % 4, whose alpha lane l32 = that row holds
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float al = __shfl(alpha, (v >> 2) * 8 + h32 * 4 + (v & 3));
-#pragma unroll
-        for (int dt = 0; dt < kD / 32; ++dt) o[dt][v] *= al;
-      }
-      // ---- O += P V over 4 steps of 16 keys
-#pragma unroll
-      for (int sstep = 0; sstep < kKT / 16; ++sstep) {
-        bf16x8 pf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[e] = static_cast<__bf16>(s[sstep >> 1][8 * (sstep & 1) + e]);
-        const int k0 = 16 * sstep + 4 * h32;
-#pragma unroll
-        for (int dt = 0; dt < kD / 32; ++dt) {
-          const unsigned char* vrow = vb + (dt * 32 + l32) * kVPitch;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + k0 * 2);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (k0 + 8) * 2);
-          const uint4 vv = uint4{lo.x, lo.y, hi.x, hi.y};
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf, __builtin_bit_cast(bf16x8, vv), o[dt], 0, 0, 0);
-        }
+      for (int ks = 0; ks < kD / 16; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + ((2 * ks ^ k_xor) << 4));
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[st], 0, 0, 0);
       }
     }
-    if (t + 1 < n_tiles) store_tile((t + 1) & 1);
-    __syncthreads();
+    // ---- mask: only a tile that reaches past some row's window (wave-uniform test)
+    const int t0 = t * kKT;
+    if (t0 + kKT - 1 > wave_min_lim) {
+      const int lim = max(min(my_lim - t0, kKT), -1);
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (4 * h32 + st * 32 + (v >> 2) * 8 + (v & 3) > lim) s[st][v] = -INFINITY;
+    }
+    // ---- running max on the raw scores (the scale is positive), probabilities in base 2
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, s[st][v]);
+    const float m_new = fmaxf(m_run, pair_max(mloc));
+    // rows that have seen no key yet keep m = -inf: scale 1, probabilities 0
+    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * a.scale_log2e);
+    const float mc = m_new == -INFINITY ? 0.f : m_new * a.scale_log2e;
+    float lsum = 0.f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[st][v], a.scale_log2e, -mc));
+        s[st][v] = p;
+        lsum += p;
+      }
+    l_run = l_run * alpha + lsum;  // this lane's half of the row sum
+    m_run = m_new;
+    if (!__all(alpha == 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt) o[dt] *= alpha;
+    }
+    // ---- O^T += V^T P^T over 4 steps of 16 keys
+#pragma unroll
+    for (int sstep = 0; sstep < kKT / 16; ++sstep) {
+      bf16x8 pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = static_cast<__bf16>(s[sstep >> 1][8 * (sstep & 1) + e]);
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt) {
+        const unsigned char* vp = vb + v_off[dt] + 16 * sstep * kRowBytes;
+        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(vp));
+        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(vp + 8 * kRowBytes));
+        const shortx4 vv[2] = {lo, hi};
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[dt], 0, 0, 0);
+      }
+    }
   }
 
   if (!wave_active) return;
-  // ---- normalise and store: O row q' = 8 (v / 4) + 4 h + v % 4 of the wave
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // ---- normalise and store: lane (l32, h) holds row my_row, columns 32 dt + 8 j + 4 h + 0..3
+  const float l_tot = pair_sum(l_run);
   const float inv_l = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (!row_ok) return;
+  uint16_t* orow = a.out + (q0 + my_tok) * a.ld_o + static_cast<int64_t>(my_head) * kD + 4 * h32;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int qr = (v >> 2) * 8 + h32 * 4 + (v & 3);
-    const float il = __shfl(inv_l, qr);
-    const int64_t row = rw0 + qr;
-    if (row >= n_rows) continue;
-    const int64_t tok = row / a.G;
-    const int head = g * a.G + static_cast<int>(row % a.G);
-    uint16_t* orow = a.out + (q0 + tok) * a.ld_o + static_cast<int64_t>(head) * kD + l32;
+  for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < kD / 32; ++dt) orow[dt * 32] = f32_to_bf16_bits(o[dt][v] * il);
-  }
+    for (int j = 0; j < 4; ++j) {
+      bf16x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = static_cast<__bf16>(o[dt][4 * j + e] * inv_l);
+      *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * j) = __builtin_bit_cast(uint2, r);
+    }
 }
 
 }  // namespace
@@ -271,16 +304,17 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   a.kv_slots = p.kv_slots;
   a.out = static_cast<uint16_t*>(p.out);
   a.ld_o = static_cast<int64_t>(p.Hq) * kD;
-  a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.G = p.Hq / p.Hkv;
+  a.pairs = p.n_seqs * p.Hkv;
+  a.pairs8 = (a.pairs + kPairsPerXcd - 1) / kPairsPerXcd * kPairsPerXcd;
+  a.mblocks = static_cast<int>((static_cast<int64_t>(p.max_q_len) * a.G + kRowsWG - 1) / kRowsWG);
   a.max_q_len = p.max_q_len;
   a.scale_log2e = p.scale * 1.4426950408889634f;
   a.causal = p.causal;
-  const int64_t mblocks = (static_cast<int64_t>(p.max_q_len) * a.G + kRowsWG - 1) / kRowsWG;
-  dim3 grid(static_cast<unsigned>(p.n_seqs), static_cast<unsigned>(mblocks), static_cast<unsigned>(p.Hkv));
+  const int64_t blocks = static_cast<int64_t>(a.mblocks) * a.pairs8;
   timing_begin(s);
-  hipLaunchKernelGGL(attn_kernel, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a);
   timing_end(s);
   return hipGetLastError();
 }
