@@ -48,7 +48,8 @@ constexpr int kRowsWG = 128;                 // query rows per workgroup
 constexpr int kRowBytes = kD * 2;            // one K or V row in LDS: 256 bytes, unpadded
 constexpr int kTileBytes = kKT * kRowBytes;  // 16 KB
 constexpr int kStageBytes = 2 * kTileBytes;  // K tile, then V tile
-constexpr int kPairsPerXcd = 8;              // XCDs: consecutive workgroups go to consecutive XCDs
+constexpr int kPairsPerXcd = 8;
+constexpr float kLazyLog2 = 8.f;             // rescale threshold of the running max (exp2 units)              // XCDs: consecutive workgroups go to consecutive XCDs
 
 // The DMA source of keys past the sequence and of slots outside the cache.
 __device__ __attribute__((aligned(256))) uint16_t g_zero_row[kD] = {};
@@ -83,10 +84,6 @@ __device__ __forceinline__ float pair_max(float x) {
   // max of x over lanes l and l ^ 32
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
@@ -123,16 +120,6 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   const int my_lim = !row_ok ? -1 : (a.causal ? kv_len - q_len + my_tok : kv_len - 1);
   // smallest window end of the wave's rows (-1 when some row is past the sequence)
   const int wave_min_lim = rw0 + 31 < n_rows ? (a.causal ? kv_len - q_len + rw0 / a.G : kv_len - 1) : -1;
-  bf16x8 qf[kD / 16];
-  {
-    const uint16_t* qr = a.q + (q0 + my_tok) * a.ld_q + static_cast<int64_t>(my_head) * kD + 8 * h32;
-#pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) {
-      const uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qr + 16 * ks) : uint4{0u, 0u, 0u, 0u};
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-
   // ---- DMA: instruction c of wave w fills keys 16 w + 4 c .. + 3 of the tile (1 KB); lane
   // `lane` takes LDS chunk position lane % 16 of key 16 w + 4 c + lane / 16, whose source is
   // the logical chunk position ^ (key % 16) of K and position ^ v_xor(key) of V.
@@ -141,26 +128,32 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) kchunk[c] = pos ^ (4 * c + kq);
   const int vchunk = pos ^ v_xor(kq);
-  const uint16_t* kc_g = a.kc + static_cast<int64_t>(g) * kD;
-  const uint16_t* vc_g = a.vc + static_cast<int64_t>(g) * kD;
+  const char* kc_g = reinterpret_cast<const char*>(a.kc + static_cast<int64_t>(g) * kD);
+  const char* vc_g = reinterpret_cast<const char*>(a.vc + static_cast<int64_t>(g) * kD);
+  const uint32_t row_bytes = static_cast<uint32_t>(a.ld_kv) * 2u;
+  // the zero row's address, kept in scalar registers (not reloaded in the loop)
+  const char* zrow = reinterpret_cast<const char*>(g_zero_row);
+  asm volatile("" : "+s"(zrow));
   const uint32_t lds0 = tile::lds_addr(smem) + static_cast<uint32_t>(wave) * 4096u;
-  int32_t sl[4];  // slots of the next tile to load (-1: zero row)
+  // Slot numbers of the next tile to load, as read from the list: they are checked only where
+  // the DMA uses them (an iteration later), so no wave waits for the slot-list loads.
+  int32_t sl[4];
+  int sl_tile = 0;  // the tile sl belongs to
   auto load_slots = [&](int t) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int key = t * kKT + 16 * wave + 4 * c + kq;
-      const int32_t s = a.kv_slots[kv0 + min(key, kv_end - 1)];
-      sl[c] = key < kv_end && s >= 0 && s < a.num_slots ? s : -1;
-    }
+    for (int c = 0; c < 4; ++c) sl[c] = a.kv_slots[kv0 + min(t * kKT + 16 * wave + 4 * c + kq, kv_end - 1)];
+    sl_tile = t;
   };
   auto issue_dma = [&](int buf) {
     const uint32_t dst = lds0 + static_cast<uint32_t>(buf * kStageBytes);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      // sl[c] >= 0 wherever the row is used: one 32 x 32 -> 64-bit multiply
-      const uint64_t row = static_cast<uint64_t>(static_cast<uint32_t>(sl[c])) * static_cast<uint32_t>(a.ld_kv);
-      const uint16_t* ks = sl[c] >= 0 ? kc_g + row + 8 * kchunk[c] : g_zero_row + 8 * kchunk[c];
-      const uint16_t* vs = sl[c] >= 0 ? vc_g + row + 8 * vchunk : g_zero_row + 8 * vchunk;
+      const int key = sl_tile * kKT + 16 * wave + 4 * c + kq;
+      const bool ok = key < kv_end && sl[c] >= 0 && sl[c] < a.num_slots;  // else a zero row
+      // one 32 x 32 -> 64-bit multiply (sl[c] >= 0 wherever the row is used), in bytes
+      const uint64_t row = static_cast<uint64_t>(static_cast<uint32_t>(sl[c])) * row_bytes;
+      const char* ks = ok ? kc_g + row + 16 * kchunk[c] : zrow + 16 * kchunk[c];
+      const char* vs = ok ? vc_g + row + 16 * vchunk : zrow + 16 * vchunk;
       tile::dma16(ks, dst + c * 1024);
       tile::dma16(vs, dst + kTileBytes + c * 1024);
     }
@@ -188,12 +181,40 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   floatx16 o[kD / 32];
 #pragma unroll
   for (int dt = 0; dt < kD / 32; ++dt) o[dt] = floatx16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY;
+  // row sums: every entry of lane (l32, h) accumulates row l32's sum; entry 0 is kept scaled
+  floatx16 lsum = floatx16{};
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = static_cast<__bf16>(1.0f);
 
+  // ---- Q rows and output rows: lane `lane` moves 16-byte chunk lane % 16 of the wave's rows
+  // 4 c + lane / 16, c = 0..7 (four whole 256-byte rows per instruction)
+  auto row_off = [&](int c, int64_t ld) -> int64_t {  // -1: row past the sequence's rows
+    const int rho = rw0 + 4 * c + kq;
+    if (rho >= n_rows) return -1;
+    const int tok = rho / a.G;
+    return (q0 + tok) * ld + static_cast<int64_t>(g * a.G + rho - tok * a.G) * kD;
+  };
+  bf16x8 qf[kD / 16];
   if (n_tiles > 0) {
     load_slots(0);
+    {
+      // Q rows of the wave into stage 1 (row r of the workgroup at r * 256, chunks XOR r % 16)
+      const uint32_t dst = tile::lds_addr(smem) + kStageBytes + static_cast<uint32_t>(wave) * 8192u;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int chunk = pos ^ ((4 * c + kq) & 15);
+        const int64_t off = row_off(c, a.ld_q);
+        tile::dma16(off >= 0 ? reinterpret_cast<const char*>(a.q + off) + 16 * chunk : zrow + 16 * chunk, dst + c * 1024);
+      }
+    }
     issue_dma(0);
     if (n_tiles > 1) load_slots(1);
+    tile::wait_barrier<0>();
+    const unsigned char* qrow = smem + kStageBytes + (32 * wave + l32) * kRowBytes;
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ((2 * ks ^ k_xor) << 4));
   }
   for (int t = 0; t < n_tiles; ++t) {
     // tile t is in LDS (every wave's loads), and every wave is done with tile t - 1
@@ -205,54 +226,52 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     if (!wave_active) continue;
     const unsigned char* kb = smem + (t & 1) * kStageBytes;
     const unsigned char* vb = kb + kTileBytes;
-    // ---- S^T = K Q^T for the two 32-key halves
-    floatx16 s[2];
+    // ---- S^T = K Q^T for the two 32-key halves (their accumulation chains interleaved)
+    floatx16 s[2] = {floatx16{}, floatx16{}};
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      s[st] = floatx16{};
-      const unsigned char* krow = kb + st * 32 * kRowBytes + k_row_off;
+    for (int ks = 0; ks < kD / 16; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < kD / 16; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + ((2 * ks ^ k_xor) << 4));
+      for (int st = 0; st < 2; ++st) {
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(kb + st * 32 * kRowBytes + k_row_off + ((2 * ks ^ k_xor) << 4));
         s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[st], 0, 0, 0);
       }
-    }
-    // ---- mask: only a tile that reaches past some row's window (wave-uniform test)
+    // ---- mask: only a tile that reaches past some row's window (wave-uniform test); the lane's
+    // keys sit at 4 h + (compile-time offsets) within the tile
     const int t0 = t * kKT;
     if (t0 + kKT - 1 > wave_min_lim) {
-      const int lim = max(min(my_lim - t0, kKT), -1);
+      const int lim = max(min(my_lim - t0, kKT), -1) - 4 * h32;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (4 * h32 + st * 32 + (v >> 2) * 8 + (v & 3) > lim) s[st][v] = -INFINITY;
+        for (int v = 0; v < 16; ++v) s[st][v] = st * 32 + (v >> 2) * 8 + (v & 3) > lim ? -INFINITY : s[st][v];
     }
-    // ---- running max on the raw scores (the scale is positive), probabilities in base 2
+    // ---- reference max on the raw scores (the scale is positive), probabilities in base 2.
+    // The reference moves only when the row's max exceeds it by more than kLazyLog2 (in exp2
+    // units), so most tiles rescale nothing; probabilities stay below 2^kLazyLog2.
     float mloc = -INFINITY;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, s[st][v]);
-    const float m_new = fmaxf(m_run, pair_max(mloc));
-    // rows that have seen no key yet keep m = -inf: scale 1, probabilities 0
-    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * a.scale_log2e);
+    const float m_tile = pair_max(mloc);
+    // a row that has seen no key keeps m = -inf (scale 1, probabilities 0); -inf - -inf is NaN
+    const bool grow = (m_tile - m_run) * a.scale_log2e > kLazyLog2;
+    const float m_new = grow ? m_tile : m_run;
+    const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * a.scale_log2e) : 1.f;
     const float mc = m_new == -INFINITY ? 0.f : m_new * a.scale_log2e;
-    float lsum = 0.f;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[st][v], a.scale_log2e, -mc));
-        s[st][v] = p;
-        lsum += p;
-      }
-    l_run = l_run * alpha + lsum;  // this lane's half of the row sum
+      for (int v = 0; v < 16; ++v) s[st][v] = __builtin_amdgcn_exp2f(fmaf(s[st][v], a.scale_log2e, -mc));
     m_run = m_new;
     if (!__all(alpha == 1.f)) {
 #pragma unroll
       for (int dt = 0; dt < kD / 32; ++dt) o[dt] *= alpha;
+      lsum[0] *= alpha;
     }
-    // ---- O^T += V^T P^T over 4 steps of 16 keys
+    // ---- O^T += V^T P^T over 4 steps of 16 keys; the row sums of the (bf16) probabilities come
+    // from the same product with an all-ones A operand
 #pragma unroll
     for (int sstep = 0; sstep < kKT / 16; ++sstep) {
       bf16x8 pf;
@@ -266,15 +285,16 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
         const shortx4 vv[2] = {lo, hi};
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[dt], 0, 0, 0);
       }
+      lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf, lsum, 0, 0, 0);
     }
   }
 
   if (!wave_active) return;
-  // ---- normalise and store: lane (l32, h) holds row my_row, columns 32 dt + 8 j + 4 h + 0..3
-  const float l_tot = pair_sum(l_run);
+  // ---- normalise, stage the wave's 32 x 128 output block in LDS (a stage no wave reads any
+  // more: the one tile n_tiles - 1 did not use), then store whole rows
+  const float l_tot = lsum[0];
   const float inv_l = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (!row_ok) return;
-  uint16_t* orow = a.out + (q0 + my_tok) * a.ld_o + static_cast<int64_t>(my_head) * kD + 4 * h32;
+  unsigned char* ob = smem + (n_tiles & 1) * kStageBytes + wave * 8192;
 #pragma unroll
   for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
@@ -282,8 +302,19 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
       bf16x4 r;
 #pragma unroll
       for (int e = 0; e < 4; ++e) r[e] = static_cast<__bf16>(o[dt][4 * j + e] * inv_l);
-      *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * j) = __builtin_bit_cast(uint2, r);
+      *reinterpret_cast<bf16x4*>(ob + l32 * kRowBytes + (((4 * dt + j) ^ (l32 & 15)) << 4) + 8 * h32) = r;
     }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int rr = 4 * c + kq;
+    const uint4 v = *reinterpret_cast<const uint4*>(ob + rr * kRowBytes + ((pos ^ (rr & 15)) << 4));
+    const int64_t off = row_off(c, a.ld_o);
+    if (off >= 0) *reinterpret_cast<uint4*>(a.out + off + 8 * pos) = v;
+  }
 }
 
 }  // namespace
