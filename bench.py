@@ -103,7 +103,8 @@ def kernel_source_digest(variant_name: str) -> str:
     """sha256 of the sources that define a kernel family (for matching stored counters)."""
     files = {"tiled": ["fwd_tiled.hip", "tile_common.h"], "decode": ["fwd_decode.hip", "tile_common.h"],
              "generic": ["fwd_generic.hip"], "bwd_tiled": ["bwd_tiled.hip", "tile_common.h"],
-             "bwd_generic": ["bwd_generic.hip"]}[variant_name]
+             "bwd_generic": ["bwd_generic.hip"], "attn": ["attn.hip", "tile_common.h"],
+             "mlp": ["mlp_tiled.hip", "tile_common.h"]}[variant_name]
     h = hashlib.sha256()
     for f in files + ["lrq_internal.h"]:
         p = os.path.join(ROOT, "layer_rmsnorm_qkv_amd", "csrc", f)
@@ -273,10 +274,11 @@ def working_set_copies(w, prob, n_copies: int):
     return sets
 
 
-def run_config(name, args, B, wl, DeviceProblem, dropout=None, nf4=False):
+def run_config(name, args, B, wl, DeviceProblem, dropout=None, nf4=False, key=None):
     """Measure one workload: returns its result object (the shape of the top-level line).
     ``dropout`` = (rate, seed, offset) runs it with LoRA dropout; ``nf4`` stores the base as NF4
-    blocks (the QLoRA base, quantised on the device before the steps)."""
+    blocks (the QLoRA base, quantised on the device before the steps); ``key`` names the entry
+    (stored counter traffic is looked up under it; default: the workload's name)."""
     import numpy as np
     import torch
 
@@ -414,7 +416,7 @@ def run_config(name, args, B, wl, DeviceProblem, dropout=None, nf4=False):
     assert dom_ms <= ms_per_step
     work, kind = dominant_kernel_work(w, family, backward_dominant, nf4)
     kname = KERNEL_NAMES[(family, backward_dominant)]
-    traffic = stored_traffic(w.name, ("bwd_" if backward_dominant else "") + family)
+    traffic = stored_traffic(key or w.name, ("bwd_" if backward_dominant else "") + family)
     common = {"traffic": traffic, "kernel": kname, "launch_ms": dom_ms, "launch_ms_eager_events": dom_eager,
               "launch_ms_clamped_to_step": dom_eager > ms_per_step,
               "share_of_step": dom_ms / ms_per_step}
@@ -520,7 +522,8 @@ def run_mlp_config(name, args, B, wl):
                       "launch": "one HIP graph replay of the K steps" if graph is not None else "eager calls"},
            "tflops_step": (f_gu + f_dn) / (ms_per_step * 1e-3) / 1e12,
            "roofline": {"bound": "mfma", "achieved": f_gu / (dom * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
-                        "unit": "TFLOP/s", "frac": f_gu / (dom * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "traffic": None,
+                        "unit": "TFLOP/s", "frac": f_gu / (dom * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                        "traffic": stored_traffic(w.name, "mlp"),
                         "kernel": "mlp_gate_up_kernel", "launch_ms": dom, "launch_ms_eager_events": k_ms,
                         "algorithmic_flop": f_gu}}
     if not args.no_cpu_baseline:
@@ -558,7 +561,7 @@ def attn_work(w):
 
 def run_attn_config(name, args, B, wl):
     """Attention over the key/value cache (the step after the projection): timed like the
-    projection's workloads; MFMA roofline for prefill, HBM for decode."""
+    projection's workloads; roofline against the peak the call's algorithmic work binds."""
     import numpy as np
     import torch
 
@@ -616,15 +619,21 @@ def run_attn_config(name, args, B, wl):
                       "causal": w.causal, "kernel_family": "attention (flash, MFMA)",
                       "launch": "one HIP graph replay of the K steps" if graph is not None else "eager calls"},
            "tflops_step": flop / (ms_per_step * 1e-3) / 1e12}
-    common = {"traffic": None, "kernel": "attn_kernel", "launch_ms": dom, "launch_ms_eager_events": k_ms}
-    if w.q_len == 1:
+    common = {"traffic": stored_traffic(w.name, "attn"), "kernel": "attn_kernel", "launch_ms": dom,
+              "launch_ms_eager_events": k_ms}
+    # the bound is whichever peak the algorithmic work takes longer on: at these sizes both
+    # calls are HBM-bound (the prefill's 215 FLOP/B is below the 312 FLOP/B ridge)
+    mfma_frac = flop / (dom * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+    if byts / (PEAK_HBM_GBS * 1e9) >= flop / (PEAK_BF16_TFLOPS * 1e12):
         ach = byts / (dom * 1e-3) / 1e9
         res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                           "frac": ach / PEAK_HBM_GBS, "algorithmic_bytes": byts, **common}
+                           "frac": ach / PEAK_HBM_GBS, "algorithmic_bytes": byts, "algorithmic_flop": flop,
+                           "mfma_frac": mfma_frac, **common}
     else:
         ach = flop / (dom * 1e-3) / 1e12
         res["roofline"] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": ach / PEAK_BF16_TFLOPS, "algorithmic_flop": flop, **common}
+                           "frac": ach / PEAK_BF16_TFLOPS, "algorithmic_flop": flop, "algorithmic_bytes": byts,
+                           **common}
     if not args.no_cpu_baseline:
         import oracle.attn_oracle as at
         from oracle.lrq_oracle import rel_frobenius
@@ -661,7 +670,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30, help="untimed steps first (the clocks settle within about 20 steps of sustained MFMA load)")
     ap.add_argument("--workload", default="all",
-                    choices=("all",) + ALL_WORKLOADS + ("train_dropout", "decode_nf4", "attn_prefill", "attn_decode"),
+                    choices=("all",) + ALL_WORKLOADS + ("train_dropout", "decode_nf4", "attn_prefill", "attn_decode",
+                                                       "mlp_llama3"),
                     help="all: every workload, the headline (llama2, the largest) on the top level and all five "
                          "under 'configs'")
     ap.add_argument("--variant", default="auto", choices=["auto", "generic", "tiled", "decode"])
@@ -715,7 +725,7 @@ def main():
     names = ALL_WORKLOADS if args.workload == "all" else (args.workload,)
     results = {}
     for name in names:
-        if name in ("train_dropout", "decode_nf4") or name.startswith("attn_"):
+        if name in ("train_dropout", "decode_nf4", "mlp_llama3") or name.startswith("attn_"):
             continue
         print(f"[bench] {name}: measuring", file=sys.stderr, flush=True)
         results[name] = run_config(name, args, B, wl, DeviceProblem)
@@ -725,7 +735,7 @@ def main():
     if args.workload in ("all", "decode_nf4"):
         # the decode step with the QLoRA base (NF4 blocks)
         print("[bench] decode_nf4: measuring", file=sys.stderr, flush=True)
-        results["decode_nf4"] = run_config("decode", args, B, wl, DeviceProblem, nf4=True)
+        results["decode_nf4"] = run_config("decode", args, B, wl, DeviceProblem, nf4=True, key="decode_nf4")
         r = results["decode_nf4"]
         print(f"[bench] decode_nf4: {r['ms_per_step']:.4f} ms/step, roofline {r['roofline']['frac']:.3f}",
               file=sys.stderr, flush=True)
@@ -734,7 +744,7 @@ def main():
         # the training step again with LoRA dropout (default: the rate of the pages' SFT example)
         print("[bench] train_dropout: measuring", file=sys.stderr, flush=True)
         results["train_dropout"] = run_config("train", args, B, wl, DeviceProblem,
-                                              dropout=(args.dropout or 0.05, 0x5EED, 1))
+                                              dropout=(args.dropout or 0.05, 0x5EED, 1), key="train_dropout")
         r = results["train_dropout"]
         print(f"[bench] train_dropout: {r['ms_per_step']:.4f} ms/step, roofline {r['roofline']['frac']:.3f}",
               file=sys.stderr, flush=True)
@@ -747,14 +757,19 @@ def main():
             print(f"[bench] {an}: {r['ms_per_step']:.4f} ms/step, roofline {r['roofline']['frac']:.3f}",
                   file=sys.stderr, flush=True)
             names = tuple(n for n in names if n != an) + (an,)
-    if args.workload == "all" and not args.no_mlp:
+    if (args.workload == "all" and not args.no_mlp) or args.workload == "mlp_llama3":
         print("[bench] mlp_llama3: measuring", file=sys.stderr, flush=True)
         results["mlp_llama3"] = run_mlp_config("mlp_llama3", args, B, wl)
         r = results["mlp_llama3"]
         print(f"[bench] mlp_llama3: {r['ms_per_step']:.4f} ms/step, roofline {r['roofline']['frac']:.3f}",
               file=sys.stderr, flush=True)
-        names = names + ("mlp_llama3",)
+        names = tuple(n for n in names if n != "mlp_llama3") + ("mlp_llama3",)
     top = dict(results[names[0]])
+    # an entry measured on its own (attention, MLP) still carries the line's common fields
+    for k, v in (("metric", f"{names[0]} throughput"), ("n_gpus", 1), ("steps", args.steps),
+                 ("warmup", args.warmup), ("higher_is_better", True), ("scaling", "weak"),
+                 ("vs_baseline", None), ("data", "synthetic")):
+        top.setdefault(k, v)
     if len(names) > 1:
         top["configs"] = {n: {k: v for k, v in results[n].items()
                               if k not in ("metric", "n_gpus", "higher_is_better", "scaling", "data", "steps",
