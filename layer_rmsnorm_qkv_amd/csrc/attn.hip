@@ -219,23 +219,45 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   for (int t = 0; t < n_tiles; ++t) {
     // tile t is in LDS (every wave's loads), and every wave is done with tile t - 1
     tile::wait_barrier<0>();
-    if (t + 1 < n_tiles) {
-      issue_dma((t + 1) & 1);  // slots of tile t + 1 were read an iteration ago
-      if (t + 2 < n_tiles) load_slots(t + 2);
+    auto next_tile = [&]() {
+      if (t + 1 < n_tiles) {
+        issue_dma((t + 1) & 1);  // slots of tile t + 1 were read an iteration ago
+        if (t + 2 < n_tiles) load_slots(t + 2);
+      }
+    };
+    if (!wave_active) {
+      next_tile();
+      continue;
     }
-    if (!wave_active) continue;
     const unsigned char* kb = smem + (t & 1) * kStageBytes;
     const unsigned char* vb = kb + kTileBytes;
-    // ---- S^T = K Q^T for the two 32-key halves (their accumulation chains interleaved)
+    // ---- S^T = K Q^T for the two 32-key halves (their accumulation chains interleaved), the K
+    // fragments read two steps ahead of their MFMAs; the next tile's loads are issued after the
+    // first steps, while the matrix cores work
     floatx16 s[2] = {floatx16{}, floatx16{}};
+    auto kread = [&](int ks, int st) {
+      return *reinterpret_cast<const bf16x8*>(kb + st * 32 * kRowBytes + k_row_off + ((2 * ks ^ k_xor) << 4));
+    };
+    bf16x8 kfr[3][2];
+    kfr[0][0] = kread(0, 0);
+    kfr[0][1] = kread(0, 1);
+    kfr[1][0] = kread(1, 0);
+    kfr[1][1] = kread(1, 1);
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(kb + st * 32 * kRowBytes + k_row_off + ((2 * ks ^ k_xor) << 4));
-        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[st], 0, 0, 0);
+    for (int ks = 0; ks < kD / 16; ++ks) {
+      if (ks + 2 < kD / 16) {
+        kfr[(ks + 2) % 3][0] = kread(ks + 2, 0);
+        kfr[(ks + 2) % 3][1] = kread(ks + 2, 1);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[ks % 3][0], qf[ks], s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[ks % 3][1], qf[ks], s[1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks == 1) {
+        next_tile();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     // ---- mask: only a tile that reaches past some row's window (wave-uniform test); the lane's
     // keys sit at 4 h + (compile-time offsets) within the tile
     const int t0 = t * kKT;
