@@ -137,11 +137,42 @@ __device__ __forceinline__ void slice_stats(Acc& ta, const Frags& f) {
 // Per-lane DMA sources.  Instruction c (0..7) of wave w fills rows R = 64 w + 8 c + lane / 8
 // of a stage; the lane's 16 bytes land in physical chunk lane % 8, which holds logical
 // chunk (lane % 8) ^ chunk_xor(R) = (lane % 8) ^ (lane / 8) ^ (c & 1).
+// Two forms of the A sources: Src holds the eight row pointers; SrcC forms a row's address
+// where its load is issued, from one base pointer and the lane's first row.  Eight 64-bit
+// pointers live through a whole K loop are what the register allocator spills in a kernel
+// with a heavy epilogue, and every reload of a spilled pointer in the loop makes the wave
+// wait for all of its loads in flight (the stage ring drains); the compact form avoids that
+// at the price of a few VALU instructions per load, and can push spills elsewhere instead,
+// so each kernel takes the form it measures faster with.
 struct Src {
   const uint16_t* a[8];  // A row per instruction; rows past the panel's end re-read its last row
   const uint16_t* b[2];  // B row 64 w + lane / 8 of column tile 0, for even / odd c
   int64_t ldb;           // row stride of B (elements)
 };
+struct SrcC {
+  const uint16_t* a_even;  // A + the lane's logical chunk of even instructions
+  int64_t lda;             // row stride of A (elements)
+  int row_first;           // panel row of instruction 0 for this lane
+  int row_last;            // rows past the panel's end re-read this one (never stored)
+  int a_odd;               // element offset of the odd instructions' chunk (+8 or -8)
+  const uint16_t* b[2];
+  int64_t ldb;
+};
+
+// The lane's first row as a value the compiler cannot treat as loop-invariant (so it does
+// not hoist the eight addresses out of the loop).
+__device__ __forceinline__ int opaque_row(int r) {
+  asm volatile("" : "+v"(r));
+  return r;
+}
+// A row of instruction c; `rf` from issue_row(s), taken once per group of loads
+__device__ __forceinline__ int issue_row(const Src&) { return 0; }
+__device__ __forceinline__ const uint16_t* src_a(const Src& s, int c, int) { return s.a[c]; }
+__device__ __forceinline__ int issue_row(const SrcC& s) { return opaque_row(s.row_first); }
+__device__ __forceinline__ const uint16_t* src_a(const SrcC& s, int c, int rf) {
+  const int row = min(rf + 8 * c, s.row_last);
+  return s.a_even + static_cast<int64_t>(row) * s.lda + ((c & 1) ? s.a_odd : 0);
+}
 
 // Sources for the A panel rows [row0, row0 + 256) of A (stride lda; rows >= rows_valid
 // re-read row rows_valid - 1, whose results are never stored) and the B rows (stride ldb).
@@ -163,6 +194,24 @@ __device__ __forceinline__ Src make_src(const uint16_t* A, int64_t lda, int64_t 
   return s;
 }
 
+// The same sources in the compact form (row indices fit in 32 bits: the library limits T).
+__device__ __forceinline__ SrcC make_src_c(const uint16_t* A, int64_t lda, int64_t row0, int64_t rows_valid,
+                                           const uint16_t* B, int64_t ldb, int wave, int lane) {
+  SrcC s;
+  const int pc = lane & 7;
+  const int rsub = lane >> 3;
+  s.a_even = A + (pc ^ rsub) * 8;
+  s.a_odd = ((pc ^ rsub ^ 1) - (pc ^ rsub)) * 8;
+  s.lda = lda;
+  s.row_first = static_cast<int>(row0) + 64 * wave + rsub;
+  s.row_last = static_cast<int>(rows_valid - 1);
+  // chunk_xor(64 w + 8 c + rsub) = rsub ^ (c & 1)
+  s.b[0] = B + static_cast<int64_t>(64 * wave + rsub) * ldb + (pc ^ rsub) * 8;
+  s.b[1] = B + static_cast<int64_t>(64 * wave + rsub) * ldb + (pc ^ rsub ^ 1) * 8;
+  s.ldb = ldb;
+  return s;
+}
+
 // One tile's K-loop over nk steps: acc = A_panel B_tile^T, B_tile = B rows [col0, col0 + 256);
 // with STATS also the A rows' sums of squares.
 //
@@ -174,8 +223,8 @@ __device__ __forceinline__ Src make_src(const uint16_t* A, int64_t lda, int64_t 
 // After the barrier of step ks every wave holds the rest of stage ks in registers, so that
 // buffer is free.  Spreading the DMA keeps the wave from stalling on a full address queue
 // while the matrix core waits.  sched_fence() pins the interleaving.
-template <bool STATS>
-__device__ __forceinline__ void kloop(unsigned char* smem, Acc& ta, const Src& src, int64_t col0, int nk, int wave,
+template <bool STATS, typename S>
+__device__ __forceinline__ void kloop(unsigned char* smem, Acc& ta, const S& src, int64_t col0, int nk, int wave,
                                       int lane) {
   constexpr int kLoads = 16;  // DMA instructions per stage and wave
   const int wm = wave >> 1, wn = wave & 1;
@@ -187,8 +236,9 @@ __device__ __forceinline__ void kloop(unsigned char* smem, Acc& ta, const Src& s
 
   auto issue_x = [&](int ks, int c0) {
     const uint32_t xs = sbase + kStageA + (ks & 1) * kTileBytes + wave * 8192;
+    const int rf = issue_row(src);
 #pragma unroll
-    for (int c = c0; c < c0 + 4; ++c) dma16(src.a[c] + ks * BK, xs + c * 1024);
+    for (int c = c0; c < c0 + 4; ++c) dma16(src_a(src, c, rf) + ks * BK, xs + c * 1024);
   };
   auto issue_w = [&](int ks, int c0) {
     const uint32_t ws = sbase + kStageB + (ks & 1) * kTileBytes + wave * 8192;
@@ -199,8 +249,9 @@ __device__ __forceinline__ void kloop(unsigned char* smem, Acc& ta, const Src& s
   // instructions c0, c0 + 1 of the x / W' loads of step ks
   auto issue_x2 = [&](int ks, int c0) {
     const uint32_t xs = sbase + kStageA + (ks & 1) * kTileBytes + wave * 8192;
-    dma16(src.a[c0] + ks * BK, xs + c0 * 1024);
-    dma16(src.a[c0 + 1] + ks * BK, xs + (c0 + 1) * 1024);
+    const int rf = issue_row(src);
+    dma16(src_a(src, c0, rf) + ks * BK, xs + c0 * 1024);
+    dma16(src_a(src, c0 + 1, rf) + ks * BK, xs + (c0 + 1) * 1024);
   };
   auto issue_w2 = [&](int ks, int c0) {
     const uint32_t ws = sbase + kStageB + (ks & 1) * kTileBytes + wave * 8192;
@@ -471,8 +522,8 @@ __device__ __forceinline__ RankSrc make_rank_src(const uint16_t* Bs, int64_t ldr
 // (i = 0..3).  Lane layout of u[i] is that of a 32x32 MFMA accumulator.  Leaves the stage
 // ring free (barrier at the end).
 //   step ks: DMA stage ks + 1 | wait for stage ks, barrier | MFMAs | barrier (reads done)
-template <int RB>
-__device__ __forceinline__ void rankpass(unsigned char* smem, const Src& src, const RankSrc& rs, int nk, int wave,
+template <int RB, typename S>
+__device__ __forceinline__ void rankpass(unsigned char* smem, const S& src, const RankSrc& rs, int nk, int wave,
                                          int lane, floatx16 (&u)[RB == 2 ? 4 : 2]) {
   constexpr int kLoads = 8 + RB;       // DMA instructions per stage and wave
   constexpr int NB = RB == 2 ? 4 : 2;  // row blocks per wave
@@ -483,8 +534,9 @@ __device__ __forceinline__ void rankpass(unsigned char* smem, const Src& src, co
 
   auto issue = [&](int ks) {
     const uint32_t as = sbase + kStageA + (ks & 1) * kTileBytes + wave * 8192;
+    const int rf = issue_row(src);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) dma16(src.a[c] + ks * BK, as + c * 1024);
+    for (int c = 0; c < 8; ++c) dma16(src_a(src, c, rf) + ks * BK, as + c * 1024);
     const uint32_t rsl = sbase + kStageB + (ks & 1) * kRStage + wave * RB * 1024;
 #pragma unroll
     for (int q = 0; q < RB; ++q) dma16(rs.r[q] + ks * BK, rsl + q * 1024);
