@@ -61,6 +61,12 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
 
+// The same with a wave-uniform base address in scalar registers and a 32-bit byte offset per
+// lane: per-lane state of one VGPR per distinct row instead of a 64-bit pointer.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+
 // LDS byte address of a pointer into a __shared__ array (the low half of its flat address).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
@@ -358,17 +364,23 @@ struct Acc8 {
 
 // Per-lane DMA sources of the 8-wavefront pipeline.  Instruction c (0..3) of wave w fills
 // rows R = 32 w + 8 c + lane / 8 of the A and the B half of a stage (logical chunk
-// (lane % 8) ^ chunk_xor(R) lands in physical chunk lane % 8).
+// (lane % 8) ^ chunk_xor(R) = (lane % 8) ^ (lane / 8) ^ (c & 1) lands in physical chunk
+// lane % 8).  Addresses are a wave-uniform base (scalar registers, formed per load) plus a
+// 32-bit byte offset per lane: six VGPRs of state instead of eight 64-bit pointers, which the
+// register allocator spilled -- and each reload of a spilled pointer in the K loop waited for
+// every load in flight.  The library's limits (K < 2^19 columns, 256-row panels) keep every
+// offset below 2^32.
 struct Src8 {
-  const uint16_t* a[4];  // A rows; rows past the panel's end re-read its last row
-  const uint16_t* b[4];  // B rows of column tile 0
+  const char* a_base;  // A + row0 * lda, bytes
+  uint32_t a_off[4];   // (min(row0 + R, rows_valid - 1) - row0) * lda * 2 + 16 * chunk
+  const char* b_base;  // B + 32 w * ldb, bytes (column tile 0)
+  uint32_t b_off[2];   // (lane / 8) * ldb * 2 + 16 * chunk, even / odd instructions
   int64_t ldb;
   // K steps >= nk1 read B from a second matrix `tail` (row stride ld_tail) at K offset
-  // 64 (ks - nk1); its per-lane pointers are formed in those steps only
+  // 64 (ks - nk1); its lane offsets are formed in those steps only
   const uint16_t* tail;
   int64_t ld_tail;
   int nk1;
-  int lc[4];  // logical 16-byte chunk of each instruction's row
 };
 
 // B = [B1 | B2]: K steps [0, nk1) from B1 (stride ldb), the rest from B2 (stride ld2).
@@ -376,14 +388,17 @@ __device__ __forceinline__ Src8 make_src8(const uint16_t* A, int64_t lda, int64_
                                           const uint16_t* B, int64_t ldb, int nk1, const uint16_t* B2,
                                           int64_t ld2, int wave, int lane) {
   Src8 s;
+  const int pc = lane & 7, rsub = lane >> 3;
+  s.a_base = reinterpret_cast<const char*>(A + row0 * lda);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const int R = 32 * wave + 8 * c + (lane >> 3);
-    const int lc = (lane & 7) ^ chunk_xor(R);
-    s.a[c] = A + min(row0 + R, rows_valid - 1) * lda + lc * 8;
-    s.b[c] = B + static_cast<int64_t>(R) * ldb + lc * 8;
-    s.lc[c] = lc;
+    const int R = 32 * wave + 8 * c + rsub;
+    const int64_t row = min(row0 + R, rows_valid - 1) - row0;
+    s.a_off[c] = static_cast<uint32_t>(row * lda * 2 + (pc ^ chunk_xor(R)) * 16);
   }
+  s.b_base = reinterpret_cast<const char*>(B + static_cast<int64_t>(32 * wave) * ldb);
+  s.b_off[0] = static_cast<uint32_t>(rsub * ldb * 2 + (pc ^ rsub) * 16);
+  s.b_off[1] = static_cast<uint32_t>(rsub * ldb * 2 + (pc ^ rsub ^ 1) * 16);
   s.ldb = ldb;
   s.tail = B2;
   s.ld_tail = ld2;
@@ -420,19 +435,23 @@ __device__ __forceinline__ void kloop8(unsigned char* smem, Acc8& ta, const Src8
   auto issue = [&](int ks) {
     const uint32_t xa = sbase + kStageA + (ks & 1) * kTileBytes + wave * 4096;
     const uint32_t xb = sbase + kStageB + (ks & 1) * kTileBytes + wave * 4096;
+    const char* ab = src.a_base + static_cast<int64_t>(ks) * BK * 2;
     if (ks < src.nk1) {
+      const char* bb = src.b_base + (boff + static_cast<int64_t>(ks) * BK) * 2;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        dma16(src.a[c] + ks * BK, xa + c * 1024);
-        dma16(src.b[c] + boff + ks * BK, xb + c * 1024);
+        dma16s(ab, src.a_off[c], xa + c * 1024);
+        dma16s(bb + static_cast<int64_t>(8 * c) * src.ldb * 2, src.b_off[c & 1], xb + c * 1024);
       }
     } else {
       const int64_t kt = static_cast<int64_t>(ks - src.nk1) * BK;
+      const int rsub = lane >> 3, pc = lane & 7;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int64_t R = col0 + 32 * wave + 8 * c + (lane >> 3);
-        dma16(src.a[c] + ks * BK, xa + c * 1024);
-        dma16(src.tail + R * src.ld_tail + src.lc[c] * 8 + kt, xb + c * 1024);
+        const char* tb = reinterpret_cast<const char*>(src.tail + (col0 + 32 * wave + 8 * c) * src.ld_tail + kt);
+        const uint32_t toff = static_cast<uint32_t>(rsub * src.ld_tail * 2 + (pc ^ rsub ^ (c & 1)) * 16);
+        dma16s(ab, src.a_off[c], xa + c * 1024);
+        dma16s(tb, toff, xb + c * 1024);
       }
     }
   };
