@@ -171,6 +171,12 @@ __device__ __forceinline__ int opaque_row(int r) {
   asm volatile("" : "+v"(r));
   return r;
 }
+// A wave-uniform value the compiler cannot see through: addresses formed from it stay where
+// they are written instead of being formed once at kernel entry and spilled.
+__device__ __forceinline__ int opaque_s(int v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
 // A row of instruction c; `rf` from issue_row(s), taken once per group of loads
 __device__ __forceinline__ int issue_row(const Src&) { return 0; }
 __device__ __forceinline__ const uint16_t* src_a(const Src& s, int c, int) { return s.a[c]; }
@@ -229,7 +235,9 @@ __device__ __forceinline__ SrcC make_src_c(const uint16_t* A, int64_t lda, int64
 // After the barrier of step ks every wave holds the rest of stage ks in registers, so that
 // buffer is free.  Spreading the DMA keeps the wave from stalling on a full address queue
 // while the matrix core waits.  sched_fence() pins the interleaving.
-template <bool STATS, typename S>
+// OPQ: form the prologue's addresses where they are used (see below); a kernel whose
+// allocator does worse with it turns it off.
+template <bool STATS, bool OPQ = true, typename S>
 __device__ __forceinline__ void kloop(unsigned char* smem, Acc& ta, const S& src, int64_t col0, int nk, int wave,
                                       int lane) {
   constexpr int kLoads = 16;  // DMA instructions per stage and wave
@@ -267,15 +275,20 @@ __device__ __forceinline__ void kloop(unsigned char* smem, Acc& ta, const S& src
   auto sx = [&](int ks) { return smem + kStageA + (ks & 1) * kTileBytes; };
   auto sw = [&](int ks) { return smem + kStageB + (ks & 1) * kTileBytes; };
 
-  issue_x(0, 0);
-  issue_x(0, 4);
-  issue_w(0, 0);
-  issue_w(0, 4);
+  // The prologue's step index is opaque: with constant steps the compiler forms these
+  // addresses (and the first fragment reads') at kernel entry, spills them over the
+  // epilogue, and reloads each one right before its load, which makes every load wait for
+  // all loads in flight.
+  const int k0 = OPQ ? opaque_s(0) : 0;
+  issue_x(k0, 0);
+  issue_x(k0, 4);
+  issue_w(k0, 0);
+  issue_w(k0, 4);
   if (nk > 1) {
-    issue_x(1, 0);
-    issue_x(1, 4);
-    issue_w(1, 0);
-    issue_w(1, 4);
+    issue_x(k0 + 1, 0);
+    issue_x(k0 + 1, 4);
+    issue_w(k0 + 1, 0);
+    issue_w(k0 + 1, 4);
     wait_barrier<kLoads>();
   } else {
     wait_barrier<0>();
@@ -306,7 +319,7 @@ __device__ __forceinline__ void kloop(unsigned char* smem, Acc& ta, const S& src
   };
 
   Frags fa, fb;
-  read_frags(fa, sx(0), sw(0), 0, wm, wn, l32, h32);
+  read_frags(fa, sx(k0), sw(k0), 0, wm, wn, l32, h32);
   // all steps but the last (the last has no barrier, DMA or read-ahead; peeling it keeps
   // every accumulator update out of conditional code)
   for (int ks = 0; ks + 1 < nk; ++ks) {
