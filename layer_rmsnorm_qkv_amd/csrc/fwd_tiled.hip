@@ -451,12 +451,14 @@ hipError_t launch_fwd_tiled(const FwdParams& p, hipStream_t s) {
   a.runs_per_m = (a.n_nt + run - 1) / run;
   a.items = n_mt * a.runs_per_m;
   a.remap = a.items % 8 == 0;
-  const int rb = p.targets ? (p.r <= 32 ? 1 : 2) : 0;
+  // Without adapters the RB = 1 kernel runs with no target set, so it takes no LoRA pass and
+  // no up projection: its register allocation keeps the K-loop free of spills, which an
+  // adapter-free instantiation of its own did not.
+  const int rb = (!p.targets || p.r <= 32) ? 1 : 2;
   dim3 grid(a.items), block(kThreads);
   timing_begin(s);
   const bool drop = p.dropout;
   switch (rb) {
-    case 0: hipLaunchKernelGGL((fwd_tiled_kernel<0, false>), grid, block, 0, s, a); break;
     case 1:
       if (drop)
         hipLaunchKernelGGL((fwd_tiled_kernel<1, true>), grid, block, 0, s, a);
