@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 1) void mlp_down_kernel(DownArgs p) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) ta.acc[i][j] = floatx16{};
-    kloop<false, false>(smem, ta, src, col0, nk, wave, lane);
+    kloop<false, kXorReads>(smem, ta, src, col0, nk, wave, lane);
     if constexpr (LORA) {
       int urow = wm * 128 + l32, bcol = wn * 128 + l32;
       asm volatile("" : "+v"(urow), "+v"(bcol));

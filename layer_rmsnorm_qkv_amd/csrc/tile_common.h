@@ -235,9 +235,14 @@ __device__ __forceinline__ SrcC make_src_c(const uint16_t* A, int64_t lda, int64
 // After the barrier of step ks every wave holds the rest of stage ks in registers, so that
 // buffer is free.  Spreading the DMA keeps the wave from stalling on a full address queue
 // while the matrix core waits.  sched_fence() pins the interleaving.
-// OPQ: form the prologue's addresses where they are used (see below); a kernel whose
-// allocator does worse with it turns it off.
-template <bool STATS, bool OPQ = true, typename S>
+// Options, for kernels whose register allocation does better with them:
+//   kOpqPrologue: form the prologue's addresses where they are used (see below);
+//   kXorReads: form each slice's LDS read addresses from one per-lane offset per operand:
+//     slice kk's 16-byte chunk is slice 0's XOR 2 kk (the swizzle is an XOR of the row's
+//     bits), so the byte offset is slice 0's XOR (kk << 5), with kk << 5 opaque so the four
+//     offsets are not formed ahead and kept (or spilled) for the whole loop.
+constexpr int kOpqPrologue = 1, kXorReads = 2;
+template <bool STATS, int OPT = kOpqPrologue, typename S>
 __device__ __forceinline__ void kloop(unsigned char* smem, Acc& ta, const S& src, int64_t col0, int nk, int wave,
                                       int lane) {
   constexpr int kLoads = 16;  // DMA instructions per stage and wave
@@ -274,12 +279,26 @@ __device__ __forceinline__ void kloop(unsigned char* smem, Acc& ta, const S& src
   };
   auto sx = [&](int ks) { return smem + kStageA + (ks & 1) * kTileBytes; };
   auto sw = [&](int ks) { return smem + kStageB + (ks & 1) * kTileBytes; };
+  const int ra0 = swz(wm * 128 + l32, h32), rb0 = swz(wn * 128 + l32, h32);
+  auto rd = [&](Frags& f, const unsigned char* xs, const unsigned char* ws, int kk) {
+    if constexpr ((OPT & kXorReads) != 0) {
+      const int m = opaque_s(kk << 5);
+      const unsigned char* xa = xs + (ra0 ^ m);
+      const unsigned char* wb = ws + (rb0 ^ m);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(xa + i * 32 * kRowBytes);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f.b[j] = *reinterpret_cast<const bf16x8*>(wb + j * 32 * kRowBytes);
+    } else {
+      read_frags(f, xs, ws, kk, wm, wn, l32, h32);
+    }
+  };
 
   // The prologue's step index is opaque: with constant steps the compiler forms these
   // addresses (and the first fragment reads') at kernel entry, spills them over the
   // epilogue, and reloads each one right before its load, which makes every load wait for
   // all loads in flight.
-  const int k0 = OPQ ? opaque_s(0) : 0;
+  const int k0 = (OPT & kOpqPrologue) ? opaque_s(0) : 0;
   issue_x(k0, 0);
   issue_x(k0, 4);
   issue_w(k0, 0);
@@ -298,19 +317,19 @@ __device__ __forceinline__ void kloop(unsigned char* smem, Acc& ta, const S& src
     const unsigned char* xs = sx(ks);
     const unsigned char* ws = sw(ks);
     sched_fence();
-    read_frags(fb, xs, ws, 1, wm, wn, l32, h32);
+    rd(fb, xs, ws, 1);
     sched_fence();
 #pragma unroll
     for (int i = 0; i < 4; ++i) mfma_row(ta, fa, i);
     if (STATS) slice_stats(ta, fa);
     sched_fence();
-    read_frags(fa, xs, ws, 2, wm, wn, l32, h32);
+    rd(fa, xs, ws, 2);
     sched_fence();
 #pragma unroll
     for (int i = 0; i < 4; ++i) mfma_row(ta, fb, i);
     if (STATS) slice_stats(ta, fb);
     sched_fence();
-    read_frags(fb, xs, ws, 3, wm, wn, l32, h32);
+    rd(fb, xs, ws, 3);
     sched_fence();
 #pragma unroll
     for (int i = 0; i < 4; ++i) mfma_row(ta, fa, i);
@@ -319,7 +338,7 @@ __device__ __forceinline__ void kloop(unsigned char* smem, Acc& ta, const S& src
   };
 
   Frags fa, fb;
-  read_frags(fa, sx(k0), sw(k0), 0, wm, wn, l32, h32);
+  rd(fa, sx(k0), sw(k0), 0);
   // all steps but the last (the last has no barrier, DMA or read-ahead; peeling it keeps
   // every accumulator update out of conditional code)
   for (int ks = 0; ks + 1 < nk; ++ks) {
@@ -348,7 +367,7 @@ __device__ __forceinline__ void kloop(unsigned char* smem, Acc& ta, const S& src
       issue_w2(ks + 2, 4);
     }
     sched_fence();
-    read_frags(fa, sx(ks + 1), sw(ks + 1), 0, wm, wn, l32, h32);
+    rd(fa, sx(ks + 1), sw(ks + 1), 0);
     sched_fence();
     mfma_row(ta, fb, 3);
     sched_fence();
