@@ -278,36 +278,102 @@ __global__ __launch_bounds__(256) void rows_kernel(RowsArgs a) {
   const float inv = 1.0f / sqrtf(ss / static_cast<float>(a.d) + a.eps);
 
   const int half = a.D / 2;
-  // turns per position of the lane's frequencies i = lane + 64 q (D <= 512)
-  double om[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) om[q] = exp2(-(2.0 * (lane + 64 * q) / a.D) * a.log2_theta) * 0.15915494309189533577;
   const double pos = static_cast<double>(a.pos[t]);
   const uint16_t* dyr = a.dy + t * a.N;
   const uint16_t* yr = a.y + t * a.N;
   uint16_t* gr = a.gcat + t * a.K;
   float dot_y = 0.f, dot_b = 0.f;
-  for (int c0 = 0; c0 < a.N; c0 += a.D) {
-    const bool rot = c0 < a.rot_end;
+  const int gph = half / 8;  // groups of 8 frequencies per head
+  if (half % 8 == 0 && 64 % gph == 0) {
+    // 16-byte accesses: the lane takes frequencies 8 g .. 8 g + 7 (g = lane % gph, the same
+    // in every head it visits) of heads lane / gph, + 64 / gph, ...
+    const int g = lane % gph;
+    double om[8];  // turns per position
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = lane + 64 * q;
-      if (i >= half) break;
-      const int ca = c0 + i, cb = c0 + i + half;
-      const float da = bf16_bits_to_f32(dyr[ca]), db = bf16_bits_to_f32(dyr[cb]);
-      dot_y = fmaf(da, bf16_bits_to_f32(yr[ca]), fmaf(db, bf16_bits_to_f32(yr[cb]), dot_y));
-      float ga = da, gb = db;
-      if (rot) {
-        // angle pos * omega_i as a fraction of a turn, reduced in double precision
-        const double turns = pos * om[q];
-        const float f = static_cast<float>(turns - rint(turns));
-        const float s = __builtin_amdgcn_sinf(f), c = __builtin_amdgcn_cosf(f);
-        ga = da * c + db * s;
-        gb = db * c - da * s;
+    for (int e = 0; e < 8; ++e) om[e] = exp2(-(2.0 * (8 * g + e) / a.D) * a.log2_theta) * 0.15915494309189533577;
+    const int heads = a.N / a.D;
+    for (int h = lane / gph; h < heads; h += 64 / gph) {
+      const int c0 = h * a.D;
+      const int ca = c0 + 8 * g, cb = ca + half;
+      const uint4 dav = *reinterpret_cast<const uint4*>(dyr + ca), dbv = *reinterpret_cast<const uint4*>(dyr + cb);
+      const uint4 yav = *reinterpret_cast<const uint4*>(yr + ca), ybv = *reinterpret_cast<const uint4*>(yr + cb);
+      const uint32_t dw[2][4] = {{dav.x, dav.y, dav.z, dav.w}, {dbv.x, dbv.y, dbv.z, dbv.w}};
+      const uint32_t yw[2][4] = {{yav.x, yav.y, yav.z, yav.w}, {ybv.x, ybv.y, ybv.z, ybv.w}};
+      float da[8], db[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) ? 0 : 16;
+        da[e] = __uint_as_float((dw[0][e >> 1] << sh) & 0xffff0000u);
+        db[e] = __uint_as_float((dw[1][e >> 1] << sh) & 0xffff0000u);
+        const float ya = __uint_as_float((yw[0][e >> 1] << sh) & 0xffff0000u);
+        const float yb = __uint_as_float((yw[1][e >> 1] << sh) & 0xffff0000u);
+        dot_y = fmaf(da[e], ya, fmaf(db[e], yb, dot_y));
       }
-      if (a.bias) dot_b = fmaf(ga, bf16_bits_to_f32(a.bias[ca]), fmaf(gb, bf16_bits_to_f32(a.bias[cb]), dot_b));
-      gr[ca] = f32_to_bf16_bits(ga);
-      gr[cb] = f32_to_bf16_bits(gb);
+      float ga[8], gb[8];
+      if (c0 < a.rot_end) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          // angle pos * omega_i as a fraction of a turn, reduced in double precision
+          const double turns = pos * om[e];
+          const float f = static_cast<float>(turns - rint(turns));
+          const float sn = __builtin_amdgcn_sinf(f), cs = __builtin_amdgcn_cosf(f);
+          ga[e] = da[e] * cs + db[e] * sn;
+          gb[e] = db[e] * cs - da[e] * sn;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ga[e] = da[e];
+          gb[e] = db[e];
+        }
+      }
+      if (a.bias) {
+        const uint4 bav = *reinterpret_cast<const uint4*>(a.bias + ca), bbv = *reinterpret_cast<const uint4*>(a.bias + cb);
+        const uint32_t bw[2][4] = {{bav.x, bav.y, bav.z, bav.w}, {bbv.x, bbv.y, bbv.z, bbv.w}};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int sh = (e & 1) ? 0 : 16;
+          const float ba = __uint_as_float((bw[0][e >> 1] << sh) & 0xffff0000u);
+          const float bb = __uint_as_float((bw[1][e >> 1] << sh) & 0xffff0000u);
+          dot_b = fmaf(ga[e], ba, fmaf(gb[e], bb, dot_b));
+        }
+      }
+      uint32_t pa[4], pb[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        pa[q] = static_cast<uint32_t>(f32_to_bf16_bits(ga[2 * q])) | (static_cast<uint32_t>(f32_to_bf16_bits(ga[2 * q + 1])) << 16);
+        pb[q] = static_cast<uint32_t>(f32_to_bf16_bits(gb[2 * q])) | (static_cast<uint32_t>(f32_to_bf16_bits(gb[2 * q + 1])) << 16);
+      }
+      *reinterpret_cast<uint4*>(gr + ca) = make_uint4(pa[0], pa[1], pa[2], pa[3]);
+      *reinterpret_cast<uint4*>(gr + cb) = make_uint4(pb[0], pb[1], pb[2], pb[3]);
+    }
+  } else {
+    // other head sizes: one frequency pair per lane and head
+    double om[4];  // turns per position of the lane's frequencies i = lane + 64 q (D <= 512)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) om[q] = exp2(-(2.0 * (lane + 64 * q) / a.D) * a.log2_theta) * 0.15915494309189533577;
+    for (int c0 = 0; c0 < a.N; c0 += a.D) {
+      const bool rot = c0 < a.rot_end;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = lane + 64 * q;
+        if (i >= half) break;
+        const int ca = c0 + i, cb = c0 + i + half;
+        const float da = bf16_bits_to_f32(dyr[ca]), db = bf16_bits_to_f32(dyr[cb]);
+        dot_y = fmaf(da, bf16_bits_to_f32(yr[ca]), fmaf(db, bf16_bits_to_f32(yr[cb]), dot_y));
+        float ga = da, gb = db;
+        if (rot) {
+          // angle pos * omega_i as a fraction of a turn, reduced in double precision
+          const double turns = pos * om[q];
+          const float f = static_cast<float>(turns - rint(turns));
+          const float s = __builtin_amdgcn_sinf(f), c = __builtin_amdgcn_cosf(f);
+          ga = da * c + db * s;
+          gb = db * c - da * s;
+        }
+        if (a.bias) dot_b = fmaf(ga, bf16_bits_to_f32(a.bias[ca]), fmaf(gb, bf16_bits_to_f32(a.bias[cb]), dot_b));
+        gr[ca] = f32_to_bf16_bits(ga);
+        gr[cb] = f32_to_bf16_bits(gb);
+      }
     }
   }
 #pragma unroll

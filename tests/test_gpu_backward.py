@@ -38,7 +38,7 @@ CASES = {
 }
 
 
-def run_backward(w, variant, dx_rows=None, negative_positions=False):
+def run_backward(w, variant, dx_rows=None, negative_positions=False, fwd_variant=None):
     import torch
     inp = wl.make_inputs(w, with_dy=True)
     if negative_positions:
@@ -52,8 +52,13 @@ def run_backward(w, variant, dx_rows=None, negative_positions=False):
         pytest.skip(f"backward variant {variant} does not cover this shape")
     log(f"[gpu] backward {w.name} T={w.n_tokens} d={w.d_model} N={w.n_out} variant={variant}")
     prob = DeviceProblem(w, inp, variant=variant, backward=True)
-    prob.forward()
-    dx, da, db = prob.backward()
+    if fwd_variant is None:
+        prob.forward()
+        dx, da, db = prob.backward()
+    else:
+        # the forward output from another family (one that covers the shape)
+        y = DeviceProblem(w, inp, variant=fwd_variant).forward()
+        dx, da, db = prob.backward(y=y)
     torch.cuda.synchronize()
     spec = spec_of(w)
     rdx, rda, rdb = o.backward(spec, inp["x"], inp["gamma"], inp["w"], inp["bias"], inp["a"], inp["b"],
@@ -129,6 +134,27 @@ def test_backward_zero_tokens_null_inputs(variant):
     for t in prob.da + prob.db:
         if t is not None:
             assert torch.count_nonzero(t).item() == 0
+
+
+HEADS = {
+    # the tiled family's rows pass at other head sizes: its 16-byte path (64, 256; 8 frequencies
+    # per lane) and its one-pair-per-lane path (96), with bias and rotation of q and k
+    "bf16_head64": TRAIN.replace(n_tokens=70, d_model=256, head_dim=64, n_q_heads=4, n_kv_heads=2, has_bias=True,
+                                 bias_var=0.02, lora_targets=TQ | TV, seq_len=0, max_position=9000),
+    "bf16_head96": TRAIN.replace(n_tokens=70, d_model=256, head_dim=96, n_q_heads=2, n_kv_heads=2, has_bias=True,
+                                 bias_var=0.02, lora_targets=TQ | TV, seq_len=0, max_position=9000),
+    "bf16_head256": TRAIN.replace(n_tokens=70, d_model=256, head_dim=256, n_q_heads=2, n_kv_heads=1, has_bias=True,
+                                  bias_var=0.02, lora_targets=TQ | TK, seq_len=0, max_position=9000),
+}
+
+
+@pytest.mark.parametrize("name", list(HEADS))
+def test_backward_tiled_head_sizes(name):
+    """The tiled backward at head sizes other than 128 (the forward's output comes from the
+    generic family, the one that covers them)."""
+    w = HEADS[name]
+    errs = run_backward(w, B.LRQ_VARIANT_TILED, fwd_variant=B.LRQ_VARIANT_GENERIC)
+    assert_parity(errs, w.dtype)
 
 
 LIMITS = {
