@@ -5,7 +5,8 @@ output bit for bit (written rows hold exactly the k and v blocks of out; every o
 its old value); the output itself meets the forward's bar against the oracle and is the same,
 bit for bit, as lrq_forward's.  Every family is covered: the decode family stores the rows from
 its own epilogues (the streaming kernel for columns without an adapter, the LoRA-up pass for
-the others), the tiled and generic families copy them from out."""
+the others), the tiled family from the epilogue that stores out, and the generic family copies
+them from out."""
 import numpy as np
 import pytest
 
@@ -27,6 +28,13 @@ CASES = {
                                  lora_targets=TQ | TK | TV, lora_rank=3, lora_alpha=5.0), B.LRQ_VARIANT_GENERIC),
     "l3_t70_tiled": (L3.replace(n_tokens=70, d_model=512, n_q_heads=8, n_kv_heads=2), B.LRQ_VARIANT_TILED),
     "l3_t70_generic": (L3.replace(n_tokens=70, d_model=512, n_q_heads=8, n_kv_heads=2), B.LRQ_VARIANT_GENERIC),
+    # the tiled epilogue's cache stores: several token tiles with a ragged last one, k and v
+    # adapted (rank 64, the second adapter layout) with bias; and four kv heads without adapters
+    "l3_t300_tiled_r64_allt": (L3.replace(n_tokens=300, d_model=512, n_q_heads=8, n_kv_heads=2, lora_rank=64,
+                                          lora_targets=TQ | TK | TV, has_bias=True, bias_var=0.02),
+                               B.LRQ_VARIANT_TILED),
+    "l3_t520_tiled_kv4_noadapt": (L3.replace(n_tokens=520, d_model=512, n_q_heads=4, n_kv_heads=4, lora_targets=0),
+                                  B.LRQ_VARIANT_TILED),
     # k and v adapted: the rows come from the LoRA-up pass
     "dec_t200_allt": (L3.replace(n_tokens=200, d_model=1024, n_q_heads=8, n_kv_heads=2, lora_rank=24,
                                  lora_targets=TQ | TK | TV, has_bias=True, bias_var=0.02), B.LRQ_VARIANT_DECODE),
