@@ -388,9 +388,9 @@ __global__ __launch_bounds__(256) void rows_kernel(RowsArgs a) {
 }
 
 // ---------------------------------------------------------------- rank (V and U)
-// One workgroup per (256-token tile, job): u = A_panel Bs^T with the tile pipeline's rank
-// pass, then out[row][col0 + k] = bf16(scale(row) * u) for k < r and 0 for k in
-// [r, pad_to - col0) (the zero padding of Gcat's LoRA columns comes with the last V job).
+// One workgroup per (128-token block, job): u = A_rows Bs^T, then out[row][col0 + k] =
+// bf16(scale(row) * u) for k < r and 0 for k in [r, pad_to - col0) (the zero padding of Gcat's
+// LoRA columns comes with the last V job).
 struct RankJob {
   const uint16_t* a;   // A panel source: element (row, kk) at a[row * lda + kk]
   int64_t lda;
@@ -411,30 +411,93 @@ struct RankArgs {
   int64_t T;
 };
 
+// 128 token rows per workgroup through a three-stage ring (a stage: the A rows [128][64], then
+// the small operand's rows [32 RB][64], every row one 128-byte line with its 16-byte chunks
+// XOR-swizzled by row), so two workgroups share a CU and two stages are in flight per step.
+// Wave w owns rows 32 w .. 32 w + 31 and every rank: RB accumulators.
+constexpr int kRankRows = 128;
+constexpr int kRankStages = 3;
 template <int RB>
-__global__ __launch_bounds__(kThreads, 1) void rank_kernel(RankArgs a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kRingBytes];
+struct RankLay {
+  static constexpr int kA = kRankRows * kRowBytes;
+  static constexpr int kStage = kA + 32 * RB * kRowBytes;
+  static constexpr int kBytes = kRankStages * kStage;
+};
+
+template <int RB>
+__global__ __launch_bounds__(kThreads, 2) void rank_kernel(RankArgs a) {
+  using L = RankLay<RB>;
+  constexpr int kLoads = 4 + RB;  // DMA instructions per stage and wave
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[L::kBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, h32 = lane >> 5;
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * BM;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kRankRows;
   const RankJob& j = a.job[blockIdx.y];
-  const Src src = make_src(j.a, j.lda, row0, a.T, j.bs, j.ldb, wave, lane);
-  floatx16 u[RB == 2 ? 4 : 2];
-  rankpass<RB>(smem, src, make_rank_src(j.bs, j.ldb, j.r, RB, wave, lane), j.nk, wave, lane, u);
-  const int k = rank_col<RB>(wn, l32);
+  // Instruction c of wave w fills A rows R = 32 w + 8 c + lane / 8 (rows past T re-read row
+  // T - 1, never stored) and instruction q fills small-operand rows R = 8 (RB w + q) + lane / 8
+  // (rows past r re-read row r - 1); the lane's 16 bytes land in chunk lane % 8, which holds
+  // logical chunk (lane % 8) ^ chunk_xor(R).
+  const int pc = lane & 7, rsub = lane >> 3;
+  const uint16_t* asrc[4];
 #pragma unroll
-  for (int i = 0; i < (RB == 2 ? 4 : 2); ++i) {
+  for (int c = 0; c < 4; ++c) {
+    const int R = 32 * wave + 8 * c + rsub;
+    asrc[c] = j.a + min(row0 + R, a.T - 1) * j.lda + (pc ^ chunk_xor(R)) * 8;
+  }
+  const uint16_t* bsrc[RB];
+#pragma unroll
+  for (int q = 0; q < RB; ++q) {
+    const int R = 8 * (RB * wave + q) + rsub;
+    bsrc[q] = j.bs + static_cast<int64_t>(min(R, j.r - 1)) * j.ldb + (pc ^ chunk_xor(R)) * 8;
+  }
+  const uint32_t sbase = lds_addr(smem);
+  auto issue = [&](int ks) {
+    const uint32_t st = sbase + (ks % kRankStages) * L::kStage;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dma16(asrc[c] + ks * BK, st + (32 * wave + 8 * c) * kRowBytes);
+#pragma unroll
+    for (int q = 0; q < RB; ++q) dma16(bsrc[q] + ks * BK, st + L::kA + 8 * (RB * wave + q) * kRowBytes);
+  };
+
+  floatx16 u[RB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) u[b] = floatx16{};
+  const int nk = j.nk;
+#pragma unroll
+  for (int s0 = 0; s0 < kRankStages - 1; ++s0)
+    if (s0 < nk) issue(s0);
+  for (int ks = 0; ks < nk; ++ks) {
+    // stage ks landed (the one issued after it may still be in flight); every wave is past its
+    // reads of stage ks - 1, whose buffer the next issue refills
+    if (ks + 1 < nk)
+      wait_barrier<kLoads>();
+    else
+      wait_barrier<0>();
+    if (ks + kRankStages - 1 < nk) issue(ks + kRankStages - 1);
+    const unsigned char* st = smem + (ks % kRankStages) * L::kStage;
+#pragma unroll
+    for (int kk = 0; kk < kSlices; ++kk) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(st + swz(32 * wave + l32, kk * 2 + h32));
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        const bf16x8 bf = *reinterpret_cast<const bf16x8*>(st + L::kA + swz(32 * b + l32, kk * 2 + h32));
+        u[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, u[b], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int k = 32 * b + l32;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int64_t row = row0 + rank_row<RB>(i, v, wm, wn, h32);
+      const int64_t row = row0 + 32 * wave + (v >> 2) * 8 + h32 * 4 + (v & 3);
       if (row >= a.T) continue;
       uint16_t* o = j.out + row * j.ldo + j.col0;
       if (k < j.r) {
         const float f = j.inv ? j.inv[row] * j.scale : j.scale;
-        o[k] = f32_to_bf16_bits(f * u[i][v]);
+        o[k] = f32_to_bf16_bits(f * u[b][v]);
       } else if (j.col0 + k < j.pad_to) {
         o[k] = 0;
       }
@@ -442,7 +505,7 @@ __global__ __launch_bounds__(kThreads, 1) void rank_kernel(RankArgs a) {
   }
   // padding columns beyond the rank blocks (only when pad_to - col0 > 32 RB)
   const int w = j.pad_to - j.col0 - 32 * RB;
-  for (int64_t e = tid; e < static_cast<int64_t>(BM) * w; e += kThreads) {
+  for (int64_t e = tid; e < static_cast<int64_t>(kRankRows) * w; e += kThreads) {
     const int64_t row = row0 + e / w;
     if (row < a.T) j.out[row * j.ldo + j.col0 + 32 * RB + e % w] = 0;
   }
@@ -983,7 +1046,7 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
         uj.scale = 1.0f;
         uj.inv = at<float>(ws, L.inv);
       }
-      const dim3 grid(static_cast<unsigned>((p.T + BM - 1) / BM), nj);
+      const dim3 grid(static_cast<unsigned>((p.T + kRankRows - 1) / kRankRows), nj);
       if (rb == 1)
         hipLaunchKernelGGL(rank_kernel<1>, grid, dim3(kThreads), 0, s, ra2);
       else
