@@ -530,6 +530,8 @@ struct MainArgs {
   int d;
   int64_t K;
   int n_nt;   // column tiles of d
+  int n_mt;   // token tiles
+  int group_m;  // token tiles per group of the tile order
   int items;  // grid size
   int remap;
 };
@@ -599,8 +601,15 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_main_kernel(MainArgs a) {
   const int l32 = lane & 31, h32 = lane >> 5;
   int item = blockIdx.x;
   if (a.remap) item = (blockIdx.x & 7) * (a.items >> 3) + (blockIdx.x >> 3);
-  const int mt = item / a.n_nt;
-  const int nt = item - mt * a.n_nt;
+  // grouped tile order: group_m token tiles by every column tile, token tile fastest, so the
+  // workgroups that run together on one XCD share a few Gcat panels and a few W^T panels
+  // through its L2 instead of two Gcat panels and every W^T panel
+  const int gsz = a.group_m * a.n_nt;
+  const int g = item / gsz, gr = item - g * gsz;
+  const int gm = min(a.n_mt - g * a.group_m, a.group_m);
+  // (wave-uniform: the scalar-base DMA below takes addresses formed from them in SGPRs)
+  const int mt = __builtin_amdgcn_readfirstlane(g * a.group_m + gr % gm);
+  const int nt = __builtin_amdgcn_readfirstlane(gr / gm);
   const int64_t row0 = static_cast<int64_t>(mt) * BM;
   const int64_t col0 = static_cast<int64_t>(nt) * BN;
 
@@ -1070,6 +1079,8 @@ hipError_t launch_bwd_tiled(const BwdParams& bp, hipStream_t s) {
     ma.K = L.K;
     ma.n_nt = static_cast<int>(p.d / BN);
     const int n_mt = static_cast<int>((p.T + BM - 1) / BM);
+    ma.n_mt = n_mt;
+    ma.group_m = 4;
     ma.items = n_mt * ma.n_nt;
     ma.remap = ma.items % 8 == 0;
     if (p.dropout) {
