@@ -1,20 +1,26 @@
 // Decode family of the forward (bf16, at most 256 rows): with so few rows, reading W_qkv
 // from HBM is the whole cost, so the work is arranged around streaming W once.
 //
-//   main    one block per 64 weight rows and 64 token rows.  A "W block" takes the W rows
-//           of 32 rotate-half pairs of one head (columns col0 + 0..31 and col0 + D/2 + 0..31);
-//           an "A block" (one per LoRA target) takes the 64 (padded) rows of A_t.  x and the
-//           weight rows stream through a 4-stage LDS ring (direct-to-LDS loads); each wave
-//           forms bf16(x * gamma) from the staged x and gamma, accumulates x^2 for the row
-//           statistics and multiplies its share of every stage (32x32x16 bf16 MFMA).  The four
-//           waves' partial products are summed through LDS, then
-//             W block:  y = RoPE(inv * acc + b): bf16 into out for columns without an
-//                       adapter, fp32 into the workspace for columns that get a LoRA term
-//             A block:  U_t = bf16(s * inv * acc) into the workspace
-//   finish  one block per 64 adapted columns and 64 rows:  out = bf16(y + RoPE(B_t U_t)),
-//           where RoPE is applied to the LoRA term on its own (the rotation is linear).
-// With a key/value cache, the stores of the k and v columns into out (main for columns
-// without an adapter, finish for the others) also go to the token's cache row.
+//   one kernel, one block per 64 weight rows and 64 token rows.  A "W block" takes the W
+//   rows of 32 rotate-half pairs of one head (columns col0 + 0..31 and col0 + D/2 + 0..31);
+//   an "A block" (one per LoRA target) takes the 64 (padded) rows of A_t.  x and the weight
+//   rows stream through a 4-stage LDS ring (direct-to-LDS loads); each wave forms
+//   bf16(x * gamma) from the staged x and gamma, accumulates x^2 for the row statistics and
+//   multiplies its share of every stage (32x32x16 bf16 MFMA).  The four waves' partial
+//   products are summed through LDS, then
+//     A block:  U_t = bf16(s * inv * acc), 64 tokens x 64 ranks, into the workspace, and a
+//               count that says so
+//     W block:  out = bf16(RoPE(inv * acc + b + B_t U_t)); a block whose columns have an
+//               adapter waits for its U_t's count first (B_t is loaded before the stream).
+//   The A blocks come first in the grid and wait for nothing: workgroups start in index
+//   order on each XCD, so every A block is running or done before a W block that could
+//   wait for it starts, and the waits end.  Each wait is bounded all the same.  A count
+//   word carries a tag of the launch itself (its packet index in the hardware queue and
+//   the queue's address, so it differs between any two launches, replays of a captured
+//   launch included): whatever the workspace held before reads as "nothing stored yet",
+//   and nothing has to be cleared between launches.
+// With a key/value cache, the stores of the k and v columns into out also go to the token's
+// cache row.
 // With an NF4 W (the QLoRA base) a W block streams the rows' 4-bit codes instead (a quarter of
 // the bytes) and dequantises them into the MFMA operand: code book value times the block
 // scale, rounded once to bf16; its scales are staged once per block.  Those blocks stream
@@ -47,11 +53,19 @@ constexpr int kMaxTokens = 256;
 
 size_t al256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
+
+// One 64-bit count word per (row group, A block): the launch tag in bits 8..63, and in bits
+// 0..7 the waves of the A block whose U_t stores have landed (0..2).
+constexpr int kSyncWords = (kMaxTokens / kRows) * 3;
+// Polls of a count word before a wave gives up (never reached when the blocks run: what it
+// waits for is done by a running block that waits for nothing).
+constexpr int kSpinLimit = 1 << 20;
+
 struct DecodeLayout {
   int Tp;      // rows rounded up to the row group
   int nt;      // number of LoRA targets
   int tgt[3];  // target of A block i
-  size_t y, u, xg, inv, total;
+  size_t sync, u, xg, inv, total;
 };
 
 DecodeLayout decode_layout(const FwdParams& p) {
@@ -60,8 +74,8 @@ DecodeLayout decode_layout(const FwdParams& p) {
   for (int t = 0; t < 3; ++t)
     if (p.targets & (1u << t)) L.tgt[L.nt++] = t;
   size_t o = 0;
-  L.y = o;  // fp32 [Tp][N]: adapted columns before their LoRA term
-  o += al256(L.nt ? static_cast<size_t>(L.Tp) * p.N * 4 : 0);
+  L.sync = o;  // uint64 [kSyncWords]: the U_t count words
+  o += al256(L.nt ? kSyncWords * 8 : 0);
   L.u = o;  // bf16 [Tp][nt * 64]: s * inv * U_t, ranks padded to 64
   o += al256(static_cast<size_t>(L.Tp) * L.nt * 64 * 2);
   L.xg = o;  // NF4 weights: bf16 [T][d] x * gamma from the prep pass
@@ -92,16 +106,18 @@ struct MainArgs {
   int nf4;
   const uint16_t* bias;
   const uint16_t* a[3];  // A of the targets in A-block order
+  const uint16_t* b[3];  // B_t by target
+  int ublock[3];         // A block of target t, or -1
   const int32_t* pos;
   uint16_t* out;
-  float* y;
   uint16_t* u;
+  uint64_t* sync;        // U_t count words
   uint16_t* kv_k;           // key/value cache rows (nullptr: none)
   uint16_t* kv_v;
   const int32_t* kv_slots;
   int64_t kv_num_slots;
   int64_t T;
-  int d, N, D, r, nt, n_wblocks;
+  int d, N, D, r, nt, n_wblocks, groups;
   int col_k, col_v, rot_end;
   uint32_t targets;
   float scale, eps;
@@ -178,11 +194,22 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(PrepArgs a) {
   if (lane == 0) a.inv[row] = 1.0f / sqrtf(ss / static_cast<float>(a.d) + a.eps);
 }
 
+// The AQL packet index of this launch in its hardware queue (LLVM's dispatch-id intrinsic).
+extern "C" __device__ uint64_t lrq_decode_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+
+// Tag of this launch in bits 8..63: packet index and queue address mixed, so two launches
+// differ, whether on one queue (indices differ) or on two (addresses differ).
+__device__ __forceinline__ uint64_t launch_tag() {
+  const uint64_t q = reinterpret_cast<uint64_t>(__builtin_amdgcn_queue_ptr());
+  const uint64_t h = (lrq_decode_dispatch_id() + 1) * 0x9E3779B97F4A7C15ull ^ (q * 0xC2B2AE3D27D4EB4Full);
+  return h & ~uint64_t{255};
+}
+
 // Tiles: rt = token-row tile (32 rows), ct = weight-row tile (32 rows).  In a W block the
 // weight rows of ct 0 and ct 1 are the two members of rotate-half pairs, so a pair sits in
 // the same lane and register of the two tiles.
 template <bool NF4>
-__device__ __forceinline__ void decode_main_body(const MainArgs& a, unsigned char* smem) {
+__device__ __forceinline__ void decode_main_body(const MainArgs& a, unsigned char* smem, int nb, int rg) {
   constexpr int kPer = kLoads / 2;                   // x loads (and dense weight loads) per stage
   constexpr int kLoadsT = NF4 ? kPer + 1 : kLoads;   // loads per thread and stage
   constexpr int kStageT = NF4 ? kStageNf4 : kStageBytes;
@@ -190,7 +217,6 @@ __device__ __forceinline__ void decode_main_body(const MainArgs& a, unsigned cha
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h32 = lane >> 5;
-  const int nb = blockIdx.x, rg = blockIdx.y;
   const bool wblock = nb < a.n_wblocks;
   const int half = a.D / 2;
   const int per_head = a.D / 64;
@@ -248,6 +274,42 @@ __device__ __forceinline__ void decode_main_body(const MainArgs& a, unsigned cha
     const int p = wave * 64 + lane, row = p >> 2, lc = (p & 3) ^ ((row >> 2) & 3);
     const int64_t wrow = col0 + (row >> 5) * half + (row & 31);
     csrc = a.wq.codes + wrow * (ld / 2) + lc * 16;
+  }
+  // LoRA-up operand of a W block whose columns have an adapter: B_t's fragments for the
+  // epilogue waves, loaded before the stream so their latency hides under it.  Ranks past r
+  // are zero (16-byte loads clamped into the row, then zeroed; element loads clamped and
+  // zeroed), so the four rank steps of the epilogue run unconditionally.
+  const int t = col0 < a.col_k ? 0 : (col0 < a.col_v ? 1 : 2);
+  const bool adapted = wblock && ((a.targets >> t) & 1u);
+  bf16x8 bf[4][2];
+  if (adapted && wave < 2) {
+    const uint16_t* bt = t == 0 ? a.b[0] : (t == 1 ? a.b[1] : a.b[2]);
+    const int lo_t = t == 0 ? 0 : (t == 1 ? a.col_k : a.col_v);
+    if ((a.r & 7) == 0) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const uint16_t* brow = bt + static_cast<int64_t>(col0 + ct * half + l32 - lo_t) * a.r;
+          bf[kk][ct] = *reinterpret_cast<const bf16x8*>(brow + min(kk * 16 + 8 * h32, a.r - 8));
+        }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        if (kk * 16 + 8 * h32 >= a.r) bf[kk][0] = bf[kk][1] = bf16x8{};
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const uint16_t* brow = bt + static_cast<int64_t>(col0 + ct * half + l32 - lo_t) * a.r;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int rank = kk * 16 + 8 * h32 + e;
+            const uint16_t v = brow[min(rank, a.r - 1)];
+            bf[kk][ct][e] = __builtin_bit_cast(__bf16, rank < a.r ? v : uint16_t{0});
+          }
+        }
+    }
   }
   const uint32_t lds0 = tile::lds_addr(smem) + wave * kPer * 1024;
   const uint32_t ldsc = tile::lds_addr(smem) + kPartBytes + wave * 1024;
@@ -397,11 +459,23 @@ __device__ __forceinline__ void decode_main_body(const MainArgs& a, unsigned cha
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) ub[row * ldu + ct * 32 + l32] = f32_to_bf16_bits(f * y[ct][v]);
     }
+    // this wave's 32 token rows are stored: make them visible device-wide, then count them
+    // (a word with another tag is left over from before: this wave is the first)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (lane == 0) {
+      uint64_t* cw = a.sync + rg * 3 + ab;
+      const uint64_t tag = launch_tag();
+      uint64_t old = __hip_atomic_load(cw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int n = 0; n < kSpinLimit; ++n) {
+        const uint64_t nw = (old & ~uint64_t{255}) == tag ? old + 1 : (tag | 1u);
+        if (__hip_atomic_compare_exchange_strong(cw, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+          break;
+      }
+    }
     return;
   }
 
-  const int t = col0 < a.col_k ? 0 : (col0 < a.col_v ? 1 : 2);
-  const bool adapted = (a.targets >> t) & 1u;
   const int c0 = col0 + l32, c1 = col0 + half + l32;
   const float b0 = a.bias ? bf16_bits_to_f32(a.bias[c0]) : 0.f;
   const float b1 = a.bias ? bf16_bits_to_f32(a.bias[c1]) : 0.f;
@@ -411,6 +485,35 @@ __device__ __forceinline__ void decode_main_body(const MainArgs& a, unsigned cha
   const int64_t myrow = rg * kRows + rt * 32 + l32;
   const int pos_l = myrow < a.T ? a.pos[myrow] : 0;
   const int slot_l = a.kv_slots && myrow < a.T ? a.kv_slots[myrow] : -1;
+
+  // LoRA term B_t U_t of this lane's token rows and columns (the accumulator layout of y)
+  floatx16 lo[2] = {floatx16{}, floatx16{}};
+  if (adapted) {
+    const int ublk = t == 0 ? a.ublock[0] : (t == 1 ? a.ublock[1] : a.ublock[2]);
+    // U_t of this row group: both of its A block's waves have counted their stores
+    uint64_t* cw = a.sync + rg * 3 + ublk;
+    const uint64_t ready = launch_tag() | 2u;
+    for (int n = 0; n < kSpinLimit; ++n) {
+      if (__hip_atomic_load(cw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ready) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    // U_t is read with device-coherent loads, issued after the count was seen; an acquire
+    // fence would instead drop every line of this XCD's L2 (the x rows other blocks stream)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const uint64_t* urow = reinterpret_cast<const uint64_t*>(a.u + myrow * (static_cast<int64_t>(a.nt) * 64) + ublk * 64);
+    bf16x8 uf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int q = (kk * 16 + 8 * h32) / 4;
+      const uint64_t lo64 = __hip_atomic_load(urow + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t hi64 = __hip_atomic_load(urow + q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      uf[kk] = __builtin_bit_cast(bf16x8, make_ulonglong2(lo64, hi64));
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) lo[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(uf[kk], bf[kk][ct], lo[ct], 0, 0, 0);
+  }
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int rsub = (v >> 2) * 8 + h32 * 4 + (v & 3);
@@ -420,6 +523,10 @@ __device__ __forceinline__ void decode_main_body(const MainArgs& a, unsigned cha
     const int slot = __shfl(slot_l, rsub);
     float y0 = fmaf(y[0][v], inv, b0);
     float y1 = fmaf(y[1][v], inv, b1);
+    if (adapted) {
+      y0 += lo[0][v];
+      y1 += lo[1][v];
+    }
     if (rot) {
       const double tt = static_cast<double>(pos) * om;
       const float f = static_cast<float>(tt - rint(tt));
@@ -429,141 +536,8 @@ __device__ __forceinline__ void decode_main_body(const MainArgs& a, unsigned cha
       y1 = r1;
     }
     if (row < a.T) {
-      if (adapted) {
-        float* o = a.y + row * a.N;
-        o[c0] = y0;
-        o[c1] = y1;
-      } else {
-        uint16_t* o = a.out + row * a.N;
-        const uint16_t o0 = f32_to_bf16_bits(y0), o1 = f32_to_bf16_bits(y1);
-        o[c0] = o0;
-        o[c1] = o1;
-        uint16_t* kvr = cache_row(a.kv_k, a.kv_v, a.kv_num_slots, slot, col0, a.col_k, a.col_v);
-        if (kvr) {
-          const int cb = col0 < a.col_v ? a.col_k : a.col_v;
-          kvr[c0 - cb] = o0;
-          kvr[c1 - cb] = o1;
-        }
-      }
-    }
-  }
-}
-
-__global__ __launch_bounds__(256, 1) void decode_main_kernel(MainArgs a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kRingBytes + 2 * kMaxD];
-  if (a.nf4 && static_cast<int>(blockIdx.x) < a.n_wblocks)
-    decode_main_body<true>(a, smem);
-  else
-    decode_main_body<false>(a, smem);
-}
-
-// ---------------------------------------------------------------- finish
-struct FinishArgs {
-  const float* y;
-  const uint16_t* u;
-  const uint16_t* b[3];
-  const int32_t* pos;
-  uint16_t* out;
-  uint16_t* kv_k;
-  uint16_t* kv_v;
-  const int32_t* kv_slots;
-  int64_t kv_num_slots;
-  int64_t T;
-  int N, D, r, nt;
-  int col_k, col_v, rot_end;
-  int ublock[3];  // A block of target t, or -1
-  double log2_theta;
-};
-
-// Two waves, one per 32-row token tile; each holds both members of its 32 rotate-half pairs.
-// VEC: r is a multiple of 8, so a lane's 8 ranks of a B row are one aligned 16-byte load.
-template <bool VEC>
-__global__ __launch_bounds__(128) void decode_finish_kernel(FinishArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l32 = lane & 31, h32 = lane >> 5;
-  const int nb = blockIdx.x, rg = blockIdx.y;
-  const int half = a.D / 2;
-  const int per_head = a.D / 64;
-  const int head = nb / per_head, sub = nb % per_head;
-  const int col0 = head * a.D + sub * 32;
-  const int t = col0 < a.col_k ? 0 : (col0 < a.col_v ? 1 : 2);
-  const int ublk = t == 0 ? a.ublock[0] : (t == 1 ? a.ublock[1] : a.ublock[2]);
-  if (ublk < 0) return;  // no adapter: main stored these columns
-  const uint16_t* bt = t == 0 ? a.b[0] : (t == 1 ? a.b[1] : a.b[2]);
-  const int rt = wave;
-  const int lo_t = t == 0 ? 0 : (t == 1 ? a.col_k : a.col_v);
-  const int64_t ldu = static_cast<int64_t>(a.nt) * 64;
-  const int64_t myrow = rg * kRows + rt * 32 + l32;
-  const uint16_t* urow = a.u + myrow * ldu + ublk * 64;
-
-  // every load is issued before any result is needed: y, U and B fragments, positions
-  const int c0 = col0 + l32, c1 = col0 + half + l32;
-  float yv[16][2];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int64_t row = min(static_cast<int64_t>(rg * kRows + rt * 32 + (v >> 2) * 8 + h32 * 4 + (v & 3)), a.T - 1);
-    yv[v][0] = a.y[row * a.N + c0];
-    yv[v][1] = a.y[row * a.N + c1];
-  }
-  const int pos_l = myrow < a.T ? a.pos[myrow] : 0;
-  const int slot_l = a.kv_slots && myrow < a.T ? a.kv_slots[myrow] : -1;
-  // ranks past r: B is zero there (vector loads skip them; element loads are clamped into
-  // the row and zeroed), so the four rank steps run unconditionally (U holds finite padding)
-  bf16x8 uf[4], bf[4][2];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int rank0 = kk * 16 + 8 * h32;
-    uf[kk] = *reinterpret_cast<const bf16x8*>(urow + rank0);
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const uint16_t* brow = bt + static_cast<int64_t>(col0 + ct * half + l32 - lo_t) * a.r;
-      if constexpr (VEC) {
-        // unconditional load (clamped into the row; zeroed below): a load under a lane-divergent
-        // branch makes the compiler wait for every earlier load at the branch's end
-        bf[kk][ct] = *reinterpret_cast<const bf16x8*>(brow + min(rank0, a.r - 8));
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint16_t v = brow[min(rank0 + e, a.r - 1)];
-          bf[kk][ct][e] = __builtin_bit_cast(__bf16, rank0 + e < a.r ? v : uint16_t{0});
-        }
-      }
-    }
-  }
-  // the rotation frequency (a double-precision exp2) while the loads are in flight
-  tile::sched_fence();
-  const bool rot = col0 < a.rot_end;
-  const double om = exp2(-(2.0 * (sub * 32 + l32) / a.D) * a.log2_theta) * 0.15915494309189533577;
-  tile::sched_fence();
-  if constexpr (VEC) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      if (kk * 16 + 8 * h32 >= a.r) bf[kk][0] = bf[kk][1] = bf16x8{};
-  }
-  floatx16 lo[2] = {floatx16{}, floatx16{}};
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) lo[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(uf[kk], bf[kk][ct], lo[ct], 0, 0, 0);
-
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int rsub = (v >> 2) * 8 + h32 * 4 + (v & 3);
-    const int64_t row = rg * kRows + rt * 32 + rsub;
-    const int pos = __shfl(pos_l, rsub);
-    const int slot = __shfl(slot_l, rsub);
-    float l0 = lo[0][v], l1 = lo[1][v];
-    if (rot) {
-      const double tt = static_cast<double>(pos) * om;
-      const float f = static_cast<float>(tt - rint(tt));
-      const float sn = __builtin_amdgcn_sinf(f), cs = __builtin_amdgcn_cosf(f);
-      const float r0 = l0 * cs - l1 * sn, r1 = l1 * cs + l0 * sn;
-      l0 = r0;
-      l1 = r1;
-    }
-    if (row < a.T) {
       uint16_t* o = a.out + row * a.N;
-      const uint16_t o0 = f32_to_bf16_bits(yv[v][0] + l0), o1 = f32_to_bf16_bits(yv[v][1] + l1);
+      const uint16_t o0 = f32_to_bf16_bits(y0), o1 = f32_to_bf16_bits(y1);
       o[c0] = o0;
       o[c1] = o1;
       uint16_t* kvr = cache_row(a.kv_k, a.kv_v, a.kv_num_slots, slot, col0, a.col_k, a.col_v);
@@ -575,6 +549,28 @@ __global__ __launch_bounds__(128) void decode_finish_kernel(FinishArgs a) {
     }
   }
 }
+
+// One-dimensional grid of (n_wblocks + nt) * groups blocks: first the nt * groups A blocks
+// (block k: row group k / nt, A block k % nt), then the W blocks (block na + i: row group
+// i / n_wblocks, W block i % n_wblocks).
+__global__ __launch_bounds__(256, 1) void decode_main_kernel(MainArgs a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kRingBytes + 2 * kMaxD];
+  const int job = static_cast<int>(blockIdx.x);
+  const int na = a.nt * a.groups;
+  int nb, rg;
+  if (job < na) {
+    rg = job / a.nt;
+    nb = a.n_wblocks + (job - rg * a.nt);
+  } else {
+    rg = (job - na) / a.n_wblocks;
+    nb = (job - na) - rg * a.n_wblocks;
+  }
+  if (a.nf4 && nb < a.n_wblocks)
+    decode_main_body<true>(a, smem, nb, rg);
+  else
+    decode_main_body<false>(a, smem, nb, rg);
+}
+
 
 }  // namespace
 
@@ -618,8 +614,13 @@ hipError_t launch_fwd_decode(const FwdParams& p, hipStream_t s) {
   ma.kv_v = static_cast<uint16_t*>(p.kv_v);
   ma.kv_slots = p.kv_slots;
   ma.kv_num_slots = p.kv_num_slots;
-  ma.y = reinterpret_cast<float*>(ws + L.y);
   ma.u = reinterpret_cast<uint16_t*>(ws + L.u);
+  ma.sync = reinterpret_cast<uint64_t*>(ws + L.sync);
+  for (int t = 0; t < 3; ++t) {
+    ma.b[t] = static_cast<const uint16_t*>(p.b[t]);
+    ma.ublock[t] = -1;
+  }
+  for (int i = 0; i < L.nt; ++i) ma.ublock[L.tgt[i]] = i;
   ma.T = p.T;
   ma.d = static_cast<int>(p.d);
   ma.N = p.N;
@@ -627,6 +628,7 @@ hipError_t launch_fwd_decode(const FwdParams& p, hipStream_t s) {
   ma.r = p.r;
   ma.nt = L.nt;
   ma.n_wblocks = p.N / 64;
+  ma.groups = groups;
   ma.col_k = p.col_k;
   ma.col_v = p.col_v;
   ma.rot_end = p.rot_end;
@@ -635,37 +637,8 @@ hipError_t launch_fwd_decode(const FwdParams& p, hipStream_t s) {
   ma.eps = p.eps;
   ma.log2_theta = log2(p.theta);
   timing_begin(s);
-  hipLaunchKernelGGL(decode_main_kernel, dim3(ma.n_wblocks + L.nt, groups), dim3(256), 0, s, ma);
+  hipLaunchKernelGGL(decode_main_kernel, dim3(static_cast<unsigned>((ma.n_wblocks + L.nt) * groups)), dim3(256), 0, s, ma);
   timing_end(s);
-  if (L.nt == 0) return hipGetLastError();
-
-  FinishArgs fa{};
-  fa.y = ma.y;
-  fa.u = ma.u;
-  for (int t = 0; t < 3; ++t) {
-    fa.b[t] = static_cast<const uint16_t*>(p.b[t]);
-    fa.ublock[t] = -1;
-  }
-  for (int i = 0; i < L.nt; ++i) fa.ublock[L.tgt[i]] = i;
-  fa.pos = p.pos;
-  fa.out = ma.out;
-  fa.kv_k = ma.kv_k;
-  fa.kv_v = ma.kv_v;
-  fa.kv_slots = ma.kv_slots;
-  fa.kv_num_slots = ma.kv_num_slots;
-  fa.T = p.T;
-  fa.N = p.N;
-  fa.D = p.D;
-  fa.r = p.r;
-  fa.nt = L.nt;
-  fa.col_k = p.col_k;
-  fa.col_v = p.col_v;
-  fa.rot_end = p.rot_end;
-  fa.log2_theta = ma.log2_theta;
-  if (p.r % 8 == 0)
-    hipLaunchKernelGGL(decode_finish_kernel<true>, dim3(p.N / 64, groups), dim3(128), 0, s, fa);
-  else
-    hipLaunchKernelGGL(decode_finish_kernel<false>, dim3(p.N / 64, groups), dim3(128), 0, s, fa);
   return hipGetLastError();
 }
 

@@ -250,6 +250,73 @@ def test_forward_replays_in_a_hip_graph(variant):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("variant", ["tiled", "decode"])
+def test_graph_replays_follow_new_inputs(variant):
+    """A captured forward replayed over new x in the same buffer gives each new input's eager
+    result, bit for bit (in the decode family the W blocks wait for this launch's U_t, never
+    for the one a previous replay stored)."""
+    import torch
+    w = SMALL_BF16["dec_t200_gqa_r24"]
+    if B.lrq_select_variant(desc_for(w, variant=VARIANTS[variant])) < 0:
+        pytest.skip("variant does not cover this shape")
+    log(f"[gpu] graph replays over new inputs variant={variant}")
+    prob = DeviceProblem(w, wl.make_inputs(w), variant=VARIANTS[variant])
+    xs = [prob.x.clone()] + [DeviceProblem(w, wl.make_inputs(w, seed=11 + k), variant=VARIANTS[variant]).x
+                             for k in range(3)]
+    expect = []
+    for x in xs:
+        prob.x.copy_(x)
+        expect.append(prob.forward().clone())
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        prob.forward()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        prob.forward()
+    for rnd in range(2):
+        for k in range(len(xs)):
+            prob.x.copy_(xs[k])
+            prob.out.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(prob.out, expect[k]), (rnd, k)
+
+
+@pytest.mark.parametrize("fill", ["zeros", "ones", "random"])
+def test_decode_ignores_what_the_workspace_held(fill):
+    """The decode family's LoRA-down blocks hand U_t to the W blocks through count words in the
+    workspace.  Whatever the workspace held before (zeros, all bits set, random bytes), and with
+    a call on other inputs through the same workspace in between, the result is the same, bit
+    for bit, as the first call's."""
+    import torch
+    w = SMALL_BF16["dec_t200_gqa_r24"]
+    log(f"[gpu] decode over a used workspace fill={fill}")
+    prob = DeviceProblem(w, wl.make_inputs(w), variant=B.LRQ_VARIANT_DECODE)
+    other = DeviceProblem(w, wl.make_inputs(w, seed=7), variant=B.LRQ_VARIANT_DECODE)
+    other.workspace = prob.workspace
+    eager = prob.forward().clone()
+    other_ref = other.forward().clone()
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    for _ in range(3):
+        if fill == "zeros":
+            prob.workspace.zero_()
+        elif fill == "ones":
+            prob.workspace.fill_(255)
+        else:
+            prob.workspace.copy_(torch.randint(0, 256, prob.workspace.shape, generator=gen, dtype=torch.uint8))
+        prob.out.zero_()
+        prob.forward()
+        other.forward()
+        torch.cuda.synchronize()
+        assert torch.equal(prob.out, eager)
+        assert torch.equal(other.out, other_ref)
+
+
 def test_forward_output_past_2_31_elements():
     """T x N above 2^31 output elements (360448 tokens x 6144 columns, d = 512): every row and
     column offset must be formed in 64 bits.  Checked on sampled rows, including the last."""
