@@ -79,8 +79,8 @@ def dominant_kernel_work(w, family: str, backward: bool, nf4: bool = False):
     """Algorithmic work of one launch of a call's dominant kernel: (amount, unit kind).
 
     Forward, tiled or generic: every matmul FLOP of the forward.  Forward, decode: the bytes
-    the streaming kernel must move (x, gamma, W, bias, the targets' A, positions, and the
-    outputs of columns without an adapter; the LoRA-up pass writes the rest).  Backward,
+    the streaming kernel must move (x, gamma, W, bias, the targets' A and B, positions, and
+    every output).  Backward,
     tiled: dh = G W + sum_t V'_t A_t, 2 T d (N + sum of ranks) FLOPs.  Backward, generic:
     every matmul FLOP of the backward."""
     f_fwd, f_bwd, _ = algorithmic_work(w)
@@ -91,8 +91,8 @@ def dominant_kernel_work(w, family: str, backward: bool, nf4: bool = False):
         return (2.0 * T * d * (N + ranks), "flop") if family == "tiled" else (f_bwd, "flop")
     if family == "decode":
         eb = 2
-        unadapted = sum(hi - lo for t, (lo, hi) in cols.items() if not (w.lora_targets & t))
-        nbytes = eb * (T * d + d + N * d + (N if w.has_bias else 0) + ranks * d + T * unadapted) + 4 * T
+        b_elems = sum(r * (hi - lo) for t, (lo, hi) in cols.items() if w.lora_targets & t)
+        nbytes = eb * (T * d + d + N * d + (N if w.has_bias else 0) + ranks * d + b_elems + T * N) + 4 * T
         if nf4:  # the QLoRA base: 4-bit codes plus a float32 scale per 64 weights instead of bf16
             nbytes -= eb * N * d - (N * d // 2 + N * (d // 64) * 4)
         return nbytes, "bytes"

@@ -43,10 +43,10 @@ def test_dominant_kernel_work():
     assert bench.dominant_kernel_work(wl.get("llama3"), "tiled", False) == (414061690880.0, "flop")
     # tiled backward main product: 2 T d (N + sum of ranks) = 2 * 16384 * 4096 * (6144 + 16)
     assert bench.dominant_kernel_work(wl.get("train"), "tiled", True) == (2.0 * 16384 * 4096 * 6160, "flop")
-    # decode streaming kernel: x, gamma, W, bias, the targets' A, positions (all columns have
-    # an adapter, so it writes no output columns)
+    # decode streaming kernel: x, gamma, W, bias, the targets' A and B (rank 64 on q, k and v:
+    # 64 x d and N x 64 elements), every output, positions
     T, d, N = 64, 4096, 12288
-    expected = 2 * (T * d + d + N * d + N + 3 * 64 * d) + 4 * T
+    expected = 2 * (T * d + d + N * d + N + 3 * 64 * d + N * 64 + T * N) + 4 * T
     assert bench.dominant_kernel_work(wl.get("decode"), "decode", False) == (expected, "bytes")
 
 
