@@ -47,6 +47,10 @@ SMALL_BF16 = {
                                    lora_targets=TQ | TK | TV, has_bias=True, bias_var=0.02),
     "dec_d64head_konly": DEC.replace(n_tokens=33, d_model=512, n_q_heads=4, n_kv_heads=2, head_dim=64,
                                      lora_targets=TK, lora_rank=5),
+    # the decode family's LoRA hand-over: a second row group holding one row, a rank that is
+    # not a multiple of 8 (element loads of B) on every target, bias, GQA
+    "dec_t65_r5_allt": L3.replace(n_tokens=65, d_model=512, n_q_heads=8, n_kv_heads=2, lora_rank=5,
+                                  lora_targets=TQ | TK | TV, has_bias=True, bias_var=0.02),
     # a rank that is not a multiple of 8 in the MFMA families (element loads of B in the
     # tiled epilogue, a ragged rank block)
     "l3_t130_r5_konly": L3.replace(n_tokens=130, d_model=512, n_q_heads=4, n_kv_heads=2, lora_rank=5,
