@@ -46,7 +46,7 @@
  * hipStream_t; NULL = the null stream) and nothing is synchronised.  The library allocates
  * no device memory; scratch space is the caller's `workspace` of at least
  * lrq_workspace_size() bytes, 256-byte aligned (LRQ_ERR_UNSUPPORTED otherwise), used only
- * until the enqueued work ends.
+ * until the enqueued work ends; its contents before a call do not matter.
  * Calls that share a workspace must be ordered on one stream.
  *
  * Errors: every entry point validates its arguments on the host before enqueuing
@@ -261,9 +261,10 @@ size_t lrq_workspace_size_prepared(const lrq_desc* desc, int for_backward);
  * tiled family needs the scratch only for the adapters' folded A rows when weights are
  * prepared (without prepared weights its W' does not fit and the call is refused); the decode
  * family keeps its per-call intermediates there.  Every call on a GPU shares that GPU's array:
- * calls that overlap on one GPU (other streams, other threads) race and give wrong results;
- * order them.  No part of the scratch needs to start at zero: every call writes what it
- * reads.  Same results, bit for bit, as lrq_forward_prepared; same errors, plus UNSUPPORTED
+ * calls that overlap on one GPU (other streams, other threads) race and give wrong results
+ * (in the decode family, whose blocks hand data to each other through the scratch, a call can
+ * then also wait up to about a second before giving up); order them.  No part of the scratch
+ * needs to start at zero: every call writes what it reads.  Same results, bit for bit, as lrq_forward_prepared; same errors, plus UNSUPPORTED
  * when the call needs more than LRQ_NOALLOC_SCRATCH_BYTES of scratch (lrq_workspace_size or
  * lrq_workspace_size_prepared tells how much), and LRQ_ERR_HIP if the array's device address
  * cannot be looked up. */
