@@ -493,9 +493,10 @@ __device__ __forceinline__ void decode_main_body(const MainArgs& a, unsigned cha
     // U_t of this row group: both of its A block's waves have counted their stores
     uint64_t* cw = a.sync + rg * 3 + ublk;
     const uint64_t ready = launch_tag() | 2u;
-    for (int n = 0; n < kSpinLimit; ++n) {
-      if (__hip_atomic_load(cw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ready) break;
-      __builtin_amdgcn_s_sleep(1);
+    bool landed = false;
+    for (int n = 0; n < kSpinLimit && !landed; ++n) {
+      landed = __hip_atomic_load(cw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ready;
+      if (!landed) __builtin_amdgcn_s_sleep(1);
     }
     // U_t is read with device-coherent loads, issued after the count was seen; an acquire
     // fence would instead drop every line of this XCD's L2 (the x rows other blocks stream)
@@ -513,6 +514,11 @@ __device__ __forceinline__ void decode_main_body(const MainArgs& a, unsigned cha
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) lo[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(uf[kk], bf[kk][ct], lo[ct], 0, 0, 0);
+    if (!landed) {
+      // the wait gave up (never expected): poison these outputs rather than use stale U_t
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) lo[ct] = floatx16{} + __builtin_nanf("");
+    }
   }
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
