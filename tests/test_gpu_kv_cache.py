@@ -4,9 +4,9 @@ Bars: the cache rows are byte work, so they must equal the oracle's cache update
 output bit for bit (written rows hold exactly the k and v blocks of out; every other row keeps
 its old value); the output itself meets the forward's bar against the oracle and is the same,
 bit for bit, as lrq_forward's.  Every family is covered: the decode family stores the rows from
-its own epilogues (the streaming kernel for columns without an adapter, the LoRA-up pass for
-the others), the tiled family from the epilogue that stores out, and the generic family copies
-them from out."""
+the streaming kernel's epilogue (after the LoRA term for columns with an adapter), the tiled
+family from the epilogue that stores out, and the generic family copies them from out.  A
+seeded sweep of random shapes runs each through every family that covers it."""
 import numpy as np
 import pytest
 
@@ -35,10 +35,10 @@ CASES = {
                                B.LRQ_VARIANT_TILED),
     "l3_t520_tiled_kv4_noadapt": (L3.replace(n_tokens=520, d_model=512, n_q_heads=4, n_kv_heads=4, lora_targets=0),
                                   B.LRQ_VARIANT_TILED),
-    # k and v adapted: the rows come from the LoRA-up pass
+    # k and v adapted: the rows are stored after the LoRA term handed over from the A blocks
     "dec_t200_allt": (L3.replace(n_tokens=200, d_model=1024, n_q_heads=8, n_kv_heads=2, lora_rank=24,
                                  lora_targets=TQ | TK | TV, has_bias=True, bias_var=0.02), B.LRQ_VARIANT_DECODE),
-    # k and v without adapters: the rows come from the streaming kernel
+    # k and v without adapters: no wait for a LoRA term before the store
     "dec_t33_q_only": (DEC.replace(n_tokens=33, d_model=512, n_q_heads=4, n_kv_heads=4, lora_targets=TQ),
                        B.LRQ_VARIANT_DECODE),
     "dec_t1_noadapt": (DEC.replace(n_tokens=1, d_model=512, n_q_heads=4, n_kv_heads=4, lora_targets=0),
@@ -125,3 +125,29 @@ def test_zero_slots_writes_nothing(name):
     slots = make_slots(w.n_tokens, w.n_tokens + 7, seed=3)
     _, prob, out_kv, kc, vc, init = run(w, variant, 0, slots, rows=16)
     assert np.array_equal(to_np(kc), init[0]) and np.array_equal(to_np(vc), init[1])
+
+
+@pytest.mark.parametrize("variant", ["generic", "tiled", "decode"])
+@pytest.mark.parametrize("seed", range(6))
+def test_forward_kv_cache_random_shape(seed, variant):
+    """Seeded random layers (the generator of the random-shape forward sweep; for the decode
+    family at most 256 rows and d = 512) through lrq_forward_kv with padding tokens and a slot past the
+    cache, in every family that covers the shape: out to the forward's bar, the cache rows bit
+    for bit."""
+    from test_gpu_random_shapes import random_case
+    w, _ = random_case(200 + seed)
+    if variant == "decode":  # the decode family's range: at most 256 rows, d a multiple of 512
+        w = w.replace(n_tokens=1 + (w.n_tokens - 1) % 256, d_model=512, w_var=1.0 / 512)
+    v = {"generic": B.LRQ_VARIANT_GENERIC, "tiled": B.LRQ_VARIANT_TILED, "decode": B.LRQ_VARIANT_DECODE}[variant]
+    num_slots = w.n_tokens + 5
+    slots = make_slots(w.n_tokens, num_slots, seed=seed)
+    inp, prob, out_kv, kc, vc, init = run(w, v, num_slots, slots, seed=seed)
+    import torch
+    assert torch.equal(out_kv, prob.out), "lrq_forward_kv and lrq_forward disagree on out"
+    got = to_np(out_kv)
+    errs = forward_errors(w, got, oracle_forward(w, inp))
+    log(f"  errors {errs}")
+    assert_parity(errs, w.dtype)
+    ek, ev = o.kv_cache_write(spec_of(w), got, slots, init[0], init[1])
+    assert np.array_equal(to_np(kc), ek)
+    assert np.array_equal(to_np(vc), ev)
