@@ -174,3 +174,27 @@ def test_projection_cache_attention_chain():
     log(f"  errors {errs}")
     assert_parity(errs, "bf16")
     assert TOL["bf16"] > 0
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_attention_random_batches(seed):
+    """Seeded random batches: 1-6 sequences of 0-400 cached tokens with 0..kv_len queries each,
+    1, 2 or 4 kv heads with 1-8 q heads per kv head, q rows inside a wider projection output or
+    not, a few slots outside the cache or not, causal on or off."""
+    rng = np.random.default_rng(500 + seed)
+    lens = []
+    for _ in range(int(rng.integers(1, 7))):
+        kl = int(rng.integers(0, 401))
+        lens.append((int(rng.integers(0, kl + 1)), kl))
+    hkv = int(rng.choice([1, 2, 4]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8]))
+    total_kv = sum(kl for _, kl in lens)
+    c = make_case(seed=seed, lens=tuple(lens), hq=hq, hkv=hkv, ld_extra=int(rng.choice([0, 128])),
+                  bad_slots=2 if total_kv >= 2 and rng.random() < 0.3 else 0)
+    causal = int(rng.integers(0, 2))
+    log(f"[gpu] random attention seed={seed} lens={lens} heads={hq}/{hkv} causal={causal}")
+    got = run_gpu(c, causal=causal)
+    ref = oracle_of(c, causal=bool(causal))
+    errs = errors(got, ref)
+    log(f"  errors {errs}")
+    assert_parity(errs, "bf16")
