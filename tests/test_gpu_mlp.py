@@ -107,3 +107,18 @@ def test_mlp_repeated_and_graph_replay():
         assert torch.equal(prob.out, first)
         prob.forward()
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_mlp_random_shape(seed):
+    """Seeded random MLPs in the kernel's range: 1-400 tokens, d a multiple of 256 up to 768,
+    d_ff a multiple of 128 up to 1024, rank 1-32, any subset of gate / up / down adapted."""
+    rng = np.random.default_rng(700 + seed)
+    w = BASE.replace(name=f"mlp_rand{seed}", n_tokens=int(rng.integers(1, 401)),
+                     d_model=256 * int(rng.integers(1, 4)), d_ff=128 * int(rng.integers(1, 9)),
+                     lora_rank=int(rng.choice([1, 5, 8, 16, 24, 32])), lora_targets=int(rng.integers(0, 8)),
+                     lora_alpha=float(rng.choice([8.0, 16.0, 32.0])))
+    got, ref, _, _ = run(w)
+    errs = errors(w, got, ref)
+    log(f"  errors {errs}")
+    assert_parity(errs, "bf16", w.name)
