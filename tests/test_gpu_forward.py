@@ -290,6 +290,29 @@ def test_graph_replays_follow_new_inputs(variant):
             assert torch.equal(prob.out, expect[k]), (rnd, k)
 
 
+def test_decode_calls_on_two_streams_at_once():
+    """Two decode calls in flight together on two streams, each with its own workspace (the
+    blocks of each launch hand U_t over through their own count words): both results equal
+    the same calls made one at a time, bit for bit, over several rounds."""
+    import torch
+    w = SMALL_BF16["dec_t200_gqa_r24"]
+    log("[gpu] decode on two streams at once")
+    pa = DeviceProblem(w, wl.make_inputs(w), variant=B.LRQ_VARIANT_DECODE)
+    pb = DeviceProblem(w, wl.make_inputs(w, seed=9), variant=B.LRQ_VARIANT_DECODE)
+    ea, eb = pa.forward().clone(), pb.forward().clone()
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(4):
+        pa.out.zero_()
+        pb.out.zero_()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            pa.forward(stream=sa.cuda_stream)
+            pb.forward(stream=sb.cuda_stream)
+        torch.cuda.synchronize()
+        assert torch.equal(pa.out, ea) and torch.equal(pb.out, eb)
+
+
 @pytest.mark.parametrize("fill", ["zeros", "ones", "random"])
 def test_decode_ignores_what_the_workspace_held(fill):
     """The decode family's LoRA-down blocks hand U_t to the W blocks through count words in the
